@@ -1,0 +1,213 @@
+"""Block-sparse tiled video attention for MI355X (gfx950).
+
+Python face of libbsta.so.  The four calls of the path keep the C names:
+
+    attn_tile(g, x)                      raster [B,L,H,D] -> tiles [B,Lpad,H,D]
+    attn_select_blocks(g, qt, kt, ...)   pooled scores -> top-k / window -> CSR
+    attn_block_sparse_fwd(g, qt, kt, vt, row_ptr, col_idx)
+    attn_untile(g, yt)                   tiles -> raster
+
+``g`` is a ``Geometry``.  Tensors are torch bfloat16 tensors on the ROCm
+device; outputs are allocated with torch when not given.  Every kernel runs on
+torch's current stream.  Nothing here computes: each call checks shapes,
+marshals pointers and forwards to the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import SELECT_STA, SELECT_TOPK, BstaError
+
+__all__ = [
+    "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "attn_tile", "attn_untile",
+    "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
+    "attn_workspace_bytes", "block_sparse_attention",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    B: int
+    H: int
+    D: int
+    T: int
+    Y: int
+    X: int
+
+    @property
+    def c(self) -> _lib.Geom:
+        return _lib.geom(self.B, self.H, self.D, self.T, self.Y, self.X)
+
+    @property
+    def L(self) -> int:
+        return self.T * self.Y * self.X
+
+    @property
+    def num_tiles(self) -> int:
+        return attn_geometry(self)[0]
+
+    @property
+    def Lpad(self) -> int:
+        return attn_geometry(self)[1]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} (contiguous={t.is_contiguous()}, "
+                         f"device={t.device})")
+
+
+def attn_geometry(g: Geometry, with_occupancy: bool = False):
+    """(Nt, Lpad[, occupancy list]) computed by the library on the host."""
+    lib = _lib.load()
+    nt = ctypes.c_int32()
+    lpad = ctypes.c_int64()
+    _lib.check(lib.attn_geometry(ctypes.byref(g.c), ctypes.byref(nt), ctypes.byref(lpad), None))
+    if not with_occupancy:
+        return nt.value, lpad.value
+    occ = (ctypes.c_int32 * nt.value)()
+    _lib.check(lib.attn_geometry(ctypes.byref(g.c), None, None, occ))
+    return nt.value, lpad.value, list(occ)
+
+
+def _windows_arg(windows):
+    if windows is None:
+        return None, None
+    flat = [int(v) for row in windows for v in row]
+    arr = (ctypes.c_int32 * len(flat))(*flat)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def attn_select_capacity(g: Geometry, mode: int, topk: int = 0, windows=None) -> int:
+    lib = _lib.load()
+    _keep, w = _windows_arg(windows)
+    return _lib.check(lib.attn_select_capacity(ctypes.byref(g.c), mode, topk, w))
+
+
+def attn_workspace_bytes(g: Geometry, mode: int) -> int:
+    return _lib.check(_lib.load().attn_workspace_bytes(ctypes.byref(g.c), mode))
+
+
+def attn_tile(g: Geometry, x, out=None):
+    torch = _torch()
+    _expect(x, (g.B, g.L, g.H, g.D), torch.bfloat16, "x")
+    lpad = attn_geometry(g)[1]
+    if out is None:
+        out = torch.empty((g.B, lpad, g.H, g.D), dtype=torch.bfloat16, device=x.device)
+    _expect(out, (g.B, lpad, g.H, g.D), torch.bfloat16, "x_tiled")
+    _lib.check(_lib.load().attn_tile(ctypes.byref(g.c), _ptr(x), _ptr(out), _stream()))
+    return out
+
+
+def attn_untile(g: Geometry, y_tiled, out=None):
+    torch = _torch()
+    lpad = attn_geometry(g)[1]
+    _expect(y_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "y_tiled")
+    if out is None:
+        out = torch.empty((g.B, g.L, g.H, g.D), dtype=torch.bfloat16, device=y_tiled.device)
+    _expect(out, (g.B, g.L, g.H, g.D), torch.bfloat16, "y")
+    _lib.check(_lib.load().attn_untile(ctypes.byref(g.c), _ptr(y_tiled), _ptr(out), _stream()))
+    return out
+
+
+@dataclasses.dataclass
+class Selection:
+    row_ptr: object        # int32 [B*H*Nt + 1]
+    col_idx: object        # int32 [nnz]
+    block_mask: object     # uint8 [B, H, Nt, Nt] or None
+    workspace: object      # fp32 workspace (pooled Q, K, scores) or None
+
+    def pooled(self, g: Geometry):
+        """Views of the pooled Q and K (fp32 [B, H, Nt, D]) left in the workspace."""
+        nt = attn_geometry(g)[0]
+        n = g.B * g.H * nt * g.D
+        ws = self.workspace
+        return ws[:n].view(g.B, g.H, nt, g.D), ws[n:2 * n].view(g.B, g.H, nt, g.D)
+
+    def scores(self, g: Geometry):
+        nt = attn_geometry(g)[0]
+        n = g.B * g.H * nt * g.D
+        return self.workspace[2 * n:2 * n + g.B * g.H * nt * nt].view(g.B, g.H, nt, nt)
+
+
+def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, topk: int = 0,
+                       windows: Optional[Sequence[Sequence[int]]] = None, want_mask: bool = True,
+                       out: Optional[Selection] = None) -> Selection:
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    dev = (q_tiled if q_tiled is not None else torch.empty(0, device="cuda")).device
+    if mode == SELECT_TOPK:
+        _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
+        _expect(k_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "k_tiled")
+    cap = attn_select_capacity(g, mode, topk, windows)
+    wsb = attn_workspace_bytes(g, mode)
+    if out is None:
+        out = Selection(
+            row_ptr=torch.empty(g.B * g.H * nt + 1, dtype=torch.int32, device=dev),
+            col_idx=torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+            block_mask=(torch.empty((g.B, g.H, nt, nt), dtype=torch.uint8, device=dev)
+                        if want_mask else None),
+            workspace=(torch.empty(wsb // 4, dtype=torch.float32, device=dev) if wsb > 0 else None))
+    _keep, w = _windows_arg(windows)
+    ws = out.workspace
+    status = _lib.load().attn_select_blocks(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), mode, topk, w, _ptr(out.block_mask),
+        _ptr(out.row_ptr), _ptr(out.col_idx), out.col_idx.numel(), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _lib.check(status)
+    return out
+
+
+def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
+                          softmax_scale: Optional[float] = None, causal: bool = False,
+                          out=None, lse=None, want_lse: bool = False):
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    for name, t in (("q_tiled", q_tiled), ("k_tiled", k_tiled), ("v_tiled", v_tiled)):
+        _expect(t, (g.B, lpad, g.H, g.D), torch.bfloat16, name)
+    _expect(row_ptr, (g.B * g.H * nt + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
+        raise ValueError("col_idx: expected contiguous int32")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(g.D)
+    if out is None:
+        out = torch.empty_like(q_tiled)
+    _expect(out, (g.B, lpad, g.H, g.D), torch.bfloat16, "o_tiled")
+    if lse is None and want_lse:
+        lse = torch.empty((g.B, g.H, lpad), dtype=torch.float32, device=q_tiled.device)
+    _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
+    _lib.check(_lib.load().attn_block_sparse_fwd(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(row_ptr),
+        _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(out),
+        _ptr(lse), _stream()))
+    return (out, lse) if want_lse or lse is not None else out
+
+
+def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
+                           windows=None):
+    """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile."""
+    qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
+    sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
+    ot = attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx)
+    return attn_untile(g, ot)

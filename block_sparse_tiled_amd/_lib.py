@@ -1,0 +1,88 @@
+"""ctypes binding of libbsta.so (argument marshalling only).
+
+Every function here forwards to the C ABI declared in include/bsta.h with
+the same name.  Tensors are torch tensors on a ROCm device; only their data
+pointers, the geometry and the current HIP stream cross the boundary.  A
+non-zero status raises BstaError carrying attn_last_error().  There is no
+fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsta.so")
+
+BSTA_OK = 0
+BSTA_ERR_NULL = -1
+BSTA_ERR_SHAPE = -2
+BSTA_ERR_UNSUPPORTED = -3
+BSTA_ERR_CAPACITY = -4
+BSTA_ERR_HIP = -5
+SELECT_TOPK = 0
+SELECT_STA = 1
+MAX_STA_HEADS = 256
+
+EXPORTS = (
+    "attn_geometry", "attn_tile", "attn_untile", "attn_select_capacity",
+    "attn_workspace_bytes", "attn_select_blocks", "attn_block_sparse_fwd",
+    "attn_status_string", "attn_last_error",
+)
+
+
+class BstaError(ValueError):
+    """A libbsta call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "H", "D", "T", "Y", "X", "tile_t", "tile_y", "tile_x")]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbsta.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    G = ctypes.POINTER(Geom)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "attn_geometry": (i32, [G, ctypes.POINTER(i32), ctypes.POINTER(i64), P]),
+        "attn_tile": (i32, [G, P, P, P]),
+        "attn_untile": (i32, [G, P, P, P]),
+        "attn_select_capacity": (i64, [G, i32, i32, P]),
+        "attn_workspace_bytes": (i64, [G, i32]),
+        "attn_select_blocks": (i32, [G, P, P, i32, i32, P, P, P, P, i64, P, i64, P]),
+        "attn_block_sparse_fwd": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P]),
+        "attn_status_string": (ctypes.c_char_p, [i32]),
+        "attn_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> int:
+    if status < 0:
+        lib = load()
+        raise BstaError(int(status), lib.attn_last_error().decode())
+    return status
+
+
+def geom(B, H, D, T, Y, X) -> Geom:
+    return Geom(int(B), int(H), int(D), int(T), int(Y), int(X), 4, 4, 4)

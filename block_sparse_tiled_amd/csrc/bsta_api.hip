@@ -1,0 +1,278 @@
+// C ABI of libbsta.so: argument checks, geometry, and kernel launches.
+//
+// Every entry point validates on the host before touching HIP, so the checks
+// (and the host-only helpers) work on a machine without a GPU.  Argument
+// rules follow the "bsa_attn" page (__init__: no grouped-query attention, no
+// causal mode, scale must be 1/sqrt(d) within rel 1e-4 / abs 1e-5; forward:
+// sequence length must match the tiling) and the "video_sparse_attn_h3" page
+// (tile(): ValueError on a sequence-length mismatch; build(): tile size from
+// a fixed registry).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bsta_common.hpp"
+
+namespace bsta {
+hipError_t launch_permute(const Geo& g, const void* src, void* dst, bool to_tiles,
+                          hipStream_t stream);
+hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
+                       hipStream_t stream);
+hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,
+                         hipStream_t stream);
+hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32_t* row_ptr,
+                       int32_t* col_idx, hipStream_t stream);
+hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32_t* row_ptr,
+                      int32_t* col_idx, hipStream_t stream);
+hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
+                           const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                           float scale, void* o, float* lse, hipStream_t stream);
+}  // namespace bsta
+
+using bsta::Geo;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+// Largest tile count top-k selection accepts (its per-row keys and flags
+// live in LDS: 5 bytes per tile).
+constexpr int kMaxTopkTiles = 12288;
+// Largest grid side (tile coordinates travel as int16 in window mode).
+constexpr int kMaxDim = 1 << 15;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t ok() {
+    g_err[0] = '\0';
+    return BSTA_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(BSTA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Validate a geometry and fill the derived fields.
+int32_t make_geo(const bsta_geom* in, Geo* g) {
+    if (in == nullptr) return fail(BSTA_ERR_NULL, "geometry pointer is NULL");
+    if (in->tile_t != 4 || in->tile_y != 4 || in->tile_x != 4)
+        return fail(BSTA_ERR_UNSUPPORTED, "tile %dx%dx%d unsupported: only 4x4x4 (64 tokens)",
+                    in->tile_t, in->tile_y, in->tile_x);
+    if (in->D != 64 && in->D != 128)
+        return fail(BSTA_ERR_UNSUPPORTED, "head dim D=%d unsupported: must be 64 or 128", in->D);
+    if (in->B < 1 || in->H < 1 || in->T < 1 || in->Y < 1 || in->X < 1)
+        return fail(BSTA_ERR_SHAPE, "B=%d H=%d T=%d Y=%d X=%d: all must be >= 1", in->B, in->H,
+                    in->T, in->Y, in->X);
+    if (in->T > kMaxDim || in->Y > kMaxDim || in->X > kMaxDim)
+        return fail(BSTA_ERR_SHAPE, "grid side above %d", kMaxDim);
+    g->B = in->B;
+    g->H = in->H;
+    g->D = in->D;
+    g->T = in->T;
+    g->Y = in->Y;
+    g->X = in->X;
+    g->nT = (in->T + 3) / 4;
+    g->nY = (in->Y + 3) / 4;
+    g->nX = (in->X + 3) / 4;
+    const int64_t nt = (int64_t)g->nT * g->nY * g->nX;
+    if (nt > (1 << 26)) return fail(BSTA_ERR_SHAPE, "tile count %lld too large", (long long)nt);
+    g->Nt = (int32_t)nt;
+    g->L = (int64_t)in->T * in->Y * in->X;
+    g->Lpad = nt * 64;
+    // Offsets are 64-bit in the kernels; keep every element count well
+    // inside int64 and grid sizes inside 32 bits.
+    const double elems = (double)g->B * (double)g->Lpad * (double)g->H * (double)g->D;
+    if (elems > 9.0e15) return fail(BSTA_ERR_SHAPE, "tensor too large");
+    if ((double)g->B * g->H * g->Nt * 8.0 > 4.0e9)
+        return fail(BSTA_ERR_SHAPE, "B*H*Nt too large for one launch");
+    return BSTA_OK;
+}
+
+int32_t check_windows(const Geo& g, const int32_t* w, int64_t* per_batch) {
+    if (w == nullptr) return fail(BSTA_ERR_NULL, "sta_windows_host is NULL in window mode");
+    if (g.H > BSTA_MAX_STA_HEADS)
+        return fail(BSTA_ERR_SHAPE, "H=%d above %d heads in window mode", g.H, BSTA_MAX_STA_HEADS);
+    int64_t sum = 0;
+    const int n[3] = {g.nT, g.nY, g.nX};
+    for (int h = 0; h < g.H; ++h) {
+        int64_t prod = 1;
+        for (int ax = 0; ax < 3; ++ax) {
+            const int v = w[3 * h + ax];
+            if (v < 1 || v > n[ax])
+                return fail(BSTA_ERR_SHAPE, "head %d window %d,%d,%d outside tile grid %d,%d,%d", h,
+                            w[3 * h], w[3 * h + 1], w[3 * h + 2], n[0], n[1], n[2]);
+            prod *= v;
+        }
+        sum += prod;
+    }
+    *per_batch = sum;
+    return BSTA_OK;
+}
+
+// CSR entry count of a selection, or a negative status.
+int64_t capacity_of(const Geo& g, int32_t mode, int32_t topk, const int32_t* windows) {
+    int64_t nnz;
+    if (mode == BSTA_SELECT_TOPK) {
+        if (topk < 1 || topk > g.Nt)
+            return fail(BSTA_ERR_SHAPE, "topk=%d outside [1, Nt=%d]", topk, g.Nt);
+        nnz = (int64_t)g.B * g.H * g.Nt * topk;
+    } else if (mode == BSTA_SELECT_STA) {
+        int64_t per_batch = 0;
+        int32_t st = check_windows(g, windows, &per_batch);
+        if (st != BSTA_OK) return st;
+        nnz = (int64_t)g.B * g.Nt * per_batch;
+    } else {
+        return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode);
+    }
+    if (nnz > 0x7fffffffLL)
+        return fail(BSTA_ERR_SHAPE, "%lld CSR entries overflow int32 row_ptr", (long long)nnz);
+    return nnz;
+}
+
+int64_t workspace_of(const Geo& g, int32_t mode) {
+    if (mode == BSTA_SELECT_STA) return 0;
+    if (mode != BSTA_SELECT_TOPK) return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode);
+    const int64_t pooled = (int64_t)2 * g.B * g.H * g.Nt * g.D;
+    const int64_t scores = (int64_t)g.B * g.H * g.Nt * g.Nt;
+    return (pooled + scores) * (int64_t)sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int32_t status) {
+    switch (status) {
+        case BSTA_OK: return "ok";
+        case BSTA_ERR_NULL: return "null pointer";
+        case BSTA_ERR_SHAPE: return "shape or size outside the specification";
+        case BSTA_ERR_UNSUPPORTED: return "unsupported argument";
+        case BSTA_ERR_CAPACITY: return "output or workspace too small";
+        case BSTA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int32_t attn_geometry(const bsta_geom* gin, int32_t* num_tiles, int64_t* padded_len,
+                      int32_t* occupancy) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (num_tiles) *num_tiles = g.Nt;
+    if (padded_len) *padded_len = g.Lpad;
+    if (occupancy)
+        for (int j = 0; j < g.Nt; ++j) occupancy[j] = bsta::tile_occupancy(g, j);
+    return ok();
+}
+
+int64_t attn_select_capacity(const bsta_geom* gin, int32_t mode, int32_t topk,
+                             const int32_t* sta_windows_host) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    int64_t n = capacity_of(g, mode, topk, sta_windows_host);
+    if (n >= 0) ok();
+    return n;
+}
+
+int64_t attn_workspace_bytes(const bsta_geom* gin, int32_t mode) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    int64_t n = workspace_of(g, mode);
+    if (n >= 0) ok();
+    return n;
+}
+
+int32_t attn_tile(const bsta_geom* gin, const void* x, void* x_tiled, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (x == nullptr || x_tiled == nullptr) return fail(BSTA_ERR_NULL, "attn_tile: NULL tensor");
+    return hip_status(bsta::launch_permute(g, x, x_tiled, true, (hipStream_t)stream), "attn_tile");
+}
+
+int32_t attn_untile(const bsta_geom* gin, const void* y_tiled, void* y, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (y == nullptr || y_tiled == nullptr) return fail(BSTA_ERR_NULL, "attn_untile: NULL tensor");
+    return hip_status(bsta::launch_permute(g, y_tiled, y, false, (hipStream_t)stream),
+                      "attn_untile");
+}
+
+int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
+                           int32_t mode, int32_t topk, const int32_t* sta_windows_host,
+                           uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (row_ptr == nullptr || col_idx == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_select_blocks: NULL row_ptr or col_idx");
+    const int64_t need = capacity_of(g, mode, topk, sta_windows_host);
+    if (need < 0) return (int32_t)need;
+    if (col_capacity < need)
+        return fail(BSTA_ERR_CAPACITY, "col_capacity %lld < %lld entries needed",
+                    (long long)col_capacity, (long long)need);
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == BSTA_SELECT_STA)
+        return hip_status(bsta::launch_sta(g, sta_windows_host, block_mask, row_ptr, col_idx, s),
+                          "attn_select_blocks(window)");
+    if (q_tiled == nullptr || k_tiled == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_select_blocks: NULL q_tiled or k_tiled in top-k mode");
+    if (g.Nt > kMaxTopkTiles)
+        return fail(BSTA_ERR_SHAPE, "top-k selection supports at most %d tiles, got %d",
+                    kMaxTopkTiles, g.Nt);
+    const int64_t ws = workspace_of(g, mode);
+    if (workspace == nullptr) return fail(BSTA_ERR_NULL, "attn_select_blocks: NULL workspace");
+    if (workspace_bytes < ws)
+        return fail(BSTA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                    (long long)workspace_bytes, (long long)ws);
+    float* pq = (float*)workspace;
+    float* pk = pq + (int64_t)g.B * g.H * g.Nt * g.D;
+    float* sc = pk + (int64_t)g.B * g.H * g.Nt * g.D;
+    hipError_t e = bsta::launch_pool(g, q_tiled, k_tiled, pq, pk, s);
+    if (e == hipSuccess) e = bsta::launch_scores(g, pq, pk, sc, s);
+    if (e == hipSuccess) e = bsta::launch_topk(g, topk, sc, block_mask, row_ptr, col_idx, s);
+    return hip_status(e, "attn_select_blocks(top-k)");
+}
+
+int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
+                              const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_len, float softmax_scale, int32_t causal,
+                              void* o_tiled, float* lse, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o_tiled == nullptr ||
+        row_ptr == nullptr || col_idx == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd: NULL tensor or index pointer");
+    if (causal != 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "causal=%d: block-sparse attention is bidirectional only",
+                    causal);
+    const double expected = 1.0 / sqrt((double)g.D);
+    const double diff = fabs((double)softmax_scale - expected);
+    const double tol = fmax(1e-4 * fmax(fabs((double)softmax_scale), expected), 1e-5);
+    if (!(diff <= tol))
+        return fail(BSTA_ERR_UNSUPPORTED, "softmax_scale %g must be 1/sqrt(D) = %g",
+                    (double)softmax_scale, expected);
+    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
+    return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
+                                            col_len, softmax_scale, o_tiled, lse,
+                                            (hipStream_t)stream),
+                      "attn_block_sparse_fwd");
+}
+
+}  // extern "C"

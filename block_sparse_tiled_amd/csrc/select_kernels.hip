@@ -1,0 +1,333 @@
+// Coarse stage kernels: per-tile mean pooling, pooled scores, per-row top-k
+// with CSR output, and sliding-tile-window (STA) CSR.
+//
+// Method ("sla" page, get_block_map / mean_pool): Q and K are mean-pooled
+// per tile, the score of query tile i against key tile j is the dot product
+// of the pooled vectors (no scale), and every query tile keeps its k best key
+// tiles.  Window mode follows the "STA_configuration" page: a window is a
+// count of tiles along t, h, w, and every query tile is charged
+// prod(window) tiles.  The CSR form is the map_to_index step of the
+// "video_sparse_attn_h3" page.
+//
+// Precision: pooled vectors are fp32 sums of the valid bf16 rows in row
+// order, divided by the valid count; scores are fp32 dot products summed in
+// d order.  Selection is exact on those scores: radix select on
+// order-preserving 32-bit keys, equal keys resolved toward the lower index.
+#include "bsta_common.hpp"
+
+namespace bsta {
+
+// ------------------------------------------------------------------ pooling
+// grid (B*Nt, 2): one workgroup per (batch, tile, tensor).  Each thread owns
+// eight consecutive (head, d) columns and sums the tile's valid rows.
+__global__ __launch_bounds__(256) void pool_kernel(
+        Geo g, const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+        float* __restrict__ pq, float* __restrict__ pk) {
+    const int b = blockIdx.x / g.Nt;
+    const int j = blockIdx.x - b * g.Nt;
+    const u32x4* src = blockIdx.y ? k : q;
+    float* dst = blockIdx.y ? pk : pq;
+    const int n = tile_occupancy(g, j);
+    const int nvec = g.H * g.D / 8;
+    const u32x4* base = src + ((int64_t)b * g.Lpad + (int64_t)j * kTileElems) * nvec;
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int r = 0;
+        for (; r + 8 <= n; r += 8) {
+            u32x4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = base[(int64_t)(r + u) * nvec + v];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[2 * c] += __uint_as_float(w[u][c] << 16);
+                    acc[2 * c + 1] += __uint_as_float(w[u][c] & 0xffff0000u);
+                }
+            }
+        }
+        for (; r < n; ++r) {
+            u32x4 w = base[(int64_t)r * nvec + v];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[2 * c] += __uint_as_float(w[c] << 16);
+                acc[2 * c + 1] += __uint_as_float(w[c] & 0xffff0000u);
+            }
+        }
+        const int col = v * 8;
+        const int h = col / g.D;
+        const int d0 = col - h * g.D;
+        float* out = dst + (((int64_t)b * g.H + h) * g.Nt + j) * g.D + d0;
+        // Divide (not multiply by 1/n) for the correctly rounded quotient.
+        const float fn = (float)n;
+        f32x4 lo = {acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn};
+        f32x4 hi = {acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn};
+        *(f32x4*)out = lo;
+        *(f32x4*)(out + 4) = hi;
+    }
+}
+
+// ------------------------------------------------------------------ scores
+// S[bh] = Pq[bh] Pk[bh]^T, fp32, [Nt, Nt] per (batch, head).  64x64 output
+// tile per workgroup, 4x4 per thread, D staged through LDS in chunks of 32.
+constexpr int kScoreTile = 64;
+constexpr int kScoreKc = 32;
+
+__global__ __launch_bounds__(256) void score_kernel(
+        int Nt, int D, const float* __restrict__ pq, const float* __restrict__ pk,
+        float* __restrict__ s) {
+    __shared__ float As[kScoreKc][kScoreTile + 4];
+    __shared__ float Bs[kScoreKc][kScoreTile + 4];
+    // 1-D grid: blockIdx.x = (bh * nb + bi) * nb + bj.
+    const int nb = (Nt + kScoreTile - 1) / kScoreTile;
+    const int bj = blockIdx.x % nb;
+    const int rest = blockIdx.x / nb;
+    const int bi = rest % nb;
+    const int bh = rest / nb;
+    const int i0 = bi * kScoreTile;
+    const int j0 = bj * kScoreTile;
+    const float* A = pq + (int64_t)bh * Nt * D;
+    const float* Bm = pk + (int64_t)bh * Nt * D;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+    for (int d0 = 0; d0 < D; d0 += kScoreKc) {
+        // 64 rows x 32 d of each operand: 2048 floats, 8 per thread.
+        for (int e = threadIdx.x; e < kScoreTile * kScoreKc; e += 256) {
+            int row = e / kScoreKc, dd = e - row * kScoreKc;
+            int ia = i0 + row, jb = j0 + row;
+            As[dd][row] = ia < Nt ? A[(int64_t)ia * D + d0 + dd] : 0.f;
+            Bs[dd][row] = jb < Nt ? Bm[(int64_t)jb * D + d0 + dd] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int dd = 0; dd < kScoreKc; ++dd) {
+            f32x4 a = *(const f32x4*)&As[dd][ty * 4];
+            f32x4 bv = *(const f32x4*)&Bs[dd][tx * 4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w] = __builtin_fmaf(a[u], bv[w], acc[u][w]);
+        }
+        __syncthreads();
+    }
+    float* out = s + (int64_t)bh * Nt * Nt;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        int i = i0 + ty * 4 + u;
+        if (i >= Nt) continue;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            int j = j0 + tx * 4 + w;
+            if (j < Nt) out[(int64_t)i * Nt + j] = acc[u][w];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ top-k
+// Order-preserving key of an fp32 score (-0 folded onto +0).
+__device__ inline uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the 256 threads of a workgroup; *total gets the sum.
+__device__ inline int block_exclusive_scan(int x, int* smem4, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) smem4[wave] = incl;
+    __syncthreads();
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        int t = smem4[w];
+        before += (w < wave) ? t : 0;
+        sum += t;
+    }
+    __syncthreads();
+    *total = sum;
+    return before + incl - x;
+}
+
+// One workgroup per CSR row (b, h, i).  Keys live in LDS (Nt * 4 bytes),
+// selection flags after them (Nt bytes).
+__global__ __launch_bounds__(256) void topk_kernel(
+        int Nt, int k, int64_t rows, const float* __restrict__ s,
+        uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr,
+        int32_t* __restrict__ col_idx) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* keys = smem;
+    uint8_t* flags = (uint8_t*)(keys + Nt);
+    __shared__ int hist[256];
+    __shared__ int scan4[4];
+    __shared__ int sel_digit, sel_rest;
+
+    const int64_t row = blockIdx.x;
+    const float* srow = s + row * Nt;
+    for (int j = threadIdx.x; j < Nt; j += 256) keys[j] = score_key(srow[j]);
+
+    uint32_t prefix = 0, pmask = 0;
+    int kk = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+        for (int j = threadIdx.x; j < Nt; j += 256) {
+            uint32_t key = keys[j];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // Count of keys whose digit is >= this thread's digit (suffix sum).
+        const int c = hist[threadIdx.x];
+        int tot;
+        const int excl = block_exclusive_scan(c, scan4, &tot);
+        const int at_or_above = tot - excl;
+        const int above = at_or_above - c;
+        if (c > 0 && above < kk && kk <= at_or_above) {
+            sel_digit = threadIdx.x;
+            sel_rest = kk - above;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sel_digit << shift;
+        pmask |= 255u << shift;
+        kk = sel_rest;
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;  // key of the k-th largest score
+    const int take_eq = kk;        // how many keys equal to thr are kept
+
+    // Contiguous chunk of j per thread so that prefix sums follow j order.
+    const int chunk = (Nt + 255) / 256;
+    const int j0 = min(Nt, (int)threadIdx.x * chunk);
+    const int j1 = min(Nt, j0 + chunk);
+    int eq = 0;
+    for (int j = j0; j < j1; ++j) eq += keys[j] == thr;
+    int dummy;
+    int eq_before = block_exclusive_scan(eq, scan4, &dummy);
+    int nsel = 0;
+    for (int j = j0; j < j1; ++j) {
+        uint32_t key = keys[j];
+        bool sel = key > thr;
+        if (key == thr) {
+            sel = eq_before < take_eq;
+            ++eq_before;
+        }
+        flags[j] = sel;
+        nsel += sel;
+    }
+    int pos = block_exclusive_scan(nsel, scan4, &dummy);
+    int32_t* out = col_idx + row * k;
+    for (int j = j0; j < j1; ++j)
+        if (flags[j] && pos < k) out[pos++] = j;
+    __syncthreads();
+    if (mask) {
+        uint8_t* mrow = mask + row * Nt;
+        for (int j = threadIdx.x; j < Nt; j += 256) mrow[j] = flags[j];
+    }
+    if (threadIdx.x == 0) {
+        row_ptr[row] = (int32_t)(row * k);
+        if (row == rows - 1) row_ptr[rows] = (int32_t)(rows * k);
+    }
+}
+
+// ------------------------------------------------------------------ STA
+struct StaArgs {
+    int16_t win[BSTA_MAX_STA_HEADS][3];
+    int32_t head_prefix[BSTA_MAX_STA_HEADS + 1];  // sum of prod(window) over heads < h
+};
+
+__device__ inline int sta_start(int a, int w, int n) {
+    int s = a - w / 2;
+    s = s < 0 ? 0 : s;
+    return s > n - w ? n - w : s;
+}
+
+// One workgroup per CSR row.
+__global__ __launch_bounds__(256) void sta_kernel(
+        Geo g, StaArgs args, uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr,
+        int32_t* __restrict__ col_idx) {
+    const int64_t row = blockIdx.x;
+    const int i = (int)(row % g.Nt);
+    const int64_t bh = row / g.Nt;
+    const int h = (int)(bh % g.H);
+    const int64_t b = bh / g.H;
+    const int wt = args.win[h][0], wy = args.win[h][1], wx = args.win[h][2];
+    const int cnt = wt * wy * wx;
+    const int64_t per_batch = (int64_t)args.head_prefix[g.H] * g.Nt;
+    const int64_t start = b * per_batch + (int64_t)args.head_prefix[h] * g.Nt + (int64_t)i * cnt;
+    TileInfo ti = tile_info(g, i);
+    const int sa = sta_start(ti.a, wt, g.nT);
+    const int sb = sta_start(ti.b, wy, g.nY);
+    const int sc = sta_start(ti.c, wx, g.nX);
+    for (int e = threadIdx.x; e < cnt; e += 256) {
+        int dx = e % wx;
+        int r = e / wx;
+        int dy = r % wy;
+        int dt = r / wy;
+        col_idx[start + e] = ((sa + dt) * g.nY + (sb + dy)) * g.nX + (sc + dx);
+    }
+    if (mask) {
+        uint8_t* mrow = mask + row * g.Nt;
+        for (int j = threadIdx.x; j < g.Nt; j += 256) {
+            TileInfo tj = tile_info(g, j);
+            bool in = tj.a >= sa && tj.a < sa + wt && tj.b >= sb && tj.b < sb + wy &&
+                      tj.c >= sc && tj.c < sc + wx;
+            mrow[j] = in;
+        }
+    }
+    if (threadIdx.x == 0) {
+        row_ptr[row] = (int32_t)start;
+        const int64_t rows = (int64_t)g.B * g.H * g.Nt;
+        if (row == rows - 1) row_ptr[rows] = (int32_t)(g.B * per_batch);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(g.B * g.Nt), 2), dim3(256), 0, stream, g,
+                       (const u32x4*)q, (const u32x4*)k, pq, pk);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,
+                         hipStream_t stream) {
+    const int nb = (g.Nt + kScoreTile - 1) / kScoreTile;
+    const int64_t blocks = (int64_t)nb * nb * g.B * g.H;
+    hipLaunchKernelGGL(score_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g.Nt, g.D,
+                       pq, pk, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32_t* row_ptr,
+                       int32_t* col_idx, hipStream_t stream) {
+    const int64_t rows = (int64_t)g.B * g.H * g.Nt;
+    const size_t lds = (size_t)g.Nt * 5 + 16;
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), lds, stream, g.Nt, k, rows,
+                       s, mask, row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32_t* row_ptr,
+                      int32_t* col_idx, hipStream_t stream) {
+    StaArgs args = {};
+    int32_t acc = 0;
+    for (int h = 0; h < g.H; ++h) {
+        args.win[h][0] = (int16_t)windows[3 * h];
+        args.win[h][1] = (int16_t)windows[3 * h + 1];
+        args.win[h][2] = (int16_t)windows[3 * h + 2];
+        args.head_prefix[h] = acc;
+        acc += windows[3 * h] * windows[3 * h + 1] * windows[3 * h + 2];
+    }
+    args.head_prefix[g.H] = acc;
+    const int64_t rows = (int64_t)g.B * g.H * g.Nt;
+    hipLaunchKernelGGL(sta_kernel, dim3((unsigned)rows), dim3(256), 0, stream, g, args, mask,
+                       row_ptr, col_idx);
+    return hipGetLastError();
+}
+
+}  // namespace bsta

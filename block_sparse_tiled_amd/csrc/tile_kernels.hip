@@ -1,0 +1,84 @@
+// Tile permutation kernels: raster [B,L,H,D] <-> zero-padded tile order
+// [B,Lpad,H,D] ("bsa_attn" page: preprocess_qkv / postprocess_output with
+// get_tile_partition_indices and its inverse; "video_sparse_attn_h3" page:
+// tile() keeps pad positions zero).
+//
+// Both layouts keep a token's H*D row contiguous, so each kernel is a row
+// gather: one output row per token slot, copied in 16-byte vectors.  The
+// slot <-> token map is computed in closed form per row (no index tensor).
+// HBM bound: read L rows, write Lpad rows (tile) or the reverse (untile).
+#include "bsta_common.hpp"
+
+namespace bsta {
+
+// Raster token of slot s (s in [0, Lpad)), or -1 for a pad slot.
+__device__ inline int64_t slot_to_token(const Geo& g, int64_t s) {
+    int j = (int)(s >> 6);
+    int r = (int)(s & 63);
+    TileInfo t = tile_info(g, j);
+    if (r >= t.n) return -1;
+    int plane = t.sy * t.sx;
+    int dt = r / plane;
+    int rem = r - dt * plane;
+    int dy = rem / t.sx;
+    int dx = rem - dy * t.sx;
+    int tt = 4 * t.a + dt, yy = 4 * t.b + dy, xx = 4 * t.c + dx;
+    return ((int64_t)tt * g.Y + yy) * g.X + xx;
+}
+
+// Slot of raster token l.
+__device__ inline int64_t token_to_slot(const Geo& g, int64_t l) {
+    int64_t plane = (int64_t)g.Y * g.X;
+    int tt = (int)(l / plane);
+    int rem = (int)(l - (int64_t)tt * plane);
+    int yy = rem / g.X;
+    int xx = rem - yy * g.X;
+    int a = tt >> 2, b = yy >> 2, c = xx >> 2;
+    int sy = axis_extent(g.Y, b), sx = axis_extent(g.X, c);
+    int j = (a * g.nY + b) * g.nX + c;
+    int r = ((tt & 3) * sy + (yy & 3)) * sx + (xx & 3);
+    return (int64_t)j * kTileElems + r;
+}
+
+// One workgroup copies `rows_per_wg` consecutive output rows; a row is
+// `nvec` 16-byte vectors.  TO_TILES selects the direction.
+template <bool TO_TILES>
+__global__ __launch_bounds__(256) void permute_rows_kernel(
+        Geo g, const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+        int nvec, int rows_per_wg, int64_t total_rows) {
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int work = rows_per_wg * nvec;
+    const int64_t in_rows = TO_TILES ? g.L : g.Lpad;
+    const int64_t out_rows = TO_TILES ? g.Lpad : g.L;
+    for (int e = threadIdx.x; e < work; e += 256) {
+        int rl = e / nvec;
+        int v = e - rl * nvec;
+        int64_t row = row0 + rl;
+        if (row >= total_rows) break;
+        int64_t b = row / out_rows;
+        int64_t pos = row - b * out_rows;
+        int64_t from = TO_TILES ? slot_to_token(g, pos) : token_to_slot(g, pos);
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (from >= 0) val = __builtin_nontemporal_load(&src[(b * in_rows + from) * nvec + v]);
+        dst[row * nvec + v] = val;
+    }
+}
+
+hipError_t launch_permute(const Geo& g, const void* src, void* dst, bool to_tiles,
+                          hipStream_t stream) {
+    const int nvec = g.H * g.D / 8;
+    const int64_t total_rows = (int64_t)g.B * (to_tiles ? g.Lpad : g.L);
+    int rows_per_wg = (4096 + nvec - 1) / nvec;  // ~64 KB per workgroup
+    if (rows_per_wg < 1) rows_per_wg = 1;
+    const int64_t blocks = (total_rows + rows_per_wg - 1) / rows_per_wg;
+    if (blocks <= 0) return hipSuccess;
+    if (to_tiles)
+        hipLaunchKernelGGL(permute_rows_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           g, (const u32x4*)src, (u32x4*)dst, nvec, rows_per_wg, total_rows);
+    else
+        hipLaunchKernelGGL(permute_rows_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           g, (const u32x4*)src, (u32x4*)dst, nvec, rows_per_wg, total_rows);
+    return hipGetLastError();
+}
+
+}  // namespace bsta

@@ -1,0 +1,181 @@
+/*
+ * bsta.h -- block-sparse tiled video attention on MI355X (gfx950).
+ *
+ * C ABI of libbsta.so.  The path, in call order:
+ *
+ *   attn_tile            raster [B,L,H,D] -> zero-padded tile order [B,Lpad,H,D]
+ *   attn_select_blocks   per-tile mean pooling of Q and K, pooled scores, top-k
+ *                        key tiles per query tile (or a sliding tile window),
+ *                        block mask and CSR index map
+ *   attn_block_sparse_fwd  softmax(q k^T / sqrt(D)) v over the selected tiles
+ *   attn_untile          tile order -> raster order
+ *
+ * Conventions shared by every call:
+ *   - Tensors are bfloat16, contiguous, in the layout [B, L, H, D] that the
+ *     FastVideo attention backends use ("bsa_attn" page, forward: query, key
+ *     and value are [B, L, num_heads, D]).  Q, K and V share H: grouped-query
+ *     attention is not expressible.
+ *   - The latent grid is (T, Y, X) with L = T*Y*X tokens in raster order
+ *     (token l = (t*Y + y)*X + x).  Tiles are 4x4x4 = 64 tokens; there are
+ *     Nt = ceil(T/4)*ceil(Y/4)*ceil(X/4) tiles and Lpad = 64*Nt slots.
+ *   - Every tensor, mask and index pointer is a DEVICE pointer unless its
+ *     comment says host.  The caller allocates and owns all memory and the
+ *     stream.  The library allocates nothing, frees nothing, never
+ *     synchronises, keeps no device state, and enqueues every kernel on the
+ *     given stream (a hipStream_t passed as void*; NULL = the null stream).
+ *   - Every call checks its arguments on the host before any HIP call and
+ *     returns a status (0 = BSTA_OK).  On failure nothing is enqueued and
+ *     attn_last_error() returns a thread-local message with the detail.
+ *     A failed launch returns BSTA_ERR_HIP.
+ */
+#ifndef BSTA_H
+#define BSTA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem geometry.  D must be 64 or 128; tile_t = tile_y = tile_x = 4. */
+typedef struct bsta_geom {
+    int32_t B, H, D;            /* batch, heads, head dim                  */
+    int32_t T, Y, X;            /* latent token grid                       */
+    int32_t tile_t, tile_y, tile_x;
+} bsta_geom;
+
+enum {
+    BSTA_OK = 0,
+    BSTA_ERR_NULL = -1,         /* a required pointer is NULL               */
+    BSTA_ERR_SHAPE = -2,        /* sizes, k or a window outside the spec    */
+    BSTA_ERR_UNSUPPORTED = -3,  /* causal, a non-default scale, D, tile     */
+    BSTA_ERR_CAPACITY = -4,     /* an output or workspace is too small      */
+    BSTA_ERR_HIP = -5           /* a HIP launch failed                      */
+};
+
+enum { BSTA_SELECT_TOPK = 0, BSTA_SELECT_STA = 1 };
+
+/* Largest head count a sliding-tile-window call accepts (windows travel as
+ * kernel arguments). */
+#define BSTA_MAX_STA_HEADS 256
+
+/*
+ * attn_geometry (host only, no HIP call).
+ * Tile counts and valid tokens per tile, as the "video_sparse_attn" page's
+ * construct_variable_block_sizes defines them: per axis ceil(dim/4) tiles,
+ * the last one keeping the remainder; the count of a tile is the product of
+ * its three extents; tiles are numbered j = (a*nY + b)*nX + c.
+ *   num_tiles  [out, host, may be NULL]  Nt
+ *   padded_len [out, host, may be NULL]  Lpad = 64*Nt
+ *   occupancy  [out, host int32 [Nt], may be NULL]  valid tokens of tile j
+ */
+int32_t attn_geometry(const bsta_geom* g, int32_t* num_tiles, int64_t* padded_len,
+                      int32_t* occupancy);
+
+/*
+ * attn_tile: raster -> tile order ("bsa_attn" page, preprocess_qkv and
+ * get_tile_partition_indices; "video_sparse_attn_h3" page, tile()).
+ *   x        [in]  bf16 [B, L, H, D]
+ *   x_tiled  [out] bf16 [B, Lpad, H, D]
+ * Token (t,y,x) in tile j = (a,b,c) = (t/4, y/4, x/4) goes to slot
+ * 64*j + (dt*s_y + dy)*s_x + dx, where (dt,dy,dx) = (t,y,x) mod 4 and s_y,
+ * s_x are the tile's extents: the valid tokens of a tile come first, in the
+ * row-major order of its clipped sub-block.  Every pad slot is written with
+ * +0.0, so x_tiled needs no clearing and a reused buffer keeps no stale rows.
+ * x and x_tiled must not overlap.
+ */
+int32_t attn_tile(const bsta_geom* g, const void* x, void* x_tiled, void* stream);
+
+/*
+ * attn_untile: tile -> raster order ("bsa_attn" page, postprocess_output and
+ * get_reverse_tile_partition_indices).  Pad slots are dropped.
+ *   y_tiled  [in]  bf16 [B, Lpad, H, D]
+ *   y        [out] bf16 [B, L, H, D]
+ */
+int32_t attn_untile(const bsta_geom* g, const void* y_tiled, void* y, void* stream);
+
+/*
+ * attn_select_capacity (host only): number of CSR entries a selection
+ * produces, B*H*Nt*k for top-k and Nt*B*sum_h prod(window_h) for windows;
+ * a negative status on bad arguments.
+ */
+int64_t attn_select_capacity(const bsta_geom* g, int32_t mode, int32_t topk,
+                             const int32_t* sta_windows_host);
+
+/*
+ * attn_workspace_bytes (host only): bytes of device workspace
+ * attn_select_blocks needs in the given mode (0 for windows; for top-k the
+ * pooled Q and K, fp32 [2, B, H, Nt, D], then the pooled scores fp32
+ * [B, H, Nt, Nt]); a negative status on bad arguments.
+ */
+int64_t attn_workspace_bytes(const bsta_geom* g, int32_t mode);
+
+/*
+ * attn_select_blocks: the coarse stage.
+ * Top-k mode ("sla" page, get_block_map and mean_pool): Pq[b,h,j] and
+ * Pk[b,h,j] are the means of the n_j valid rows of tile j (fp32); the score
+ * of query tile i against key tile j is Pq[i].Pk[j] (no scale); each query
+ * tile keeps the k best key tiles, ties going to the lower index.
+ * Window mode ("STA_configuration" page: a window is a count of tiles along
+ * t, h and w): query tile (a,b,c) of head h keeps the key tiles whose
+ * coordinate on each axis lies in [s, s+w) with s = clamp(a - w/2, 0, n - w)
+ * (integer division), so every row holds prod(window) tiles.
+ * Then map_to_index ("video_sparse_attn_h3" page): row r = (b*H + h)*Nt + i
+ * of the CSR lists the kept key tiles of query tile i in ascending order.
+ *   q_tiled, k_tiled  [in]  bf16 [B, Lpad, H, D] from attn_tile (pad rows 0);
+ *                           unused (may be NULL) in window mode
+ *   mode              BSTA_SELECT_TOPK or BSTA_SELECT_STA
+ *   topk              1 <= k <= Nt (top-k mode)
+ *   sta_windows_host  [in, host int32 [H][3]] windows (window mode),
+ *                     1 <= w <= tiles on that axis; H <= BSTA_MAX_STA_HEADS
+ *   block_mask        [out, uint8 [B, H, Nt, Nt], may be NULL] 1 = kept
+ *   row_ptr           [out, int32 [B*H*Nt + 1]]
+ *   col_idx           [out, int32 [col_capacity]]
+ *   col_capacity      entries col_idx can hold (>= attn_select_capacity)
+ *   workspace         [scratch, >= attn_workspace_bytes; NULL allowed in
+ *                     window mode]; after a top-k call it holds the pooled
+ *                     Q, K and scores described above
+ * Returns BSTA_ERR_CAPACITY when col_capacity or workspace_bytes is short.
+ */
+int32_t attn_select_blocks(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
+                           int32_t mode, int32_t topk, const int32_t* sta_windows_host,
+                           uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
+/*
+ * attn_block_sparse_fwd: fused block-sparse flash attention forward
+ * ("bsa_attn" page, forward and _compute_sparse_attention; __init__ fixes
+ * the scale to 1/sqrt(d) and rejects causal attention).
+ * For every query tile i of head h in batch b and every valid row r < n_i:
+ *   o = softmax(q k^T * softmax_scale) v
+ * over the valid tokens of the key tiles listed in CSR row (b*H + h)*Nt + i.
+ * Rows r >= n_i (padding) are written as +0.0 with lse = -inf; a row whose
+ * CSR list is empty is written the same way.
+ *   q_tiled, k_tiled, v_tiled [in]  bf16 [B, Lpad, H, D], pad rows 0
+ *   row_ptr  [in] int32 [B*H*Nt + 1], non-decreasing
+ *   col_idx  [in] int32 [col_len]; entries must lie in [0, Nt).  The kernel
+ *            clamps row ranges to [0, col_len) and skips out-of-range tile
+ *            ids, so bad indices cannot read outside the tensors.
+ *   softmax_scale  must equal 1/sqrt(D) within rel 1e-4 / abs 1e-5
+ *   causal   must be 0
+ *   o_tiled  [out] bf16 [B, Lpad, H, D]
+ *   lse      [out, fp32 [B, H, Lpad], may be NULL] natural-log softmax
+ *            normaliser of the scaled scores
+ */
+int32_t attn_block_sparse_fwd(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
+                              const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_len, float softmax_scale, int32_t causal,
+                              void* o_tiled, float* lse, void* stream);
+
+/* Text of a status code (static storage). */
+const char* attn_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" when none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSTA_H */

@@ -1,0 +1,100 @@
+"""Helpers shared by the GPU parity tests: device transfer, input cache, and
+the comparison rules (bit-exact maps, tie band for top-k, max/mean-abs for
+attention outputs)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import workloads
+from oracle import select
+
+# Output tolerance for bf16 inputs (max-abs over valid rows, mean-abs).
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+# Top-k sets may differ from the oracle's only where the k-th boundary gap
+# of the oracle's scores is below this.
+TIE_BAND = 1e-4
+# Pooled vectors: |gpu - oracle| <= POOL_TOL * (1 + |oracle|).
+POOL_TOL = 1e-5
+# Log-sum-exp of valid rows (fp32 accumulation of bf16 products).
+LSE_TOL = 2e-3
+
+_cache = {}
+
+
+def inputs(w: workloads.Workload):
+    key = (w.name, w.index, w.B, w.H, w.D, w.T, w.Y, w.X, w.structure)
+    if key not in _cache:
+        if len(_cache) > 2:
+            _cache.clear()
+        _cache[key] = workloads.make_inputs(w)
+    return _cache[key]
+
+
+def to_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_dev_to_f32(t) -> np.ndarray:
+    return workloads.bf16_to_f32(from_dev(t))
+
+
+def accept_topk_rows(gpu_mask: np.ndarray, oracle_scores: np.ndarray, k: int):
+    """Check every row of a GPU top-k mask against the oracle's scores.
+
+    A row is accepted when its set equals the oracle's set, or when the
+    oracle's boundary gap S_(k) - S_(k+1) is below TIE_BAND, the row keeps k
+    tiles, every extra tile scores above S_(k) - TIE_BAND and every missing
+    tile scores below S_(k+1) + TIE_BAND.  Returns (n_exact, n_band) and
+    raises AssertionError on the first failing row.
+    """
+    om = select.topk_mask(oracle_scores, k)
+    gm = gpu_mask.astype(bool)
+    nt = oracle_scores.shape[-1]
+    s2 = oracle_scores.reshape(-1, nt)
+    om2, gm2 = om.reshape(-1, nt), gm.reshape(-1, nt)
+    diff_rows = np.nonzero(np.any(om2 != gm2, axis=1))[0]
+    if len(diff_rows) == 0:
+        return len(s2), 0
+    up, lo = select.kth_values(s2[diff_rows], k)
+    for n, r in enumerate(diff_rows):
+        g, o, s = gm2[r], om2[r], s2[r]
+        assert g.sum() == k, f"row {r}: {g.sum()} tiles kept, expected {k}"
+        assert up[n] - lo[n] < TIE_BAND, f"row {r}: set differs with gap {up[n] - lo[n]}"
+        extra = np.nonzero(g & ~o)[0]
+        missing = np.nonzero(o & ~g)[0]
+        assert np.all(s[extra] > up[n] - TIE_BAND), f"row {r}: extra tiles {extra}"
+        assert np.all(s[missing] < lo[n] + TIE_BAND), f"row {r}: missing tiles {missing}"
+    return len(s2) - len(diff_rows), len(diff_rows)
+
+
+def compare_outputs(gpu: np.ndarray, ref: np.ndarray, what: str = "output"):
+    """Max-abs and mean-abs bounds between two float arrays of valid rows."""
+    err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    mx, mean = float(err.max()), float(err.mean())
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max-abs {mx:.3g}, mean-abs {mean:.3g}"
+    return mx, mean
+
+
+def sample_rows(B, H, nt, n, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, 0), (B - 1, H - 1, nt - 1)}
+    while len(rows) < min(n, B * H * nt):
+        rows.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(nt))))
+    return sorted(rows)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def scale_of(D):
+    return 1.0 / math.sqrt(D)

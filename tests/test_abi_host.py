@@ -1,0 +1,164 @@
+"""Host-side contract of libbsta.so: exports, geometry, argument checks.
+
+Nothing here launches a kernel: every call either is host-only (geometry,
+capacity, workspace size) or fails its argument checks before any HIP call,
+so the tests run without a GPU.  Pointers passed to failing calls are dummies
+that the library never dereferences.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_sparse_tiled_amd import _lib
+from oracle import geometry
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libbsta.so not built")
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsta.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_[a-z_]+)$", nm, flags=re.M))
+    assert set(declared) <= exported
+
+
+def _g(B=1, H=2, D=64, T=8, Y=8, X=8, tile=(4, 4, 4)):
+    return _lib.Geom(B, H, D, T, Y, X, *tile)
+
+
+@pytest.mark.parametrize("grid", [(8, 8, 8), (21, 30, 52), (20, 48, 80), (5, 6, 7), (1, 1, 1)])
+def test_geometry_matches_oracle(lib, grid):
+    T, Y, X = grid
+    g = _g(T=T, Y=Y, X=X)
+    nt, lpad = ctypes.c_int32(), ctypes.c_int64()
+    assert lib.attn_geometry(ctypes.byref(g), ctypes.byref(nt), ctypes.byref(lpad), None) == 0
+    assert nt.value == geometry.num_tiles(T, Y, X)
+    assert lpad.value == geometry.padded_len(T, Y, X)
+    occ = (ctypes.c_int32 * nt.value)()
+    assert lib.attn_geometry(ctypes.byref(g), None, None, occ) == 0
+    assert np.array_equal(np.array(occ), geometry.occupancy(T, Y, X))
+
+
+def test_capacity_and_workspace(lib):
+    g = _g(B=2, H=3, D=128, T=16, Y=48, X=80)
+    nt = geometry.num_tiles(16, 48, 80)
+    assert lib.attn_select_capacity(ctypes.byref(g), 0, 7, None) == 2 * 3 * nt * 7
+    win = (ctypes.c_int32 * 9)(1, 3, 3, 3, 3, 3, 3, 5, 5)
+    assert lib.attn_select_capacity(ctypes.byref(g), 1, 0, win) == 2 * nt * (9 + 27 + 75)
+    assert lib.attn_workspace_bytes(ctypes.byref(g), 0) == 4 * (2 * 2 * 3 * nt * 128 + 2 * 3 * nt * nt)
+    assert lib.attn_workspace_bytes(ctypes.byref(g), 1) == 0
+
+
+def _err(lib):
+    return lib.attn_last_error().decode()
+
+
+def test_geometry_errors(lib):
+    assert lib.attn_geometry(None, None, None, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_geometry(ctypes.byref(_g(D=96)), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert "D=96" in _err(lib)
+    assert lib.attn_geometry(ctypes.byref(_g(tile=(8, 8, 8))), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert lib.attn_geometry(ctypes.byref(_g(B=0)), None, None, None) == _lib.BSTA_ERR_SHAPE
+    assert lib.attn_geometry(ctypes.byref(_g(T=0)), None, None, None) == _lib.BSTA_ERR_SHAPE
+    assert lib.attn_geometry(ctypes.byref(_g(X=-3)), None, None, None) == _lib.BSTA_ERR_SHAPE
+
+
+def test_tile_errors(lib):
+    assert lib.attn_tile(ctypes.byref(_g()), None, FAKE, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_tile(ctypes.byref(_g()), FAKE, None, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_untile(ctypes.byref(_g()), None, FAKE, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_tile(ctypes.byref(_g(D=32)), FAKE, FAKE, None) == _lib.BSTA_ERR_UNSUPPORTED
+
+
+def _select(lib, g, mode=0, topk=2, win=None, rp=FAKE, ci=FAKE, cap=10 ** 9, ws=FAKE, wsb=10 ** 12,
+            q=FAKE, k=FAKE):
+    return lib.attn_select_blocks(ctypes.byref(g), q, k, mode, topk, win, None, rp, ci, cap, ws,
+                                  wsb, None)
+
+
+def test_select_errors(lib):
+    g = _g()  # 8 tiles
+    assert _select(lib, g, topk=0) == _lib.BSTA_ERR_SHAPE
+    assert _select(lib, g, topk=9) == _lib.BSTA_ERR_SHAPE
+    assert "topk=9" in _err(lib)
+    assert _select(lib, g, mode=5) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _select(lib, g, rp=None) == _lib.BSTA_ERR_NULL
+    assert _select(lib, g, ci=None) == _lib.BSTA_ERR_NULL
+    assert _select(lib, g, q=None) == _lib.BSTA_ERR_NULL
+    assert _select(lib, g, ws=None) == _lib.BSTA_ERR_NULL
+    need = 1 * 2 * 8 * 2
+    assert _select(lib, g, cap=need - 1) == _lib.BSTA_ERR_CAPACITY
+    wsb = lib.attn_workspace_bytes(ctypes.byref(g), 0)
+    assert _select(lib, g, wsb=wsb - 1) == _lib.BSTA_ERR_CAPACITY
+    # window mode
+    assert _select(lib, g, mode=1, win=None) == _lib.BSTA_ERR_NULL
+    bad = (ctypes.c_int32 * 6)(1, 1, 3, 1, 1, 1)   # 3 > 2 tiles along X
+    assert _select(lib, g, mode=1, win=bad) == _lib.BSTA_ERR_SHAPE
+    zero = (ctypes.c_int32 * 6)(1, 0, 1, 1, 1, 1)
+    assert _select(lib, g, mode=1, win=zero) == _lib.BSTA_ERR_SHAPE
+    good = (ctypes.c_int32 * 6)(2, 2, 2, 1, 1, 1)
+    assert _select(lib, g, mode=1, win=good, cap=8 * 9 - 1) == _lib.BSTA_ERR_CAPACITY
+    many = _g(H=_lib.MAX_STA_HEADS + 1)
+    w = (ctypes.c_int32 * (3 * (_lib.MAX_STA_HEADS + 1)))(*([1] * 3 * (_lib.MAX_STA_HEADS + 1)))
+    assert _select(lib, many, mode=1, win=w) == _lib.BSTA_ERR_SHAPE
+
+
+def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16):
+    if scale is None:
+        scale = 1.0 / math.sqrt(g.D)
+    return lib.attn_block_sparse_fwd(ctypes.byref(g), q, FAKE, FAKE, rp, FAKE, col_len, scale,
+                                     causal, o, None, None)
+
+
+def test_fwd_errors(lib):
+    g = _g(D=128)
+    assert _fwd(lib, g, causal=1) == _lib.BSTA_ERR_UNSUPPORTED
+    assert "bidirectional" in _err(lib)
+    assert _fwd(lib, g, scale=0.125) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, scale=1.0) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, scale=float("nan")) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, q=None) == _lib.BSTA_ERR_NULL
+    assert _fwd(lib, g, o=None) == _lib.BSTA_ERR_NULL
+    assert _fwd(lib, g, rp=None) == _lib.BSTA_ERR_NULL
+    assert _fwd(lib, g, col_len=-1) == _lib.BSTA_ERR_SHAPE
+    assert _fwd(lib, _g(D=80)) == _lib.BSTA_ERR_UNSUPPORTED
+
+
+def test_scale_tolerance_rule(lib):
+    """Accept exactly the scales the pages' isclose(rel 1e-4, abs 1e-5) accepts
+    (observed through the col_len error, which comes after the scale check)."""
+    g = _g(D=128)
+    exp = 1.0 / math.sqrt(128)
+    for s, ok in [(exp * (1 + 5e-5), True), (exp * (1 + 3e-4), False), (exp - 9e-6, True),
+                  (exp + 2e-5, False)]:
+        st = _fwd(lib, g, scale=s, col_len=-1)
+        assert st == (_lib.BSTA_ERR_SHAPE if ok else _lib.BSTA_ERR_UNSUPPORTED), s
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(42) == b"unknown status"

@@ -1,0 +1,336 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: tile/untile, window masks and CSR bit-exact; top-k masks and CSR exact
+except rows whose oracle boundary gap is below 1e-4 (which may differ only
+inside that band); pooled vectors within 1e-5*(1+|x|); attention outputs
+within max-abs 2e-2 and mean-abs 2e-3 over valid rows, pad rows exactly 0.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as oatt
+from oracle import geometry, select, tiling
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "c1": workloads.WORKLOADS["c1"],
+    "ragged_d128": workloads.custom("ragged_d128", 2, 3, 128, 5, 6, 7, "topk", 3, seed=11),
+    "ragged_d64": workloads.custom("ragged_d64", 1, 2, 64, 9, 13, 10, "topk", 5, seed=12),
+    "smooth_40": workloads.custom("smooth_40", 1, 4, 128, 8, 16, 20, "topk", 10, "smooth", seed=13),
+    "lowrank_48": workloads.custom("lowrank_48", 1, 3, 128, 12, 16, 16, "topk", 6, "lowrank", seed=14),
+    "one_token": workloads.custom("one_token", 1, 1, 128, 1, 1, 1, "topk", 1, seed=15),
+    "dense_all": workloads.custom("dense_all", 1, 2, 128, 6, 7, 9, "topk", 12, seed=16),
+}
+STA_SMALL = {
+    "sta_small": (workloads.custom("sta_small", 2, 3, 128, 8, 12, 20, "sta", seed=21),
+                  [[1, 3, 3], [2, 3, 5], [2, 1, 4]]),
+    "sta_ragged": (workloads.custom("sta_ragged", 1, 2, 64, 7, 10, 13, "sta", seed=22),
+                   [[2, 3, 4], [1, 1, 1]]),
+    "sta_full": (workloads.custom("sta_full", 1, 2, 128, 8, 8, 12, "sta", seed=23),
+                 [[2, 2, 3], [2, 2, 3]]),
+}
+
+
+@pytest.fixture(scope="module")
+def bsta():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    import block_sparse_tiled_amd as m
+    from block_sparse_tiled_amd import _lib
+    _lib.load()  # fails loudly when libbsta.so is missing
+    return m
+
+
+def _geom(m, w):
+    return m.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X)
+
+
+def _oracle_tiled(w, inp):
+    """Oracle tiling of the bf16 bits, then exact widening to float32."""
+    tb = {n: tiling.tile(inp[n], w.T, w.Y, w.X) for n in ("q", "k", "v")}
+    tf = {n: workloads.bf16_to_f32(tb[n]) for n in tb}
+    return tb, tf
+
+
+def _run_gpu(m, w, inp, windows=None, want_mask=True):
+    import torch
+    g = _geom(m, w)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = m.attn_tile(g, q), m.attn_tile(g, k), m.attn_tile(g, v)
+    mode = m.SELECT_STA if w.mode == "sta" else m.SELECT_TOPK
+    sel = m.attn_select_blocks(g, qt, kt, mode, w.topk, windows, want_mask=want_mask)
+    ot, lse = m.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, want_lse=True)
+    o = m.attn_untile(g, ot)
+    torch.cuda.synchronize()
+    return dict(g=g, qt=qt, kt=kt, vt=vt, sel=sel, ot=ot, lse=lse, o=o)
+
+
+# ---------------------------------------------------------------- tiling
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_tile_untile_bit_exact(bsta, name):
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"tile/untile {name}")
+    g = _geom(bsta, w)
+    for n in ("q", "v"):
+        x = H.to_dev(inp[n])
+        xt = bsta.attn_tile(g, x)
+        assert np.array_equal(H.from_dev(xt), tiling.tile(inp[n], w.T, w.Y, w.X))
+        back = bsta.attn_untile(g, xt)
+        assert np.array_equal(H.from_dev(back), inp[n])
+
+
+def test_tile_overwrites_stale_padding(bsta):
+    """A reused tile buffer full of garbage comes back with zero pad slots."""
+    import torch
+    w = SMALL["ragged_d128"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    out = torch.full((w.B, g.Lpad, w.H, w.D), 7.0, dtype=torch.bfloat16, device="cuda")
+    bsta.attn_tile(g, H.to_dev(inp["k"]), out=out)
+    assert np.array_equal(H.from_dev(out), tiling.tile(inp["k"], w.T, w.Y, w.X))
+
+
+# ---------------------------------------------------------------- pooling + top-k
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_pool_and_topk(bsta, name):
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"pool/top-k {name}")
+    r = _run_gpu(bsta, w, inp)
+    _, tf = _oracle_tiled(w, inp)
+    pq = select.pool(tf["q"], w.T, w.Y, w.X)
+    pk = select.pool(tf["k"], w.T, w.Y, w.X)
+    gpq, gpk = (t.cpu().numpy() for t in r["sel"].pooled(r["g"]))
+    for a, b in ((gpq, pq), (gpk, pk)):
+        assert np.all(np.abs(a - b) <= H.POOL_TOL * (1 + np.abs(b)))
+    s = select.scores(pq, pk)
+    gmask = r["sel"].block_mask.cpu().numpy()
+    exact, band = H.accept_topk_rows(gmask, s, w.topk)
+    H.log(f"  rows exact {exact}, inside tie band {band}")
+    # CSR is exactly the GPU mask's rows in ascending order.
+    rp, ci = select.mask_to_csr(gmask.astype(bool))
+    assert np.array_equal(r["sel"].row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(r["sel"].col_idx.cpu().numpy()[:len(ci)], ci)
+
+
+def test_topk_zero_query_tie_break(bsta):
+    """Q = 0: every score is 0 and ties keep tiles 0..k-1 in every row."""
+    import torch
+    w = SMALL["ragged_d64"]
+    g = _geom(bsta, w)
+    inp = H.inputs(w)
+    q = torch.zeros((w.B, w.L, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    qt, kt = bsta.attn_tile(g, q), bsta.attn_tile(g, H.to_dev(inp["k"]))
+    sel = bsta.attn_select_blocks(g, qt, kt, bsta.SELECT_TOPK, 4)
+    m = sel.block_mask.cpu().numpy()
+    assert np.all(m[..., :4] == 1) and np.all(m[..., 4:] == 0)
+
+
+# ---------------------------------------------------------------- windows
+
+@pytest.mark.parametrize("name", sorted(STA_SMALL))
+def test_sta_bit_exact(bsta, name):
+    w, win = STA_SMALL[name]
+    H.log(f"STA {name}")
+    g = _geom(bsta, w)
+    sel = bsta.attn_select_blocks(g, None, None, bsta.SELECT_STA, 0, win)
+    om = select.sta_mask(w.T, w.Y, w.X, np.array(win), w.B)
+    assert np.array_equal(sel.block_mask.cpu().numpy().astype(bool), om)
+    rp, ci = select.mask_to_csr(om)
+    assert np.array_equal(sel.row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(sel.col_idx.cpu().numpy(), ci)
+
+
+@pytest.mark.parametrize("name", sorted(STA_SMALL))
+def test_sta_end_to_end(bsta, name):
+    w, win = STA_SMALL[name]
+    inp = H.inputs(w)
+    r = _run_gpu(bsta, w, inp, windows=win)
+    _, tf = _oracle_tiled(w, inp)
+    om = select.sta_mask(w.T, w.Y, w.X, np.array(win), w.B)
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], om, w.T, w.Y, w.X)
+    H.compare_outputs(H.bf16_dev_to_f32(r["o"]), tiling.untile(ref, w.T, w.Y, w.X))
+    _check_tiled_output(w, r, ref, rlse)
+
+
+# ---------------------------------------------------------------- attention
+
+def _check_tiled_output(w, r, ref_tiled, ref_lse):
+    valid = np.zeros(ref_tiled.shape[1], dtype=bool)
+    valid[geometry.token_slots(w.T, w.Y, w.X)] = True
+    got = H.bf16_dev_to_f32(r["ot"])
+    H.compare_outputs(got[:, valid], ref_tiled[:, valid], "tiled output")
+    assert np.all(H.from_dev(r["ot"])[:, ~valid] == 0), "pad rows must be +0.0"
+    lse = r["lse"].cpu().numpy()
+    assert np.all(np.isneginf(lse[:, :, ~valid]))
+    err = np.abs(lse[:, :, valid] - ref_lse[:, :, valid])
+    assert err.max() <= H.LSE_TOL, f"lse max err {err.max()}"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_on_oracle_csr(bsta, name):
+    """The attention kernel fed with the oracle's own block selection."""
+    import torch
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"attention on oracle CSR {name}")
+    tb, tf = _oracle_tiled(w, inp)
+    pq = select.pool(tf["q"], w.T, w.Y, w.X)
+    pk = select.pool(tf["k"], w.T, w.Y, w.X)
+    om = select.topk_mask(select.scores(pq, pk), w.topk)
+    rp, ci = select.mask_to_csr(om)
+    g = _geom(bsta, w)
+    qt, kt, vt = (H.to_dev(tb[n]) for n in ("q", "k", "v"))
+    ot, lse = bsta.attn_block_sparse_fwd(g, qt, kt, vt, torch.from_numpy(rp).cuda(),
+                                         torch.from_numpy(ci).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], om, w.T, w.Y, w.X)
+    _check_tiled_output(w, dict(ot=ot, lse=lse), ref, rlse)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_end_to_end(bsta, name):
+    """Whole path; the oracle attends under the GPU's (validated) mask."""
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"end to end {name}")
+    r = _run_gpu(bsta, w, inp)
+    _, tf = _oracle_tiled(w, inp)
+    gmask = r["sel"].block_mask.cpu().numpy().astype(bool)
+    s = select.scores(select.pool(tf["q"], w.T, w.Y, w.X), select.pool(tf["k"], w.T, w.Y, w.X))
+    H.accept_topk_rows(gmask, s, w.topk)
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X)
+    H.compare_outputs(H.bf16_dev_to_f32(r["o"]), tiling.untile(ref, w.T, w.Y, w.X))
+    _check_tiled_output(w, r, ref, rlse)
+
+
+def test_all_tiles_equals_dense_softmax(bsta):
+    """k = Nt: the path equals plain softmax attention (oracle brute force)."""
+    w = SMALL["dense_all"]
+    inp = H.inputs(w)
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    assert w.topk == nt
+    r = _run_gpu(bsta, w, inp)
+    q, k, v = (workloads.bf16_to_f32(inp[n]) for n in ("q", "k", "v"))
+    dense, _ = oatt.dense_masked_attention(q, k, v, np.ones((w.B, w.H, nt, nt), dtype=bool),
+                                           w.T, w.Y, w.X)
+    H.compare_outputs(H.bf16_dev_to_f32(r["o"]), dense)
+
+
+def test_empty_rows_and_out_of_range_indices(bsta):
+    """Empty CSR rows give zeros / -inf; ids outside [0, Nt) are skipped;
+    row ranges past col_len are clamped."""
+    import torch
+    w = SMALL["ragged_d128"]
+    inp = H.inputs(w)
+    tb, tf = _oracle_tiled(w, inp)
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    rows = w.B * w.H * nt
+    rng = np.random.default_rng(0)
+    cols, rp, mask = [], [0], np.zeros((w.B, w.H, nt, nt), dtype=bool)
+    for r in range(rows):
+        b, rem = divmod(r, w.H * nt)
+        h, i = divmod(rem, nt)
+        if r % 5 == 0:
+            sel = []                       # empty row
+        else:
+            sel = sorted(rng.choice(nt, size=int(rng.integers(1, nt + 1)), replace=False).tolist())
+            mask[b, h, i, sel] = True
+            if r % 3 == 0:
+                sel = sel + [nt + 3, -1]   # invalid ids, skipped by the kernel
+        cols += sel
+        rp.append(len(cols))
+    g = _geom(bsta, w)
+    qt, kt, vt = (H.to_dev(tb[n]) for n in ("q", "k", "v"))
+    ot, lse = bsta.attn_block_sparse_fwd(
+        g, qt, kt, vt, torch.tensor(rp, dtype=torch.int32, device="cuda"),
+        torch.tensor(cols, dtype=torch.int32, device="cuda"), want_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], mask, w.T, w.Y, w.X)
+    got = H.bf16_dev_to_f32(ot)
+    assert np.all(np.abs(got - ref) <= H.MAX_ABS)
+    glse = lse.cpu().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(glse), fin)
+    assert np.abs(glse[fin] - rlse[fin]).max() <= H.LSE_TOL
+    # Truncated col_len: rows past it see fewer tiles, never out-of-bounds reads.
+    short = len(cols) // 2
+    ot2 = bsta.attn_block_sparse_fwd(
+        g, qt, kt, vt, torch.tensor(rp, dtype=torch.int32, device="cuda"),
+        torch.tensor(cols[:short], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(H.bf16_dev_to_f32(ot2)))
+
+
+def test_deterministic(bsta):
+    w = SMALL["smooth_40"]
+    inp = H.inputs(w)
+    a = _run_gpu(bsta, w, inp)
+    b = _run_gpu(bsta, w, inp)
+    assert np.array_equal(H.from_dev(a["o"]), H.from_dev(b["o"]))
+    assert np.array_equal(a["sel"].col_idx.cpu().numpy(), b["sel"].col_idx.cpu().numpy())
+
+
+# ---------------------------------------------------------------- full sizes
+
+def _full_size_check(bsta, w, n_rows):
+    """Full workload in the benchmark's launch configuration; selection checked
+    for every row, attention on sampled query tiles."""
+    H.log(f"full size {w.name}: generating inputs")
+    inp = H.inputs(w)
+    win = inp.get("windows")
+    H.log(f"full size {w.name}: GPU path")
+    r = _run_gpu(bsta, w, inp, windows=None if win is None else win.tolist())
+    g = r["g"]
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    # tile permutation: bit-exact on Q
+    assert np.array_equal(H.from_dev(r["qt"]), tiling.tile(inp["q"], w.T, w.Y, w.X))
+    H.log(f"full size {w.name}: oracle selection")
+    gmask = r["sel"].block_mask.cpu().numpy().astype(bool)
+    tb, tf = _oracle_tiled(w, inp)
+    if w.mode == "sta":
+        om = select.sta_mask(w.T, w.Y, w.X, win, w.B)
+        assert np.array_equal(gmask, om)
+    else:
+        pq = select.pool(tf["q"], w.T, w.Y, w.X)
+        pk = select.pool(tf["k"], w.T, w.Y, w.X)
+        gpq, gpk = (t.cpu().numpy() for t in r["sel"].pooled(g))
+        assert np.all(np.abs(gpq - pq) <= H.POOL_TOL * (1 + np.abs(pq)))
+        assert np.all(np.abs(gpk - pk) <= H.POOL_TOL * (1 + np.abs(pk)))
+        exact, band = H.accept_topk_rows(gmask, select.scores(pq, pk), w.topk)
+        H.log(f"  rows exact {exact}, inside tie band {band}")
+    rp, ci = select.mask_to_csr(gmask)
+    assert np.array_equal(r["sel"].row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(r["sel"].col_idx.cpu().numpy()[:len(ci)], ci)
+    H.log(f"full size {w.name}: oracle attention on {n_rows} sampled query tiles")
+    rows = H.sample_rows(w.B, w.H, nt, n_rows, seed=w.index)
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X,
+                                            rows=rows)
+    got = H.bf16_dev_to_f32(r["ot"])
+    occ = geometry.occupancy(w.T, w.Y, w.X)
+    glse = r["lse"].cpu().numpy()
+    gs, rs = [], []
+    for b, h, i in rows:
+        sl = slice(i * 64, i * 64 + occ[i])
+        gs.append(got[b, sl, h])
+        rs.append(ref[b, sl, h])
+        assert np.all(H.from_dev(r["ot"][b, i * 64 + occ[i]:(i + 1) * 64, h]) == 0)
+        assert np.abs(glse[b, h, sl] - rlse[b, h, sl]).max() <= H.LSE_TOL
+    H.compare_outputs(np.concatenate(gs), np.concatenate(rs))
+    # untile of the output is the oracle untile of the GPU's tiled output
+    assert np.array_equal(H.from_dev(r["o"]), tiling.untile(H.from_dev(r["ot"]), w.T, w.Y, w.X))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size(bsta, name):
+    _full_size_check(bsta, workloads.WORKLOADS[name], 24)
