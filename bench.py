@@ -1,0 +1,210 @@
+"""Benchmark of the block-sparse tiled attention path on one MI355X.
+
+One step = the whole path on one batch already resident in HBM:
+tile Q, K, V -> select blocks (pool, score, top-k -> CSR) -> block-sparse
+attention forward -> untile O.  Prints one JSON line.
+
+Default workload: B=1, H=40, D=128, latent 20x48x80 (L=76,800, 1200 tiles of
+4x4x4), top-k 120 key tiles per query tile, Q/K/V ~ N(0,1) plus a shared
+Gaussian-blurred (sigma 2 tokens) component at 0.5 amplitude.
+
+value = selected-tile attention FLOP per step / step time (whole path),
+in TFLOP/s.  The attention kernel's own rate is in "roofline" and
+"kernels.attn_fwd".  Kernel times come from HIP events recorded on the
+stream every call is enqueued on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI355X"
+
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# on the default workload (KiB per dispatch, scaled by the copy-kernel factor),
+# keyed by kernel; None until measured for the current kernel version.
+MEASURED_TRAFFIC = {"attn_fwd": None}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def attention_flop(w, mask_rows_nnz, occupancy=None):
+    """4*D*64*64 per selected (query tile, key tile) pair (tile level)."""
+    return 4.0 * w.D * 64 * 64 * mask_rows_nnz
+
+
+def cpu_baseline(w):
+    """The oracle, as it stands, on one head of the workload (all its query tiles)."""
+    import numpy as np
+    import workloads
+    from oracle import geometry, pipeline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    w1 = workloads.custom(w.name + "_1head", w.B, 1, w.D, w.T, w.Y, w.X, w.mode, w.topk,
+                          w.structure, seed=w.seed)
+    inp = workloads.make_inputs(w1)
+    win = None
+    if w.mode == "sta":
+        win = workloads.sta_windows(w)[:1]
+    t0 = time.perf_counter()
+    res = pipeline.run(inp["q"], inp["k"], inp["v"], w.T, w.Y, w.X, w.mode, w.topk, win)
+    dt = time.perf_counter() - t0
+    flop = attention_flop(w, int(res["mask"].sum()))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {w.H} heads, all {geometry.num_tiles(w.T, w.Y, w.X)} query tiles, "
+                      f"whole oracle path (tile, pool, score, select, attend, untile), float64 numpy",
+            "seconds": dt, "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_tiled_amd as bsta
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(w)
+    g = bsta.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    nt, lpad = bsta.attn_geometry(g)
+    mode = bsta.SELECT_STA if w.mode == "sta" else bsta.SELECT_TOPK
+    win = inp["windows"].tolist() if w.mode == "sta" else None
+    # Preallocated outputs: the timed region allocates nothing.
+    qt, kt, vt, ot = (torch.empty((w.B, lpad, w.H, w.D), dtype=torch.bfloat16, device=dev)
+                      for _ in range(4))
+    o = torch.empty_like(q)
+    sel = bsta.attn_select_blocks(g, None if mode == bsta.SELECT_STA else qt,
+                                  None if mode == bsta.SELECT_STA else kt, mode, w.topk, win,
+                                  want_mask=False)
+    names = ["tile_qkv", "select", "attn_fwd", "untile"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        bsta.attn_tile(g, q, out=qt)
+        bsta.attn_tile(g, k, out=kt)
+        bsta.attn_tile(g, v, out=vt)
+        if ev:
+            ev[1].record()
+        bsta.attn_select_blocks(g, qt, kt, mode, w.topk, win, out=sel)
+        if ev:
+            ev[2].record()
+        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
+        if ev:
+            ev[3].record()
+        bsta.attn_untile(g, ot, out=o)
+        if ev:
+            ev[4].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nnz = int(sel.row_ptr[-1].item())
+
+    # Whole-step timing (no per-kernel events inside).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Per-call timing with HIP events on the launch stream.
+    per = {n: [] for n in names}
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(ev)
+        torch.cuda.synchronize()
+        for idx, n in enumerate(names):
+            per[n].append(ev[idx].elapsed_time(ev[idx + 1]))
+    ms = {n: float(np.mean(per[n])) for n in names}
+    print(f"[bench] per-call ms {ms}", file=sys.stderr, flush=True)
+
+    flop = attention_flop(w, nnz)
+    dense_flop = 4.0 * w.D * w.B * w.H * float(w.L) ** 2
+    attn_tflops = flop / (ms["attn_fwd"] * 1e-3) / 1e12
+    elem = w.B * w.H * w.D * 2
+    tile_bytes = 3 * elem * (w.L + lpad)
+    untile_bytes = elem * (w.L + lpad)
+    pool_bytes = 2 * elem * w.L + 2 * w.B * w.H * nt * w.D * 4
+    out = {
+        "metric": METRIC,
+        "value": flop / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} D={w.D} grid {w.T}x{w.Y}x{w.X} "
+                        f"(L={w.L}, {nt} tiles of 4x4x4), "
+                        + (f"top-k {w.topk}" if w.mode == "topk" else "STA windows"),
+            "selected_tile_pairs": nnz,
+            "value_basis": "selected-tile attention FLOP (4*D*64*64 per pair) per whole-path step",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel<128>",
+            "achieved": attn_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / PEAK_BF16_TFLOPS,
+            "traffic": MEASURED_TRAFFIC["attn_fwd"],
+        },
+        "kernels": {
+            "attn_fwd": {"ms": ms["attn_fwd"], "tflops": attn_tflops,
+                         "dense_equiv_tflops": dense_flop / (ms["attn_fwd"] * 1e-3) / 1e12,
+                         "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS},
+            "tile_qkv": {"ms": ms["tile_qkv"], "gbps": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9,
+                         "frac_hbm_peak": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+            "select": {"ms": ms["select"], "pool_bytes": pool_bytes},
+            "untile": {"ms": ms["untile"], "gbps": untile_bytes / (ms["untile"] * 1e-3) / 1e9},
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
