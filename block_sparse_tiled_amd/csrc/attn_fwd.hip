@@ -8,30 +8,39 @@
 // Work decomposition: one workgroup of two wave64s per query tile (64
 // rows); wave w owns query rows 32w..32w+31 for the whole key list.  For each
 // selected key tile:
-//   1. K (64 x D) is staged to LDS row-major with an XOR swizzle of 16-byte
-//      chunks; V is staged transposed (D x 64) with its keys permuted inside
-//      every 16-key group so that one 16-byte LDS read feeds one MFMA operand.
-//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N), so
-//      each lane ends up holding scores of a single query.
+//   1. K and V (64 x D each) arrive in LDS by direct global->LDS DMA
+//      (global_load_lds_dwordx4): no register staging.  Both are row-major
+//      with an XOR swizzle of 16-byte chunks, chosen so that the reads below
+//      are free of bank conflicts.  The next tile's K is fetched while this
+//      tile's softmax and P.V run; the next tile's V while the next S runs.
+//   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N): each
+//      lane ends up holding scores of a single query.
 //   3. Online softmax in the exp2 domain (log2(e)/sqrt(D) folded into the
 //      scale); the row max needs one cross-lane exchange (lane ^ 32), the row
 //      sum stays per lane until the end.
-//   4. O^T += V^T P^T on the same MFMA, P converted to bf16 in registers:
-//      the accumulator layout of step 2 is exactly the B-operand layout this
-//      product needs, up to a fixed permutation of the 16 keys of each
-//      k-step, which the transposed V layout in LDS absorbs.
+//   4. O^T += V^T P^T on the same MFMA.  The accumulator layout of step 2 is
+//      the B-operand layout this product needs, up to a fixed permutation of
+//      the 16 keys of each k-step; the A operand (V^T) comes from row-major V
+//      through the LDS transpose read ds_read_b64_tr_b16, four keys at a time
+//      in exactly that permuted order.
 // Partial key tiles (n_j < 64) mask keys r >= n_j to -inf; padded query rows
-// are written as zero.
+// are written as +0.0.  Out-of-range tile ids contribute nothing.
 //
-// MFMA 32x32x16 bf16 lane layout (gfx950): A[m][k] in lane m + 32*(k/8),
-// element k%8; B[k][n] in lane n + 32*(k/8), element k%8; D[m][n] in lane
-// n, register 8*(m/8)... precisely reg r of lane l holds
-// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// Lane layouts used (gfx950, checked on hardware):
+//   v_mfma_f32_32x32x16_bf16: A[m][k] in lane m + 32*(k/8), element k%8;
+//     B[k][n] in lane n + 32*(k/8), element k%8; register r of lane l holds
+//     D[8*(r/4) + 4*(l/32) + r%4][l%32].
+//   ds_read_b64_tr_b16, per 16-lane group: if lane s addresses 4 elements
+//     C_s, lane d receives C_{d/4 + 4m}[d%4] for m = 0..3.
+//   global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
 #include "bsta_common.hpp"
 
 namespace bsta {
 
 namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -39,26 +48,106 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-// Physical 16-byte chunk of K row `row` (D/8 chunks per row).
+// Physical 16-byte chunk of logical chunk c in K row r (D/8 chunks per row).
 template <int D>
-__device__ inline int k_chunk(int row, int c) { return c ^ (row & (D / 8 - 1)); }
+__device__ inline int k_phys(int r, int c) { return c ^ (r & (D / 8 - 1)); }
 
-// Physical 16-byte chunk of V^T row `d` (8 chunks of 8 keys per row).
-__device__ inline int vt_chunk(int d, int c) { return c ^ (d & 7); }
+// Physical 16-byte chunk of logical chunk c in V row r.
+__device__ inline int v_phys(int r, int c) { return c ^ ((r & 3) << 1); }
+
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Issue this wave's share of one 64 x D tile as 1 KB direct-to-LDS blocks:
+// block u of the wave lands at LDS byte lds0 + 2048*u (the two waves
+// interleave).  `voff` holds the per-lane source byte offsets from `base`.
+// Written as inline asm so that the compiler does not guard every later LDS
+// read with a wait for all outstanding DMA; the kernel waits on vmcnt
+// itself.  M0 (the DMA's LDS base) is saved and restored around the block.
+template <int NB>
+__device__ inline void dma_tile(const __bf16* base_any, const int32_t* voff, uint32_t lds_any) {
+    // Both the LDS base and the global base are wave-uniform; make them SGPRs.
+    // (readfirstlane returns int: go through uint32_t so that the low half is
+    // zero-extended, never sign-extended into the high half.)
+    const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_any);
+    const uint64_t b64 = (uint64_t)(uintptr_t)base_any;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    uint32_t saved;
+    if constexpr (NB == 8) {
+        asm volatile(
+            "s_mov_b32 %[t], m0\n\t"
+            "s_mov_b32 m0, %[l]\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v2], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v3], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v4], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v5], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v6], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v7], %[b]\n\t"
+            "s_mov_b32 m0, %[t]"
+            : [t] "=&s"(saved)
+            : [l] "s"(lds0), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]),
+              [v2] "v"(voff[2]), [v3] "v"(voff[3]), [v4] "v"(voff[4]), [v5] "v"(voff[5]),
+              [v6] "v"(voff[6]), [v7] "v"(voff[7])
+            : "memory", "scc");
+    } else {
+        static_assert(NB == 4, "tile of 64 x 64 or 64 x 128 bf16");
+        asm volatile(
+            "s_mov_b32 %[t], m0\n\t"
+            "s_mov_b32 m0, %[l]\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v2], %[b]\n\t"
+            "s_add_u32 m0, m0, 2048\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[v3], %[b]\n\t"
+            "s_mov_b32 m0, %[t]"
+            : [t] "=&s"(saved)
+            : [l] "s"(lds0), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]),
+              [v2] "v"(voff[2]), [v3] "v"(voff[3])
+            : "memory", "scc");
+    }
+}
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_kernel(
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
         const int32_t* __restrict__ col_idx, int64_t col_len, float scale_log2,
         __bf16* __restrict__ o, float* __restrict__ lse, int per_xcd) {
     constexpr int NDC = D / 16;   // MFMA k-steps for S (16 d each)
     constexpr int NDB = D / 32;   // 32-row d blocks of O^T
-    constexpr int CPR = D / 8;    // 16-byte chunks per K row
-    __shared__ __attribute__((aligned(16))) __bf16 ks[64 * D];
-    __shared__ __attribute__((aligned(16))) __bf16 vts[D * 64];
+    constexpr int CPR = D / 8;    // 16-byte chunks per row
+    constexpr int NBLK = 64 * D * 2 / 1024 / 2;  // DMA blocks per wave per tensor
+    __shared__ __attribute__((aligned(1024))) __bf16 ks[64 * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 vs[64 * D];
 
     // XCD-aware placement: workgroups are dealt round-robin over the 8 XCDs;
     // give each XCD a contiguous run of query tiles of one head at a time so
@@ -77,12 +166,56 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
     const int64_t head_off = (int64_t)h * D;
     const int64_t batch_row0 = (int64_t)b * g.Lpad;
 
+    // Per-lane source offsets (bytes, relative to the tile's first row) of
+    // this wave's DMA blocks: block t covers LDS bytes [1024t, 1024t+1024),
+    // i.e. row r = (1024t + 16*lane) / (2D), physical chunk p; the lane
+    // fetches the logical chunk that the swizzle stores at p.
+    int32_t koff[NBLK], voff[NBLK];
+#pragma unroll
+    for (int u = 0; u < NBLK; ++u) {
+        const int t = wave + 2 * u;
+        const int byte = t * 1024 + lane * 16;
+        const int r = byte / (2 * D);
+        const int p = (byte % (2 * D)) / 16;
+        koff[u] = 2 * ((int32_t)(r * rs) + k_phys<D>(r, p) * 8);
+        voff[u] = 2 * ((int32_t)(r * rs) + v_phys(r, p) * 8);
+    }
+
+    const int64_t row = (int64_t)bh * g.Nt + i;
+    int64_t p0 = row_ptr[row], p1 = row_ptr[row + 1];
+    p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
+    p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
+
+    // Tile id at CSR position p, or -1 when out of range (then tile 0 is
+    // fetched and fully masked, keeping the pipeline uniform).
+    auto tile_at = [&](int64_t p) -> int {
+        const int j = col_idx[p];
+        return (unsigned)j < (unsigned)g.Nt ? j : -1;
+    };
+    auto tile_base = [&](const __bf16* t, int j) {
+        return t + (batch_row0 + (int64_t)(j < 0 ? 0 : j) * 64) * rs + head_off;
+    };
+
     // Query fragment (B operand of S^T = K Q^T): query row qi, d = 16*dc + 8*half.
     const int qi = wave * 32 + l32;
     const __bf16* qrow = q + (batch_row0 + (int64_t)i * 64 + qi) * rs + head_off;
     bf16x8 qf[NDC];
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) qf[dc] = *(const bf16x8*)(qrow + dc * 16 + half * 8);
+    // Make the compiler wait for the query loads here, before the loop: it
+    // cannot see the DMA issued by inline asm, and a wait for these loads
+    // placed inside the loop would also drain the in-flight DMA.
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) asm volatile("" ::"v"(qf[dc]));
+
+    const uint32_t ks_lds = lds_addr(ks) + wave * 1024;
+    const uint32_t vs_lds = lds_addr(vs) + wave * 1024;
+    int j = p0 < p1 ? tile_at(p0) : -1;
+    if (p0 < p1) {
+        dma_tile<NBLK>(tile_base(k, j), koff, ks_lds);
+        dma_tile<NBLK>(tile_base(v, j), voff, vs_lds);
+    }
+
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -91,54 +224,23 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int64_t row = (int64_t)bh * g.Nt + i;
-    int64_t p0 = row_ptr[row], p1 = row_ptr[row + 1];
-    p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
-    p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
+    // LDS transpose-read addresses (elements) for the V^T operand: lane group
+    // G = lane/16 covers d = db*32 + 16*(G%2) + [0,16) and keys
+    // kc*16 + 4*half + [0,4) (+8 for the second read); source lane s = lane%16
+    // points at key row kbase + s/4, d offset 4*(s%4).
+    const int s16 = lane & 15, dsub = (lane >> 4) & 1;
+    const int vrow0 = 4 * half + (s16 >> 2);                  // + kc*16 (+8)
+    const int vcol = 16 * dsub + 4 * (s16 & 3);               // + db*32
+    // K operand rows: key kb*32 + l32, logical chunk dc*2 + half.
 
     for (int64_t p = p0; p < p1; ++p) {
-        const int j = col_idx[p];
-        if ((unsigned)j >= (unsigned)g.Nt) continue;  // uniform over the workgroup
-        const int nj = tile_occupancy(g, j);
-        const int64_t tile_row0 = batch_row0 + (int64_t)j * 64;
-        const __bf16* kt = k + tile_row0 * rs + head_off;
-        const __bf16* vt = v + tile_row0 * rs + head_off;
+        const int jn = p + 1 < p1 ? tile_at(p + 1) : -2;  // -2: no next tile
+        const int nj = j < 0 ? 0 : tile_occupancy(g, j);
 
-        __syncthreads();  // previous tile's LDS reads are done
-        // Stage K: 64 rows x CPR chunks.
-#pragma unroll
-        for (int e = tid; e < 64 * CPR; e += 128) {
-            const int r = e / CPR, c = e - r * CPR;
-            u32x4 val = *(const u32x4*)(kt + r * rs + c * 8);
-            *(u32x4*)(ks + r * D + k_chunk<D>(r, c) * 8) = val;
-        }
-        // Stage V^T: an 8-key x 8-d block per thread, transposed in registers.
-        // Key group kg (0..7) = 16-key chunk kc = kg/2, half hh = kg%2, holding
-        // keys 16kc + 4hh + {0..3} and 16kc + 8 + 4hh + {0..3}.
-#pragma unroll
-        for (int e = tid; e < 8 * CPR; e += 128) {
-            const int dg = e % CPR, kg = e / CPR;
-            const int kbase = (kg >> 1) * 16 + (kg & 1) * 4;
-            u32x4 in[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int key = kbase + (u & 3) + (u >> 2) * 8;
-                in[u] = *(const u32x4*)(vt + key * rs + dg * 8);
-            }
-#pragma unroll
-            for (int dv = 0; dv < 8; ++dv) {
-                u32x4 out;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t x0 = in[2 * w][dv >> 1], x1 = in[2 * w + 1][dv >> 1];
-                    out[w] = (dv & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
-                                      : ((x0 & 0xffffu) | (x1 << 16));
-                }
-                const int d = dg * 8 + dv;
-                *(u32x4*)(vts + d * 64 + vt_chunk(d, kg) * 8) = out;
-            }
-        }
-        __syncthreads();
+        // K_j landed (V_j may still be in flight).
+        if constexpr (NBLK == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
 
         // S^T = K Q^T: two 32-key blocks.
         f32x16 sacc[2];
@@ -149,10 +251,13 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
             const int krow = kb * 32 + l32;
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
-                bf16x8 a = *(const bf16x8*)(ks + krow * D + k_chunk<D>(krow, dc * 2 + half) * 8);
+                bf16x8 a = *(const bf16x8*)(ks + krow * D + k_phys<D>(krow, dc * 2 + half) * 8);
                 sacc[kb] = mfma32(a, qf[dc], sacc[kb]);
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // every wave is done reading K_j
+        if (jn != -2) dma_tile<NBLK>(tile_base(k, jn), koff, ks_lds);
 
         // Online softmax for query qi.  Key of (kb, r): 32kb + 8(r/4) + 4half + r%4.
         float mx = -INFINITY;
@@ -170,7 +275,8 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
             }
         mx = fmaxf(mx, wave_xor32(mx));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // fully masked so far
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         m_run = m_new;
         float psum = 0.f;
         bf16x8 pf[4];
@@ -178,7 +284,7 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+                const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
                 psum += pv;
                 pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
             }
@@ -188,16 +294,35 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 
+        // V_j landed (K_{j+1} may still be in flight).
+        if (jn != -2) {
+            if constexpr (NBLK == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+
         // O^T += V^T P^T: four 16-key steps per 32-row d block.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int drow = db * 32 + l32;
+        for (int kc = 0; kc < 4; ++kc) {
+            const int r0 = kc * 16 + vrow0, r1 = r0 + 8;
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                bf16x8 a = *(const bf16x8*)(vts + drow * 64 + vt_chunk(drow, kc * 2 + half) * 8);
-                oacc[db] = mfma32(a, pf[kc], oacc[db]);
+            for (int db = 0; db < NDB; ++db) {
+                const int c = db * 32 + vcol;  // d of this lane's 4-element source
+                const __bf16* a0 = vs + r0 * D + v_phys(r0, c >> 3) * 8 + (c & 7);
+                const __bf16* a1 = vs + r1 * D + v_phys(r1, c >> 3) * 8 + (c & 7);
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                i16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[db] = mfma32(__builtin_bit_cast(bf16x8, av), pf[kc], oacc[db]);
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // every wave is done reading V_j
+        if (jn != -2) dma_tile<NBLK>(tile_base(v, jn), voff, vs_lds);
+        j = jn;
     }
 
     // Finalise: l is split over lanes l and l^32.
