@@ -43,7 +43,28 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mode", default="path", choices=["path", "copy"],
+                   help="copy: time a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
+
+
+def copy_calibration(steps: int):
+    """A plain device-to-device copy of a known size: the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters of the path's kernels."""
+    import torch
+    n = 1 << 29  # bf16 elements = 1 GiB
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"mode": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                      "ms": dt * 1e3, "gbps": 4 * n / dt / 1e9}), flush=True)
 
 
 def attention_flop(w, mask_rows_nnz, occupancy=None):
@@ -83,6 +104,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.mode == "copy":
+        copy_calibration(args.steps)
+        return
     import numpy as np
     import torch
 
