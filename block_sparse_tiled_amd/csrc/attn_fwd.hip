@@ -48,6 +48,9 @@ namespace {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kRing = 5;  // half-tile slots per wave
 
@@ -86,13 +89,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // kernel waits on vmcnt itself.  M0 (the DMA's LDS base) is saved and
 // restored around the block.
 template <int NI>
-__device__ inline void dma_half(const __bf16* base_any, const int32_t* voff, uint32_t lds_any) {
+__device__ inline void dma_half(uint64_t base_any, const int32_t* voff, uint32_t lds_any) {
     // Both bases are wave-uniform; make them SGPRs.  (readfirstlane returns
     // int: go through uint32_t so the low half is never sign-extended.)
     const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_any);
-    const uint64_t b64 = (uint64_t)(uintptr_t)base_any;
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base_any >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base_any);
     const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
     uint32_t saved;
     if constexpr (NI == 4) {
@@ -165,12 +167,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NDB = D / 32;                    // 32-row d blocks of O^T
     constexpr int HALF_ELEMS = 32 * D;             // one half-tile slot
     constexpr int NI = HALF_ELEMS * 2 / 1024 / 2;  // DMA instructions per wave per half-tile
+    constexpr int SLOT_BYTES = HALF_ELEMS * 2;
     __shared__ __attribute__((aligned(1024))) __bf16 ring[kRing * HALF_ELEMS];
+
+    // CSR reads are wave-uniform: read them through the scalar cache.
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const cptr rp_s = (cptr)row_ptr;
+    const cptr ci_s = (cptr)col_idx;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t rs = (int64_t)g.H * D;  // elements between consecutive tokens
+    const int64_t rs2 = rs * 2;           // bytes
+    const bool all_full = (g.T & 3) == 0 && (g.Y & 3) == 0 && (g.X & 3) == 0;
 
     // Per-lane DMA source offsets (bytes, relative to the half-tile's first
     // row) of this wave's blocks: block t = wave + 2u covers slot bytes
@@ -185,23 +195,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         koff[u] = 2 * ((int32_t)(r * rs) + k_phys<D>(r, p) * 8);
         voff[u] = 2 * ((int32_t)(r * rs) + v_phys<D>(r, p) * 8);
     }
-    const uint32_t ring_lds = lds_addr(ring) + wave * 1024;
+    // This wave's DMA destination inside slot 0 (uniform: keep it scalar).
+    const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(ring) + wave * 1024);
 
-    // V^T transpose-read addresses inside a half-tile slot: lane group
-    // G = lane/16 covers d = db*32 + 16*(G%2) + [0,16) and keys
-    // 16*(kc%2) + 4*half + [0,4) (+8 for the second read); source lane
-    // s = lane%16 points at key row kbase + s/4, d offset 4*(s%4).  The
-    // swizzle depends on the row only through r%4, equal for all of them.
+    // LDS read addresses (bytes) inside slot 0; a slot adds a constant.
+    // K operand for k-step dc: row l32, logical chunk 2*dc + half.
+    // V^T transpose reads: lane group G = lane/16 covers d = db*32 +
+    // 16*(G%2) + [0,16) and keys 16*kk + 4*half + [0,4) (+8 for the second
+    // read); source lane s = lane%16 points at key row 16*kk + 4*half + s/4,
+    // d offset 4*(s%4).  The V swizzle depends on the row only through r%4,
+    // equal for all of them.
+    const uint32_t ring0 = lds_addr(ring);
+    uint32_t kaddr[NDC];
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) kaddr[dc] = ring0 + 2 * (l32 * D + k_phys<D>(l32, 2 * dc + half) * 8);
     const int s16 = lane & 15, dsub = (lane >> 4) & 1;
-    const int vrow0 = 4 * half + (s16 >> 2);     // + 16*(kc%2) (+8)
-    const int vcol = 16 * dsub + 4 * (s16 & 3);  // + db*32
-    int vaddr[NDB];                              // element offsets for kc%2 = 0, first read
+    const int vrow0 = 4 * half + (s16 >> 2);
+    const int vcol = 16 * dsub + 4 * (s16 & 3);
+    uint32_t vaddr[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const int c = db * 32 + vcol;
-        vaddr[db] = vrow0 * D + v_phys<D>(vrow0, c >> 3) * 8 + (c & 7);
+        vaddr[db] = ring0 + 2 * (vrow0 * D + v_phys<D>(vrow0, c >> 3) * 8 + (c & 7));
     }
     const int qi = wave * 32 + l32;  // this lane's query row in the tile
+    const int half4 = 4 * half;
 
     // Persistent, XCD-aware schedule.  Workgroups are dealt round-robin over
     // the 8 XCDs, so workgroup w runs on XCD w%8.  XCD e owns the contiguous
@@ -220,37 +238,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int b = bh / g.H, h = bh - b * g.H;
         const int64_t head_off = (int64_t)h * D;
         const int64_t batch_row0 = (int64_t)b * g.Lpad;
+        const uint64_t kbase = (uint64_t)(uintptr_t)(k + batch_row0 * rs + head_off);
+        const uint64_t vbase = (uint64_t)(uintptr_t)(v + batch_row0 * rs + head_off);
 
-        int64_t p0 = row_ptr[item], p1 = row_ptr[item + 1];
+        int64_t p0 = rp_s[item], p1 = rp_s[item + 1];
         p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
         p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
         const int n = (int)(p1 - p0);
-        const int nseq = 4 * n;  // half-tiles in consumption order
 
-        // Tile id at CSR position p, or -1 when out of range (then tile 0 is
-        // fetched and fully masked, keeping the pipeline uniform).
-        auto tile_at = [&](int64_t p) -> int {
-            const int j = col_idx[p];
+        // Tile id at CSR position p0 + t, or -1 when t is past the row or the
+        // id is out of range (then tile 0 is fetched and fully masked).
+        auto tile_id = [&](int t) -> int {
+            if (t >= n) return -1;
+            const int j = ci_s[p0 + t];
             return (unsigned)j < (unsigned)g.Nt ? j : -1;
         };
-        auto tile_rows = [&](int j) -> const int64_t {
-            return (batch_row0 + (int64_t)(j < 0 ? 0 : j) * 64) * rs + head_off;
-        };
-        // Half-tiles are consumed in the order K0lo K0hi V0lo V0hi K1lo ...;
-        // half-tile s lives in ring slot s % kRing.
-        const uint32_t slot_bytes = HALF_ELEMS * 2;
-        auto dma = [&](const __bf16* src, const int32_t* off, int slot_idx) {
-            dma_half<NI>(src, off, ring_lds + (uint32_t)slot_idx * slot_bytes);
-        };
-        // Wait for this wave's DMA of the half-tile about to be read (with
-        // `newer` later half-tiles allowed in flight) and for its own reads of
-        // the previous slot, then barrier: the half-tile is visible to both
-        // waves and the previous slot is retired.
-        auto acquire = [&](int newer) {
-            wait_dma<NI>(newer);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-        };
+        // Byte offset of a tile's first row from the head's base.
+        auto tile_bytes = [&](int j) -> uint64_t { return (uint64_t)((int64_t)(j < 0 ? 0 : j) * 64 * rs2); };
 
         // Query fragment (B operand of S^T = K Q^T): query row qi,
         // d = 16*dc + 8*half.
@@ -258,141 +262,217 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const __bf16* qrow = q + (batch_row0 + (int64_t)i * 64 + qi) * rs + head_off;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) qf[dc] = *(const bf16x8*)(qrow + dc * 16 + half * 8);
-        // Make the compiler wait for the query loads here, before the DMA: it
-        // cannot see the DMA issued by inline asm, and a wait for these loads
-        // placed inside the key loop would also drain the in-flight DMA.
+        // The compiler cannot see the DMA issued below: make it finish the
+        // query loads first, so that no wait inside the key loop drains the
+        // DMA queue on their account.
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) asm volatile("" ::"v"(qf[dc]));
 
-        // Prologue: half-tiles 0..3 (all of tile 0) into slots 0..3.  Every
-        // slot of the previous item was retired behind a barrier.
-        int slot0 = 0;  // ring slot of half-tile 4t
-        if (n > 0) {
-            const int64_t r0 = tile_rows(tile_at(p0));
-            dma(k + r0, koff, 0);
-            dma(k + r0 + 32 * rs, koff, 1);
-            dma(v + r0, voff, 2);
-            dma(v + r0 + 32 * rs, voff, 3);
-        }
+        // Half-tiles are consumed in the order K0lo K0hi, then per key tile
+        // t: K(t+1)lo K(t+1)hi V(t)lo V(t)hi (no K after the last tile);
+        // sequence position s sits in ring slot s % kRing.
+        const int NSEQ = 4 * n;
+        int next_pos = 0, next_slot = 0;  // DMA producer
+        auto issue_next = [&]() {
+            const int s = next_pos;
+            bool is_k;
+            int t, hi;
+            if (s < 2) {
+                is_k = true, t = 0, hi = s;
+            } else if (s >= NSEQ - 2) {
+                is_k = false, t = n - 1, hi = s - (NSEQ - 2);
+            } else {
+                const int q4 = (s - 2) >> 2, w = (s - 2) & 3;
+                is_k = w < 2, t = is_k ? q4 + 1 : q4, hi = w & 1;
+            }
+            const uint64_t src = (is_k ? kbase : vbase) + tile_bytes(tile_id(t)) + (hi ? 32 * rs2 : 0);
+            dma_half<NI>(src, is_k ? koff : voff, dma_lds + next_slot * SLOT_BYTES);
+            ++next_pos;
+            next_slot = next_slot == kRing - 1 ? 0 : next_slot + 1;
+        };
+        // Consumer: pairs of positions.  acquire() waits for this wave's DMA
+        // of the pair (the next position may stay in flight), then a barrier
+        // makes the pair visible to both waves and retires the previous
+        // pair, whose slots are refilled right away.  Returns the pair's
+        // first slot (the second is the next one, cyclically).
+        int read_pos = 0, read_slot = 0;
+        auto acquire = [&]() -> int {
+            if (next_pos > read_pos + 2) wait_dma<NI>(1);
+            else wait_dma<NI>(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            const int lim = read_pos + kRing < NSEQ ? read_pos + kRing : NSEQ;
+            while (next_pos < lim) issue_next();
+            const int sl = read_slot;
+            read_pos += 2;
+            read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;
+            return sl;
+        };
+        auto next_slot_of = [](int sl) { return sl == kRing - 1 ? 0 : sl + 1; };
+        // Prologue: positions 0..2.  Every slot of the previous item was
+        // retired behind a barrier.
+        while (next_pos < 3 && next_pos < NSEQ) issue_next();
 
         f32x16 oacc[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-        float m_run = -INFINITY, l_run = 0.f;
-        int jt = n > 0 ? tile_at(p0) : -1;
+        // Reference max m (exp2 domain) of this lane's query and the lane's
+        // part of the softmax denominator (lanes l and l^32 hold different
+        // keys of the same query).
+        float m_run = 0.f, l_run = 0.f;
+        bool m_init = false;
 
-        for (int t = 0; t < n; ++t) {
-            const bool more = t + 1 < n;  // tile t+1 exists: its 4 half-tiles are issued now
-            const int jn = more ? tile_at(p0 + t + 1) : -1;
-            const int64_t rn = tile_rows(jn);
-            const int nj = jt < 0 ? 0 : tile_occupancy(g, jt);
-            // Slots: half-tile 4t+p in (slot0 + p) % 5; 4(t+1)+p in (slot0 + 4 + p) % 5.
-            const int sl1 = slot0 == 4 ? 0 : slot0 + 1;
-            const int sl2 = sl1 == 4 ? 0 : sl1 + 1;
-            const int sl3 = sl2 == 4 ? 0 : sl2 + 1;
-            const int sl4 = sl3 == 4 ? 0 : sl3 + 1;
-            const int sls[4] = {slot0, sl1, sl2, sl3};
-            // Issue order of tile t+1: Klo -> slot sl4, Khi -> slot0, Vlo -> sl1, Vhi -> sl2.
-            // In flight before reading half-tile 4t+p: through 4t+3+p.
-            const int in_flight = more ? 3 : 0;  // later half-tiles of the sequence
-
-            // S^T = K Q^T, key block kb from half-tile 4t + kb.
-            f32x16 sacc[2];
+        // S^T = K Q^T of one key tile from the K half-tiles in slots
+        // (sl, next), as four groups of four k-steps; `between(g)` runs after
+        // group g's MFMAs are issued (the scheduling barriers keep the
+        // compiler from hoisting all operand reads).
+        auto scores = [&](int sl, f32x16 (&sc)[2], auto&& between) {
+            const uint32_t sb0 = (uint32_t)sl * SLOT_BYTES;
+            const uint32_t sb1 = (uint32_t)next_slot_of(sl) * SLOT_BYTES;
+            sc[0] = (f32x16){};
+            sc[1] = (f32x16){};
+            constexpr int NG = 2 * NDC / 4;
+            auto load_k = [&](int gidx, bf16x8 (&a)[4]) {
+                const int kb = gidx / (NDC / 4), d0 = (gidx % (NDC / 4)) * 4;
+                const uint32_t sb = kb == 0 ? sb0 : sb1;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                acquire(more ? 3 : 3 - kb);  // tile t: 4t+kb..4t+3 issued, maybe 4t+4..
-                if (more) {
-                    if (kb == 0) dma(k + rn, koff, sl4);           // K lo of t+1 into retired slot
-                    else dma(k + rn + 32 * rs, koff, slot0);       // K hi of t+1
-                }
-                const __bf16* kslot = ring + sls[kb] * HALF_ELEMS;
+                for (int u = 0; u < 4; ++u) a[u] = *(const lds_bf16x8*)(uintptr_t)(kaddr[d0 + u] + sb);
+            };
+            bf16x8 ka[2][4];
+            load_k(0, ka[0]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+            for (int gi = 0; gi < NG; ++gi) {
+                if (gi + 1 < NG) load_k(gi + 1, ka[(gi + 1) & 1]);
+                const int kb = gi / (NDC / 4), d0 = (gi % (NDC / 4)) * 4;
 #pragma unroll
-                for (int d0 = 0; d0 < NDC; d0 += 4) {
-                    bf16x8 a[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        a[u] = *(const bf16x8*)(kslot + l32 * D + k_phys<D>(l32, (d0 + u) * 2 + half) * 8);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) sacc[kb] = mfma32(a[u], qf[d0 + u], sacc[kb]);
-                }
+                for (int u = 0; u < 4; ++u) sc[kb] = mfma32(ka[gi & 1][u], qf[d0 + u], sc[kb]);
+                between(gi);
+                __builtin_amdgcn_sched_barrier(0);
             }
-
-            // Online softmax for query qi on raw scores (the scale is > 0), with
-            // a lazily raised reference max.  Key of (kb, r): 32kb + 8(r/4) +
-            // 4half + r%4.
-            if (nj < 64) {  // partial tile: mask keys r >= n_j (tile-uniform)
+        };
+        // Keys of tile j at or beyond its valid count score -inf.  Key of
+        // (kb, r): 32kb + 8(r/4) + 4half + r%4, compared as
+        // 4half >= n_j - (32kb + 8(r/4) + r%4) with a scalar right side.
+        auto mask = [&](f32x16 (&sc)[2], int j) {
+            const int nj = j < 0 ? 0 : (all_full ? 64 : tile_occupancy(g, j));
+            if (nj < 64) {  // tile-uniform
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-                        if (key >= nj) sacc[kb][r] = -INFINITY;
+                        const int lim = nj - (kb * 32 + (r >> 2) * 8 + (r & 3));
+                        if (half4 >= lim) sc[kb][r] = -INFINITY;
                     }
             }
-            float mx = sacc[0][0];
+            return nj;
+        };
+        // p = exp2(s*c - m) for the 8 accumulator registers [8c, 8c+8) of
+        // key block kb = c/2 as one bf16x8 B operand of the PV product (key
+        // order of the accumulator), adding the rounded p to the lane's sum.
+        auto probs_chunk = [&](const f32x16 (&sc)[2], int c, float neg_m, bf16x8& pfc, float& ps) {
+            const int kb = c >> 1, r0 = (c & 1) * 8;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int r = 0; r < 8; r += 2) {
+                const bf16x2 pp = {
+                    (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r0 + r], scale_log2, neg_m)),
+                    (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r0 + r + 1], scale_log2, neg_m))};
+                pfc[r] = pp[0];
+                pfc[r + 1] = pp[1];
+                ps = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ps, false);
+            }
+        };
+
+        f32x16 sc_cur[2];
+        int nj_cur = 0;
+        if (n > 0) {
+            const int sl = acquire();
+            scores(sl, sc_cur, [](int) {});
+            nj_cur = mask(sc_cur, tile_id(0));
+        }
+        for (int t = 0; t < n; ++t) {
+            const bool more = t + 1 < n;
+            // Probabilities of tile t, overlapped with the scores of tile t+1.
+            bf16x8 pf[4];
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+            const float neg_m = -m_run;
+            f32x16 sc_next[2];
+            if (more) {
+                // Four probability chunks spread over the score groups (two
+                // groups per chunk pair when D = 64).
+                constexpr int NG = 2 * NDC / 4;
+                const int sl = acquire();
+                scores(sl, sc_next, [&](int gi) {
 #pragma unroll
-                for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;
-            const bool raise = mx > m_run + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
-                const float m_new = raise ? mx : m_run;
-                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
+                    for (int c = gi * 4 / NG; c < (gi + 1) * 4 / NG; ++c)
+                        probs_chunk(sc_cur, c, neg_m, pf[c], ps[c]);
+                });
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) probs_chunk(sc_cur, c, neg_m, pf[c], ps[c]);
+            }
+            float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            // The reference max starts from the first tile with a valid key
+            // (m_init, wave-uniform); after that the probabilities are
+            // accepted unless some lane's sum is above 2^64 (or not
+            // finite): then m is raised to this tile's max first (rare).
+            // Lanes l and l^32 hold keys of the same query and always share
+            // m, so every decision below uses the pair's maximum.
+            const bool bad = !(psum <= 0x1p64f);
+            if (!m_init || __builtin_amdgcn_ballot_w64(bad) != 0) {
+                float mx = fmaxf(sc_cur[0][0], sc_cur[1][0]);
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc_cur[0][r], sc_cur[1][r]));
+                mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;  // tile max of s*c
+                const float m_new = !m_init ? (mx == -INFINITY ? m_run : mx) : fmaxf(m_run, mx);
+                const float alpha = !m_init ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m_run = m_new;
+                psum = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) probs_chunk(sc_cur, c, -m_new, pf[c], psum);
+                m_init = m_init || nj_cur > 0;
             }
-            const float neg_m = m_run == -INFINITY ? 0.f : -m_run;  // all masked so far: p = 0
-            float psum = 0.f;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], scale_log2, neg_m));
-                    psum += pv;
-                    pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)pv;
-                }
             l_run += psum;
 
-            // O^T += V^T P^T: 16-key steps kc; keys 0..31 in half-tile 4t+2,
-            // keys 32..63 in half-tile 4t+3.
-#pragma unroll
-            for (int vh = 0; vh < 2; ++vh) {
-                acquire(more ? 3 : 1 - vh);
-                if (more) {
-                    if (vh == 0) dma(v + rn, voff, sl1);
-                    else dma(v + rn + 32 * rs, voff, sl2);
-                }
-                const __bf16* vslot = ring + sls[2 + vh] * HALF_ELEMS;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 av[NDB];
+            // O^T += V(t)^T P(t)^T: 16-key steps kk of the V half-tiles; the
+            // V^T operands of step g+1 are read while step g multiplies.
+            {
+                const int sl = acquire();
+                const uint32_t sbv[2] = {(uint32_t)sl * SLOT_BYTES, (uint32_t)next_slot_of(sl) * SLOT_BYTES};
+                auto load_v = [&](int gidx, bf16x8 (&av)[NDB]) {
+                    const uint32_t sb = sbv[gidx >> 1] + (gidx & 1) * 32 * D;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const __bf16* a0 = vslot + vaddr[db] + kk * 16 * D;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a0);
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * D));
+                        const uint32_t a0 = vaddr[db] + sb;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a0 + 16 * D));
                         const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                         av[db] = __builtin_bit_cast(bf16x8, w);
                     }
+                };
+                bf16x8 va[2][NDB];
+                load_v(0, va[0]);
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(av[db], pf[vh * 2 + kk], oacc[db]);
+                for (int gi = 0; gi < 4; ++gi) {
+                    if (gi + 1 < 4) load_v(gi + 1, va[(gi + 1) & 1]);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[gi & 1][db], pf[gi], oacc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            (void)in_flight;
-            slot0 = sl4;
-            jt = jn;
+            if (more) {
+                nj_cur = mask(sc_next, tile_id(t + 1));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) sc_cur[kb] = sc_next[kb];
+            }
         }
-        // Retire the last slot before the next item refills the ring.
+        // Retire the last slots before the next item refills the ring.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
 

@@ -18,8 +18,11 @@ MEAN_ABS = 2e-3
 TIE_BAND = 1e-4
 # Pooled vectors: |gpu - oracle| <= POOL_TOL * (1 + |oracle|).
 POOL_TOL = 1e-5
-# Log-sum-exp of valid rows (fp32 accumulation of bf16 products).
-LSE_TOL = 2e-3
+# Log-sum-exp of valid rows.  The kernel's softmax denominator is the sum of
+# the same bf16-rounded probabilities it weights V with (8-bit significand:
+# relative rounding error at most 2^-8 each), so its log may be off by up to
+# ln(1 + 2^-8) = 3.9e-3 from the exact one, plus fp32 accumulation error.
+LSE_TOL = 5e-3
 
 _cache = {}
 

@@ -271,6 +271,47 @@ def test_empty_rows_and_out_of_range_indices(bsta):
     assert np.all(np.isfinite(H.bf16_dev_to_f32(ot2)))
 
 
+def test_unsorted_empty_and_invalid_rows(bsta):
+    """Rows that are empty, unsorted or hold ids outside [0, Nt).  Reversed
+    rows put the tiny edge tiles first, where one half of the lanes sees no
+    valid key at all: the pair must still share one reference max."""
+    import torch
+    w = SMALL["ragged_d128"]
+    inp = H.inputs(w)
+    tb, tf = _oracle_tiled(w, inp)
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    rows = w.B * w.H * nt
+    rng = np.random.default_rng(1)
+    cols, rp, mask = [], [0], np.zeros((w.B, w.H, nt, nt), dtype=bool)
+    for r in range(rows):
+        b, rem = divmod(r, w.H * nt)
+        h, i = divmod(rem, nt)
+        if r % 7 == 0:
+            sel = []
+        else:
+            sel = sorted(rng.choice(nt, size=int(rng.integers(1, nt + 1)), replace=False).tolist())
+            mask[b, h, i, sel] = True
+            if r % 3 == 0:
+                sel = sel[::-1]                 # unsorted row
+            if r % 4 == 1:
+                sel = [-5] + sel + [nt, nt + 9]  # invalid ids (sorted row stays sorted)
+        cols += sel
+        rp.append(len(cols))
+    g = _geom(bsta, w)
+    qt, kt, vt = (H.to_dev(tb[n]) for n in ("q", "k", "v"))
+    ref, rlse = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], mask, w.T, w.Y, w.X)
+    ot, lse = bsta.attn_block_sparse_fwd(
+        g, qt, kt, vt, torch.tensor(rp, dtype=torch.int32, device="cuda"),
+        torch.tensor(cols, dtype=torch.int32, device="cuda"), want_lse=True)
+    torch.cuda.synchronize()
+    got = H.bf16_dev_to_f32(ot)
+    H.compare_outputs(got, ref)
+    glse = lse.cpu().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(glse), fin)
+    assert np.abs(glse[fin] - rlse[fin]).max() <= H.LSE_TOL
+
+
 def test_deterministic(bsta):
     w = SMALL["smooth_40"]
     inp = H.inputs(w)
