@@ -18,9 +18,13 @@
 namespace bsta {
 
 // ------------------------------------------------------------------ pooling
-// grid (B*Nt, 2): one workgroup per (batch, tile, tensor).  Each thread owns
-// eight consecutive (head, d) columns and sums the tile's valid rows.
-__global__ __launch_bounds__(256) void pool_kernel(
+// grid (B*Nt, 2): one workgroup per (batch, tile, tensor), one thread per
+// eight consecutive (head, d) columns (blockDim covers the H*D row, looping
+// past 1024 columns of 8).  Each thread sums the tile's valid rows in row
+// order with 16 row loads in flight; the tile's rows are contiguous.
+constexpr int kPoolUnroll = 16;
+
+__global__ __launch_bounds__(1024) void pool_kernel(
         Geo g, const u32x4* __restrict__ q, const u32x4* __restrict__ k,
         float* __restrict__ pq, float* __restrict__ pk) {
     const int b = blockIdx.x / g.Nt;
@@ -30,30 +34,25 @@ __global__ __launch_bounds__(256) void pool_kernel(
     const int n = tile_occupancy(g, j);
     const int nvec = g.H * g.D / 8;
     const u32x4* base = src + ((int64_t)b * g.Lpad + (int64_t)j * kTileElems) * nvec;
-    for (int v = threadIdx.x; v < nvec; v += 256) {
+    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int r = 0;
-        for (; r + 8 <= n; r += 8) {
-            u32x4 w[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = base[(int64_t)(r + u) * nvec + v];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    acc[2 * c] += __uint_as_float(w[u][c] << 16);
-                    acc[2 * c + 1] += __uint_as_float(w[u][c] & 0xffff0000u);
-                }
-            }
-        }
-        for (; r < n; ++r) {
-            u32x4 w = base[(int64_t)r * nvec + v];
+        auto add = [&](const u32x4& w) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 acc[2 * c] += __uint_as_float(w[c] << 16);
                 acc[2 * c + 1] += __uint_as_float(w[c] & 0xffff0000u);
             }
+        };
+        int r = 0;
+        for (; r + kPoolUnroll <= n; r += kPoolUnroll) {
+            u32x4 w[kPoolUnroll];
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u)
+                w[u] = __builtin_nontemporal_load(&base[(int64_t)(r + u) * nvec + v]);
+#pragma unroll
+            for (int u = 0; u < kPoolUnroll; ++u) add(w[u]);
         }
+        for (; r < n; ++r) add(__builtin_nontemporal_load(&base[(int64_t)r * nvec + v]));
         const int col = v * 8;
         const int h = col / g.D;
         const int d0 = col - h * g.D;
@@ -289,7 +288,10 @@ __global__ __launch_bounds__(256) void sta_kernel(
 // ------------------------------------------------------------------ launchers
 hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
                        hipStream_t stream) {
-    hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(g.B * g.Nt), 2), dim3(256), 0, stream, g,
+    const int nvec = g.H * g.D / 8;
+    int threads = (nvec + 63) / 64 * 64;
+    if (threads > 1024) threads = 1024;
+    hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(g.B * g.Nt), 2), dim3(threads), 0, stream, g,
                        (const u32x4*)q, (const u32x4*)k, pq, pk);
     return hipGetLastError();
 }
