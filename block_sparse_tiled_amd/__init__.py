@@ -25,7 +25,7 @@ from ._lib import SELECT_STA, SELECT_TOPK, BstaError
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "attn_tile", "attn_untile",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
-    "attn_workspace_bytes", "block_sparse_attention",
+    "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
 ]
 
 
@@ -202,6 +202,13 @@ def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_i
         _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(out),
         _ptr(lse), _stream()))
     return (out, lse) if want_lse or lse is not None else out
+
+
+def attn_set_deterministic(enable: bool) -> bool:
+    """Process-wide key order of attn_block_sparse_fwd: True walks every CSR
+    row in order (bitwise reproducible), False (the default) uses the
+    cache-friendly rotated walk.  Returns the previous setting."""
+    return bool(_lib.load().attn_set_deterministic(int(bool(enable))))
 
 
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,

@@ -155,6 +155,24 @@ __device__ inline void wait_dma(int newer) {
     }
 }
 
+// Per-XCD sweep counters (one 128-byte line each): key tiles processed on
+// that XCD, bumped in steps of four.  Only the key order within rows
+// depends on them (see the kernel), so calls that overlap on one device, or
+// a counter that wraps, change speed, never results' validity.
+__device__ unsigned int g_sweep[8 * 32];
+
+// Sweep target (a key tile id in [0, nt)) for sweep clock value c.
+__device__ inline int sweep_target(uint32_t c, uint32_t period, int nt) {
+    return (int)(((uint64_t)(c % period) * (uint64_t)nt) / period);
+}
+
+// Read of the sweep clock: an atomic load, which is served by the XCD's L2
+// (where the counter's atomic adds happen), not by a CU's L1.
+__device__ inline uint32_t read_sweep(const unsigned int* ctr) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+
 }  // namespace
 
 template <int D>
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
         const int32_t* __restrict__ col_idx, int64_t col_len, float scale_log2,
-        __bf16* __restrict__ o, float* __restrict__ lse, int64_t items_per_xcd) {
+        __bf16* __restrict__ o, float* __restrict__ lse, int64_t items_per_xcd, int rotate) {
     constexpr int NDC = D / 16;                    // MFMA k-steps for S (16 d each)
     constexpr int NDB = D / 32;                    // 32-row d blocks of O^T
     constexpr int HALF_ELEMS = 32 * D;             // one half-tile slot
@@ -232,6 +250,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t first = (int64_t)xcd * items_per_xcd;
     const int64_t last = first + items_per_xcd < n_items ? first + items_per_xcd : n_items;
 
+    // Key-order rotation for L2 reuse.  The rows' key tiles are scattered
+    // over the whole head, so the K/V working set of one XCD's resident
+    // workgroups is the entire head, far beyond its L2.  Walking every row
+    // in ascending order shares cache lines only while the workgroups stay
+    // in step, and they drift apart.  Instead each row starts at the first
+    // key tile at or above a target id that sweeps 0..Nt-1 once per average
+    // item duration, measured in key tiles processed on the XCD (one period
+    // is S workgroups times the mean row length).  Concurrent workgroups
+    // then touch neighbouring key ids whatever their start times.  Any
+    // rotation visits the same set of keys, so only rounding depends on it.
+    unsigned int* const sweep = &g_sweep[xcd * 32];
+    int64_t nnz = rp_s[n_items];
+    nnz = nnz < 0 ? 0 : (nnz > col_len ? col_len : nnz);
+    const uint64_t per_raw = (uint64_t)S * (uint64_t)nnz / (uint64_t)(n_items > 0 ? n_items : 1);
+    const uint32_t period = per_raw == 0 ? 1u : (per_raw > 0x7fffffffu ? 0x7fffffffu : (uint32_t)per_raw);
+    // Wave 0 hands each item's rotation start to wave 1 through the first
+    // word of the last ring slot: between an item's final barrier and the
+    // next item's first acquire the prologue fills only the first three
+    // slots, so that word is free, and the ring keeps the workgroup's LDS at
+    // exactly five slots (four workgroups per CU).
+    int* const handoff = (int*)&ring[(kRing - 1) * HALF_ELEMS];
+
     for (int64_t item = first + slot; item < last; item += S) {
         const int bh = (int)(item / g.Nt);
         const int i = (int)(item - (int64_t)bh * g.Nt);
@@ -246,11 +286,36 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
         const int n = (int)(p1 - p0);
 
-        // Tile id at CSR position p0 + t, or -1 when t is past the row or the
-        // id is out of range (then tile 0 is fetched and fully masked).
+        // Rotation start k0: the number of the row's entries below the sweep
+        // target, i.e. for a sorted row the first entry at or above it (any
+        // start visits the same entries).  With rotation off (deterministic
+        // mode) every row is walked from its first entry.
+        int k0 = 0;
+        if (rotate && n > 1) {  // workgroup-uniform
+            if (wave == 0) {
+                const uint32_t c = read_sweep(sweep);
+                const int target = sweep_target(c, period, g.Nt);
+                int cnt = 0;
+                for (int base = 0; base < n; base += 64) {
+                    const int idx = base + lane;
+                    const int j = idx < n ? col_idx[p0 + idx] : 0x7fffffff;
+                    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j < target));
+                }
+                if (lane == 0) *handoff = cnt < n ? cnt : 0;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            k0 = __builtin_amdgcn_readfirstlane(*(volatile int*)handoff);
+        }
+
+        // Tile id of step t (CSR position p0 + (k0 + t) mod n), or -1 when t
+        // is past the row or the id is out of range (then tile 0 is fetched
+        // and fully masked).
         auto tile_id = [&](int t) -> int {
             if (t >= n) return -1;
-            const int j = ci_s[p0 + t];
+            const int r = t + k0 < n ? t + k0 : t + k0 - n;
+            const int j = ci_s[p0 + r];
             return (unsigned)j < (unsigned)g.Nt ? j : -1;
         };
         // Byte offset of a tile's first row from the head's base.
@@ -444,6 +509,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // V^T operands of step g+1 are read while step g multiplies.
             {
                 const int sl = acquire();
+                // Advance the XCD's sweep clock (no return value: nothing
+                // waits for it).
+                if (rotate && (t & 3) == 3 && tid == 0)
+                    __hip_atomic_fetch_add(sweep, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const uint32_t sbv[2] = {(uint32_t)sl * SLOT_BYTES, (uint32_t)next_slot_of(sl) * SLOT_BYTES};
                 auto load_v = [&](int gidx, bf16x8 (&av)[NDB]) {
                     const uint32_t sb = sbv[gidx >> 1] + (gidx & 1) * 32 * D;
@@ -525,7 +594,7 @@ int resident_per_xcd(const void* kernel) {
 
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, hipStream_t stream) {
+                           float scale, void* o, float* lse, bool rotate, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     const void* kernel =
         g.D == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
@@ -537,11 +606,11 @@ hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const voi
     if (g.D == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd);
+                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0);
     else
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd);
+                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "bsta_common.hpp"
 
 namespace bsta {
@@ -27,7 +29,7 @@ hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32
                       int32_t* col_idx, hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, hipStream_t stream);
+                           float scale, void* o, float* lse, bool rotate, hipStream_t stream);
 }  // namespace bsta
 
 using bsta::Geo;
@@ -35,6 +37,9 @@ using bsta::Geo;
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Process-wide key-order mode of attn_block_sparse_fwd (0 = rotated walk).
+std::atomic<int> g_deterministic{0};
 
 // Largest tile count top-k selection accepts (its per-row keys and flags
 // live in LDS: 5 bytes per tile).
@@ -271,8 +276,13 @@ int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const v
     if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
     return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                                             col_len, softmax_scale, o_tiled, lse,
+                                            g_deterministic.load(std::memory_order_relaxed) == 0,
                                             (hipStream_t)stream),
                       "attn_block_sparse_fwd");
+}
+
+int32_t attn_set_deterministic(int32_t enable) {
+    return g_deterministic.exchange(enable != 0 ? 1 : 0, std::memory_order_relaxed);
 }
 
 }  // extern "C"

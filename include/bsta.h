@@ -21,8 +21,11 @@
  *   - Every tensor, mask and index pointer is a DEVICE pointer unless its
  *     comment says host.  The caller allocates and owns all memory and the
  *     stream.  The library allocates nothing, frees nothing, never
- *     synchronises, keeps no device state, and enqueues every kernel on the
- *     given stream (a hipStream_t passed as void*; NULL = the null stream).
+ *     synchronises, and enqueues every kernel on the given stream (a
+ *     hipStream_t passed as void*; NULL = the null stream).  Its only device
+ *     state is a small static array of counters that attn_block_sparse_fwd
+ *     uses to order its walk over each row's key tiles (see there); it
+ *     never decides which keys are attended.
  *   - Every call checks its arguments on the host before any HIP call and
  *     returns a status (0 = BSTA_OK).  On failure nothing is enqueued and
  *     attn_last_error() returns a thread-local message with the detail.
@@ -162,11 +165,28 @@ int32_t attn_select_blocks(const bsta_geom* g, const void* q_tiled, const void* 
  *   o_tiled  [out] bf16 [B, Lpad, H, D]
  *   lse      [out, fp32 [B, H, Lpad], may be NULL] natural-log softmax
  *            normaliser of the scaled scores
+ * Key order.  The softmax is a sum over the row's key tiles, so their order
+ * changes only rounding.  By default each row is walked cyclically from a
+ * start that depends on how far the GPU has progressed through the call (a
+ * device-side counter), so that workgroups running at the same time read
+ * neighbouring key tiles and share them in cache; results then agree with
+ * any other order to rounding but are not bitwise reproducible from call to
+ * call.  attn_set_deterministic(1) walks every row in its CSR order instead.
  */
 int32_t attn_block_sparse_fwd(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
                               int64_t col_len, float softmax_scale, int32_t causal,
                               void* o_tiled, float* lse, void* stream);
+
+/*
+ * attn_set_deterministic (host only, no HIP call): process-wide key order of
+ * attn_block_sparse_fwd for calls made after it returns.  enable != 0: every
+ * row is walked in CSR order, so equal inputs give bitwise equal outputs;
+ * 0 (the default): the cache-friendly rotated walk described above.
+ * Returns the previous setting (0 or 1).  Thread-safe; calls already
+ * enqueued keep the mode they were made with.
+ */
+int32_t attn_set_deterministic(int32_t enable);
 
 /* Text of a status code (static storage). */
 const char* attn_status_string(int32_t status);

@@ -162,3 +162,16 @@ def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.attn_status_string(code)
     assert lib.attn_status_string(42) == b"unknown status"
+
+
+def test_set_deterministic_returns_previous(lib):
+    """Host-only switch: each call returns the previous mode (0 or 1)."""
+    first = lib.attn_set_deterministic(1)
+    try:
+        assert first in (0, 1)
+        assert lib.attn_set_deterministic(1) == 1
+        assert lib.attn_set_deterministic(0) == 1
+        assert lib.attn_set_deterministic(7) == 0
+        assert lib.attn_set_deterministic(0) == 1
+    finally:
+        lib.attn_set_deterministic(first)

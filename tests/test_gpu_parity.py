@@ -313,12 +313,37 @@ def test_unsorted_empty_and_invalid_rows(bsta):
 
 
 def test_deterministic(bsta):
+    """Deterministic mode: equal inputs give bitwise equal outputs."""
     w = SMALL["smooth_40"]
     inp = H.inputs(w)
-    a = _run_gpu(bsta, w, inp)
-    b = _run_gpu(bsta, w, inp)
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        a = _run_gpu(bsta, w, inp)
+        b = _run_gpu(bsta, w, inp)
+    finally:
+        bsta.attn_set_deterministic(prev)
     assert np.array_equal(H.from_dev(a["o"]), H.from_dev(b["o"]))
     assert np.array_equal(a["sel"].col_idx.cpu().numpy(), b["sel"].col_idx.cpu().numpy())
+
+
+def test_rotated_walk_matches_deterministic(bsta):
+    """The default rotated key walk differs from the CSR-order walk by
+    rounding only: the same selection, outputs within the parity bound of each
+    other and of the oracle, over several calls (each starts its rows at
+    different keys)."""
+    w = SMALL["smooth_40"]
+    inp = H.inputs(w)
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        ref = _run_gpu(bsta, w, inp)
+    finally:
+        bsta.attn_set_deterministic(prev)
+    assert prev is False, "the default mode is the rotated walk"
+    want = H.bf16_dev_to_f32(ref["o"])
+    for _ in range(3):
+        r = _run_gpu(bsta, w, inp)
+        assert np.array_equal(r["sel"].col_idx.cpu().numpy(), ref["sel"].col_idx.cpu().numpy())
+        H.compare_outputs(H.bf16_dev_to_f32(r["o"]), want, "rotated vs CSR order")
 
 
 # ---------------------------------------------------------------- full sizes
