@@ -37,11 +37,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "f2d11d8d289c4659",
-    "fetch_kib": 78624988, "write_kib": 782043,
-    "traffic_bytes": 161824787456,
-    "l2_hit": 0.172, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.295, "clock_ghz": 1.755,
+    "src_sha256_16": "3bbea51730aaf091",
+    "fetch_kib": 56461047, "write_kib": 819785,
+    "traffic_bytes": 116471684096,
+    "l2_hit": 0.399, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.337, "clock_ghz": 1.800,
 }
 
 
@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--deterministic", action="store_true",
+                   help="walk every CSR row in order (attn_set_deterministic) instead of the "
+                        "default rotated key walk")
     p.add_argument("--mode", default="path", choices=["path", "copy"],
                    help="copy: time a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -131,6 +134,7 @@ def main():
     import block_sparse_tiled_amd as bsta
     import workloads
 
+    bsta.attn_set_deterministic(args.deterministic)
     w = workloads.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w)
@@ -197,7 +201,7 @@ def main():
     print(f"[bench] per-call ms {ms}", file=sys.stderr, flush=True)
 
     flop = attention_flop(w, nnz)
-    prof = measured_attn() if args.workload == "c3" else None
+    prof = measured_attn() if args.workload == "c3" and not args.deterministic else None
     dense_flop = 4.0 * w.D * w.B * w.H * float(w.L) ** 2
     attn_tflops = flop / (ms["attn_fwd"] * 1e-3) / 1e12
     elem = w.B * w.H * w.D * 2
@@ -222,6 +226,8 @@ def main():
                         f"(L={w.L}, {nt} tiles of 4x4x4), "
                         + (f"top-k {w.topk}" if w.mode == "topk" else "STA windows"),
             "selected_tile_pairs": nnz,
+            "attn_key_order": "csr order (deterministic)" if args.deterministic
+                              else "rotated walk (library default)",
             "value_basis": "selected-tile attention FLOP (4*D*64*64 per pair) per whole-path step",
         },
         "roofline": {
