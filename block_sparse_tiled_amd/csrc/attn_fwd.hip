@@ -10,7 +10,8 @@
 // such workgroups share a CU, so each SIMD runs two waves whose softmax and
 // MFMA phases overlap.  Per selected key tile:
 //   1. K and V arrive in LDS by direct global->LDS DMA (global_load_lds_
-//      dwordx4, 1 KB per instruction; each wave issues half of the blocks)
+//      dwordx4, 1 KB per instruction; each half-tile is issued whole by one
+//      wave, the low halves by wave 0 and the high halves by wave 1)
 //      into a ring of five half-tile slots (32 keys x D): K low half, K high
 //      half, V low, V high, then the next tile.  Before a slot is read, one
 //      workgroup barrier both publishes it and retires the previous slot,
@@ -81,78 +82,78 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Issue this wave's NI blocks (1 KB each) of one half-tile (32 rows x D bf16)
-// by direct-to-LDS DMA: its block u lands at LDS byte lds0 + 2048*u (the two
-// waves interleave).  `voff` holds the per-lane source byte offsets from
-// `base`.  Written as inline asm so that the compiler does
-// not guard every later LDS read with a wait for all outstanding DMA; the
-// kernel waits on vmcnt itself.  M0 (the DMA's LDS base) is saved and
-// restored around the block.
-template <int NI>
-__device__ inline void dma_half(uint64_t base_any, const int32_t* voff, uint32_t lds_any) {
+// Issue one whole half-tile (32 rows x D bf16, NB = D/16 blocks of 1 KB)
+// from the calling wave by direct-to-LDS DMA: block u lands at LDS byte
+// slot + 1024*u.  The DMA's LDS address is M0 + the instruction's immediate
+// offset + 16*lane, and the same immediate is added to the global address
+// (checked on hardware), so M0 is set once, to slot + kDmaBias<D>, and block
+// u uses offset 1024*u - kDmaBias<D> (inside the signed 13-bit range).
+// `voff` holds the per-lane source byte offsets of blocks 0..3 from `base`
+// with their immediates already subtracted; for D = 128 blocks 4..7 (rows
+// 16..31) reuse them from a second base 16 rows further (less 4096, the
+// extra immediate), since the LDS swizzles depend on the row only modulo 16.
+// Written as inline asm so that the compiler does not guard every later LDS
+// read with a wait for all outstanding DMA; the kernel waits on vmcnt itself.
+// M0 is saved and restored around the block.
+template <int D>
+constexpr int kDmaBias = D == 128 ? 3584 : 1536;
+
+template <int D>
+__device__ inline void dma_half(uint64_t base_any, uint64_t rows16, const int32_t* voff,
+                                uint32_t slot_lds) {
     // Both bases are wave-uniform; make them SGPRs.  (readfirstlane returns
     // int: go through uint32_t so the low half is never sign-extended.)
-    const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_any);
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane(slot_lds + kDmaBias<D>);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base_any >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base_any);
     const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
     uint32_t saved;
-    if constexpr (NI == 4) {
+    if constexpr (D == 128) {
+        const uint64_t base16 = base + rows16 - 4096;
         asm volatile(
             "s_mov_b32 %[t], m0\n\t"
             "s_mov_b32 m0, %[l]\n\t"
             "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b]\n\t"
-            "s_add_u32 m0, m0, 2048\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b]\n\t"
-            "s_add_u32 m0, m0, 2048\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v2], %[b]\n\t"
-            "s_add_u32 m0, m0, 2048\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v3], %[b]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:-3584\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] offset:-2560\n\t"
+            "global_load_lds_dwordx4 %[v2], %[b] offset:-1536\n\t"
+            "global_load_lds_dwordx4 %[v3], %[b] offset:-512\n\t"
+            "global_load_lds_dwordx4 %[v0], %[c] offset:512\n\t"
+            "global_load_lds_dwordx4 %[v1], %[c] offset:1536\n\t"
+            "global_load_lds_dwordx4 %[v2], %[c] offset:2560\n\t"
+            "global_load_lds_dwordx4 %[v3], %[c] offset:3584\n\t"
             "s_mov_b32 m0, %[t]"
             : [t] "=&s"(saved)
-            : [l] "s"(lds0), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]),
-              [v2] "v"(voff[2]), [v3] "v"(voff[3])
-            : "memory", "scc");
+            : [l] "s"(m0v), [b] "s"(base), [c] "s"(base16), [v0] "v"(voff[0]),
+              [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3])
+            : "memory");
     } else {
-        static_assert(NI == 2, "half-tile of 32 x 64 or 32 x 128 bf16, two waves");
+        static_assert(D == 64, "head dim 64 or 128");
+        (void)rows16;
         asm volatile(
             "s_mov_b32 %[t], m0\n\t"
             "s_mov_b32 m0, %[l]\n\t"
             "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b]\n\t"
-            "s_add_u32 m0, m0, 2048\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:-1536\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] offset:-512\n\t"
+            "global_load_lds_dwordx4 %[v2], %[b] offset:512\n\t"
+            "global_load_lds_dwordx4 %[v3], %[b] offset:1536\n\t"
             "s_mov_b32 m0, %[t]"
             : [t] "=&s"(saved)
-            : [l] "s"(lds0), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1])
-            : "memory", "scc");
+            : [l] "s"(m0v), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]),
+              [v2] "v"(voff[2]), [v3] "v"(voff[3])
+            : "memory");
     }
 }
 
-// Wait until at most `newer` half-tiles issued after the one about to be
-// read are still in flight (each half-tile is NI DMA instructions).
-template <int NI>
+// Wait until at most `newer` (0..2) half-tiles this wave issued after the
+// one about to be read are still in flight (each half-tile is NP DMA
+// instructions of the issuing wave).
+template <int NP>
 __device__ inline void wait_dma(int newer) {
-    if constexpr (NI == 4) {
-        switch (newer) {
-            case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-            case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-            case 2: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-            default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-        }
-    } else {
-        switch (newer) {
-            case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-            case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-            case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-            default: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        }
-    }
+    if (newer <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NP) : "memory");
 }
 
 // Per-XCD sweep counters (one 128-byte line each): key tiles processed on
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NDC = D / 16;                    // MFMA k-steps for S (16 d each)
     constexpr int NDB = D / 32;                    // 32-row d blocks of O^T
     constexpr int HALF_ELEMS = 32 * D;             // one half-tile slot
-    constexpr int NI = HALF_ELEMS * 2 / 1024 / 2;  // DMA instructions per wave per half-tile
+    constexpr int NP = HALF_ELEMS * 2 / 1024;      // DMA instructions per half-tile (one wave)
     constexpr int SLOT_BYTES = HALF_ELEMS * 2;
     __shared__ __attribute__((aligned(1024))) __bf16 ring[kRing * HALF_ELEMS];
 
@@ -194,27 +195,29 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const cptr ci_s = (cptr)col_idx;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int lane = tid & 63;
+    // Wave-uniform by construction; readfirstlane tells the compiler so.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t rs = (int64_t)g.H * D;  // elements between consecutive tokens
     const int64_t rs2 = rs * 2;           // bytes
     const bool all_full = (g.T & 3) == 0 && (g.Y & 3) == 0 && (g.X & 3) == 0;
 
     // Per-lane DMA source offsets (bytes, relative to the half-tile's first
-    // row) of this wave's blocks: block t = wave + 2u covers slot bytes
-    // [1024t, 1024t+1024), i.e. row r = (1024t + 16*lane) / (2D), physical
-    // chunk p; the lane fetches the logical chunk the swizzle stores at p.
-    int32_t koff[NI], voff[NI];
+    // row) of blocks 0..3: block u covers slot bytes [1024u, 1024u+1024),
+    // i.e. row r = (1024u + 16*lane) / (2D), physical chunk p; the lane
+    // fetches the logical chunk the swizzle stores at p.
+    int32_t koff[4], voff[4];
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
-        const int byte = (wave + 2 * u) * 1024 + lane * 16;
+    for (int u = 0; u < 4; ++u) {
+        const int byte = u * 1024 + lane * 16;
         const int r = byte / (2 * D);
         const int p = (byte % (2 * D)) / 16;
-        koff[u] = 2 * ((int32_t)(r * rs) + k_phys<D>(r, p) * 8);
-        voff[u] = 2 * ((int32_t)(r * rs) + v_phys<D>(r, p) * 8);
+        const int imm = 1024 * u - kDmaBias<D>;  // the block's immediate offset
+        koff[u] = 2 * ((int32_t)(r * rs) + k_phys<D>(r, p) * 8) - imm;
+        voff[u] = 2 * ((int32_t)(r * rs) + v_phys<D>(r, p) * 8) - imm;
     }
-    // This wave's DMA destination inside slot 0 (uniform: keep it scalar).
-    const uint32_t dma_lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(ring) + wave * 1024);
+    const uint64_t rows16 = (uint64_t)(16 * rs2);
 
     // LDS read addresses (bytes) inside slot 0; a slot adds a constant.
     // K operand for k-step dc: row l32, logical chunk 2*dc + half.
@@ -335,48 +338,64 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // Half-tiles are consumed in the order K0lo K0hi, then per key tile
         // t: K(t+1)lo K(t+1)hi V(t)lo V(t)hi (no K after the last tile);
-        // sequence position s sits in ring slot s % kRing.
+        // sequence position s sits in ring slot s % kRing.  Wave w issues
+        // the positions of parity w (the low halves, or the high ones), each
+        // as one whole half-tile.
         const int NSEQ = 4 * n;
-        int next_pos = 0, next_slot = 0;  // DMA producer
-        auto issue_next = [&]() {
-            const int s = next_pos;
-            bool is_k;
-            int t, hi;
-            if (s < 2) {
-                is_k = true, t = 0, hi = s;
-            } else if (s >= NSEQ - 2) {
-                is_k = false, t = n - 1, hi = s - (NSEQ - 2);
-            } else {
-                const int q4 = (s - 2) >> 2, w = (s - 2) & 3;
-                is_k = w < 2, t = is_k ? q4 + 1 : q4, hi = w & 1;
-            }
-            const uint64_t src = (is_k ? kbase : vbase) + tile_bytes(tile_id(t)) + (hi ? 32 * rs2 : 0);
-            dma_half<NI>(src, is_k ? koff : voff, dma_lds + next_slot * SLOT_BYTES);
-            ++next_pos;
-            next_slot = next_slot == kRing - 1 ? 0 : next_slot + 1;
-        };
-        // Consumer: pairs of positions.  acquire() waits for this wave's DMA
-        // of the pair (the next position may stay in flight), then a barrier
-        // makes the pair visible to both waves and retires the previous
-        // pair, whose slots are refilled right away.  Returns the pair's
-        // first slot (the second is the next one, cyclically).
+        int my_next = wave;               // next position this wave issues
+        int my_slot = wave;               // and its ring slot
+        const uint64_t hi_off = wave ? (uint64_t)(32 * rs2) : 0;
+        // Byte offsets of the tiles of the last K step issued and of the one
+        // before: each tile id is looked up once, at this wave's half of its
+        // K; V(t) then reuses it (the last V follows its own K).
+        uint64_t off_k = 0, off_km1 = 0;
+        // (Producer and acquire are statement macros: captured by closures,
+        // this state would be kept in memory.)
+        //
+        // Position s: K(0) at 0, 1; then K(t+1) at s % 4 in {2, 3} and V(t)
+        // at s % 4 in {0, 1}; V(n-1) at NSEQ-2, NSEQ-1.  The half is s & 1
+        // throughout, i.e. this wave's.  (The element-wise select of the
+        // offsets keeps both arrays in registers.)
+#define BSTA_ISSUE_NEXT()                                                                  \
+    do {                                                                                   \
+        const int s_ = my_next;                                                            \
+        const bool tail_ = s_ >= NSEQ - 2;                                                 \
+        const bool is_k_ = s_ < 2 || (!tail_ && (s_ & 2) != 0);                            \
+        if (is_k_) {                                                                       \
+            off_km1 = off_k;                                                               \
+            off_k = tile_bytes(tile_id(s_ < 2 ? 0 : ((s_ - 2) >> 2) + 1));                 \
+        }                                                                                  \
+        const uint64_t src_ = (is_k_ ? kbase : vbase) + (is_k_ || tail_ ? off_k : off_km1) + \
+                              hi_off;                                                      \
+        int32_t offs_[4];                                                                  \
+        _Pragma("unroll") for (int u_ = 0; u_ < 4; ++u_) offs_[u_] =                       \
+            is_k_ ? koff[u_] : voff[u_];                                                   \
+        dma_half<D>(src_, rows16, offs_, ring0 + (uint32_t)my_slot * SLOT_BYTES);          \
+        my_next += 2;                                                                      \
+        my_slot = my_slot >= kRing - 2 ? my_slot + 2 - kRing : my_slot + 2;                \
+    } while (0)
+        // Consumer: pairs of positions (one per wave).  Acquiring waits for
+        // this wave's position of the pair (its later ones may stay in
+        // flight), then a barrier makes the pair visible to both waves and
+        // retires the previous pair, whose slots are refilled right away.
+        // Gives the pair's first slot (the second is the next one,
+        // cyclically).
         int read_pos = 0, read_slot = 0;
-        auto acquire = [&]() -> int {
-            if (next_pos > read_pos + 2) wait_dma<NI>(1);
-            else wait_dma<NI>(0);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            const int lim = read_pos + kRing < NSEQ ? read_pos + kRing : NSEQ;
-            while (next_pos < lim) issue_next();
-            const int sl = read_slot;
-            read_pos += 2;
-            read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;
-            return sl;
-        };
+#define BSTA_ACQUIRE(sl_out)                                                               \
+    do {                                                                                   \
+        wait_dma<NP>((my_next - (read_pos + wave) - 2) >> 1);                              \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
+        __builtin_amdgcn_s_barrier();                                                      \
+        const int lim_ = read_pos + kRing < NSEQ ? read_pos + kRing : NSEQ;                \
+        while (my_next < lim_) BSTA_ISSUE_NEXT();                                          \
+        (sl_out) = read_slot;                                                              \
+        read_pos += 2;                                                                     \
+        read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;        \
+    } while (0)
         auto next_slot_of = [](int sl) { return sl == kRing - 1 ? 0 : sl + 1; };
         // Prologue: positions 0..2.  Every slot of the previous item was
         // retired behind a barrier.
-        while (next_pos < 3 && next_pos < NSEQ) issue_next();
+        while (my_next < 3 && my_next < NSEQ) BSTA_ISSUE_NEXT();
 
         f32x16 oacc[NDB];
 #pragma unroll
@@ -452,7 +471,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         f32x16 sc_cur[2];
         int nj_cur = 0;
         if (n > 0) {
-            const int sl = acquire();
+            int sl;
+            BSTA_ACQUIRE(sl);
             scores(sl, sc_cur, [](int) {});
             nj_cur = mask(sc_cur, tile_id(0));
         }
@@ -467,7 +487,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // Four probability chunks spread over the score groups (two
                 // groups per chunk pair when D = 64).
                 constexpr int NG = 2 * NDC / 4;
-                const int sl = acquire();
+                int sl;
+            BSTA_ACQUIRE(sl);
                 scores(sl, sc_next, [&](int gi) {
 #pragma unroll
                     for (int c = gi * 4 / NG; c < (gi + 1) * 4 / NG; ++c)
@@ -508,7 +529,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // O^T += V(t)^T P(t)^T: 16-key steps kk of the V half-tiles; the
             // V^T operands of step g+1 are read while step g multiplies.
             {
-                const int sl = acquire();
+                int sl;
+            BSTA_ACQUIRE(sl);
                 // Advance the XCD's sweep clock (no return value: nothing
                 // waits for it).
                 if (rotate && (t & 3) == 3 && tid == 0)
@@ -541,6 +563,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int kb = 0; kb < 2; ++kb) sc_cur[kb] = sc_next[kb];
             }
         }
+#undef BSTA_ACQUIRE
+#undef BSTA_ISSUE_NEXT
         // Retire the last slots before the next item refills the ring.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
