@@ -294,6 +294,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // start visits the same entries).  With rotation off (deterministic
         // mode) every row is walked from its first entry.
         int k0 = 0;
+        // A clean row (every tile full, every id in range) needs no key
+        // masking, so its steps skip the tile lookup that masking needs.
+        // Both waves read the same ids and reach the same verdict.
+        bool clean = all_full;
+        if (all_full) {
+            for (int base = 0; base < n; base += 64) {
+                const int idx = base + lane;
+                const int j = idx < n ? col_idx[p0 + idx] : 0;
+                clean = clean && __builtin_amdgcn_ballot_w64((unsigned)j >= (unsigned)g.Nt) == 0;
+            }
+        }
         if (rotate && n > 1) {  // workgroup-uniform
             if (wave == 0) {
                 const uint32_t c = read_sweep(sweep);
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             int sl;
             BSTA_ACQUIRE(sl);
             scores(sl, sc_cur, [](int) {});
-            nj_cur = mask(sc_cur, tile_id(0));
+            nj_cur = clean ? 64 : mask(sc_cur, tile_id(0));
         }
         for (int t = 0; t < n; ++t) {
             const bool more = t + 1 < n;
@@ -558,7 +569,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
             if (more) {
-                nj_cur = mask(sc_next, tile_id(t + 1));
+                nj_cur = clean ? 64 : mask(sc_next, tile_id(t + 1));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) sc_cur[kb] = sc_next[kb];
             }
