@@ -37,11 +37,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "3bbea51730aaf091",
-    "fetch_kib": 56461047, "write_kib": 819785,
-    "traffic_bytes": 116471684096,
-    "l2_hit": 0.399, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.337, "clock_ghz": 1.800,
+    "src_sha256_16": "00c710fc27857417",
+    "fetch_kib": 54557855, "write_kib": 876544,
+    "traffic_bytes": 112632068096,
+    "l2_hit": 0.425, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.407, "clock_ghz": 1.717,
 }
 
 
