@@ -404,6 +404,35 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;        \
     } while (0)
         auto next_slot_of = [](int sl) { return sl == kRing - 1 ? 0 : sl + 1; };
+        // Steady state (at least two key tiles after step t's).  The
+        // generic acquire then always does the same thing: each wave issues
+        // exactly one half-tile (wave 0 the low half of K(t+2) at the K
+        // acquire and of V(t+1) at the V acquire; wave 1 the high half of
+        // V(t), then of K(t+2)), and at the wait wave 0 has one newer
+        // half-tile of its own in flight, wave 1 none.  This fixed form
+        // drops the generic loop's position bookkeeping, about a quarter of
+        // the scalar instructions per key tile.  `do_k` selects the K issue;
+        // `jraw2` is the unchecked id of tile t+2, loaded before the waits.
+#define BSTA_ACQUIRE_STEADY(sl_out, do_k)                                                  \
+    do {                                                                                   \
+        if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP) : "memory");          \
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                              \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
+        __builtin_amdgcn_s_barrier();                                                      \
+        const uint32_t slot_ = ring0 + (uint32_t)my_slot * SLOT_BYTES;                     \
+        if (do_k) {                                                                        \
+            off_km1 = off_k;                                                               \
+            off_k = (unsigned)jraw2 < (unsigned)g.Nt ? (uint64_t)jraw2 * tile_stride : 0;   \
+            dma_half<D>(kbase + off_k + hi_off, rows16, koff, slot_);                      \
+        } else {                                                                           \
+            dma_half<D>(vbase + off_km1 + hi_off, rows16, voff, slot_);                    \
+        }                                                                                  \
+        my_next += 2;                                                                      \
+        my_slot = my_slot >= kRing - 2 ? my_slot + 2 - kRing : my_slot + 2;                \
+        (sl_out) = read_slot;                                                              \
+        read_pos += 2;                                                                     \
+        read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;        \
+    } while (0)
         // Prologue: positions 0..2.  Every slot of the previous item was
         // retired behind a barrier.
         while (my_next < 3 && my_next < NSEQ) BSTA_ISSUE_NEXT();
@@ -481,6 +510,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         f32x16 sc_cur[2];
         int nj_cur = 0;
+        // CSR index of tile t+2 in the rotated walk (used only while t+2 <
+        // n, and then in [0, n)).
+        const cptr rowp = ci_s + p0;
+        const uint64_t tile_stride = (uint64_t)(64 * rs2);
+        int r2 = k0 + 2;
+        r2 = r2 >= n ? r2 - n : r2;
         if (n > 0) {
             int sl;
             BSTA_ACQUIRE(sl);
@@ -489,6 +524,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         for (int t = 0; t < n; ++t) {
             const bool more = t + 1 < n;
+            const bool steady = t + 2 < n;
+            // Raw id of tile t+2 (checked after the barrier, so that the
+            // scalar load's latency hides behind the waits).
+            const int jraw2 = steady ? rowp[r2] : -1;
             // Probabilities of tile t, overlapped with the scores of tile t+1.
             bf16x8 pf[4];
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -499,7 +538,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // groups per chunk pair when D = 64).
                 constexpr int NG = 2 * NDC / 4;
                 int sl;
-            BSTA_ACQUIRE(sl);
+                if (steady) BSTA_ACQUIRE_STEADY(sl, wave == 0);
+                else BSTA_ACQUIRE(sl);
                 scores(sl, sc_next, [&](int gi) {
 #pragma unroll
                     for (int c = gi * 4 / NG; c < (gi + 1) * 4 / NG; ++c)
@@ -541,7 +581,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // V^T operands of step g+1 are read while step g multiplies.
             {
                 int sl;
-            BSTA_ACQUIRE(sl);
+                if (steady) BSTA_ACQUIRE_STEADY(sl, wave == 1);
+                else BSTA_ACQUIRE(sl);
                 // Advance the XCD's sweep clock (no return value: nothing
                 // waits for it).
                 if (rotate && (t & 3) == 3 && tid == 0)
@@ -568,6 +609,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            r2 = r2 + 1 >= n ? r2 + 1 - n : r2 + 1;
             if (more) {
                 nj_cur = clean ? 64 : mask(sc_next, tile_id(t + 1));
 #pragma unroll
@@ -575,6 +617,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
 #undef BSTA_ACQUIRE
+#undef BSTA_ACQUIRE_STEADY
 #undef BSTA_ISSUE_NEXT
         // Retire the last slots before the next item refills the ring.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
