@@ -233,6 +233,73 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 }
 
+// One wave per CSR row, for rows of at most 64*C scores: lane l holds
+// scores j = 64c + l, c < C, in registers (coalesced loads, no LDS, no
+// barriers).  The k-th largest key is found bit by bit from the top: a bit
+// is kept when at least k keys are at or above the candidate (one ballot and
+// popcount per register).  Then keys above it are kept, and of the keys
+// equal to it the first k - (count above) in j order; with j = 64c + l,
+// walking c upward and ranking lanes by mbcnt visits j in increasing order,
+// so the same ballots give the tie ranks and the ascending CSR positions.
+template <int C>
+__global__ __launch_bounds__(256) void topk_wave_kernel(
+        int Nt, int k, int64_t rows, const float* __restrict__ s,
+        uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr,
+        int32_t* __restrict__ col_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const float* srow = s + row * Nt;
+    uint32_t key[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * 64 + lane;
+        key[c] = j < Nt ? score_key(srow[j]) : 0u;
+    }
+    // Padding slots hold key 0 and every candidate below is >= 1, so they
+    // never count; a real key 0 is handled by the explicit validity test in
+    // the final pass.
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
+        if (cnt >= k) thr = cand;
+    }
+    int above = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const bool valid = c * 64 + lane < Nt;
+        above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key[c] > thr));
+    }
+    const int take_eq = k - above;
+    int32_t* out = col_idx + row * k;
+    uint8_t* mrow = mask ? mask + row * Nt : nullptr;
+    int base = 0, eq_base = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * 64 + lane;
+        const bool valid = j < Nt;
+        const bool eq = valid && key[c] == thr;
+        const uint64_t eqm = __builtin_amdgcn_ballot_w64(eq);
+        const int eq_rank = eq_base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+        eq_base += __builtin_popcountll(eqm);
+        const bool sel = valid && (key[c] > thr || (eq && eq_rank < take_eq));
+        const uint64_t sm = __builtin_amdgcn_ballot_w64(sel);
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+        base += __builtin_popcountll(sm);
+        if (sel && pos < k) out[pos] = j;
+        if (mrow && valid) mrow[j] = sel;
+    }
+    if (lane == 0) {
+        row_ptr[row] = (int32_t)(row * k);
+        if (row == rows - 1) row_ptr[rows] = (int32_t)(rows * k);
+    }
+}
+
 // ------------------------------------------------------------------ STA
 struct StaArgs {
     int16_t win[BSTA_MAX_STA_HEADS][3];
@@ -308,9 +375,21 @@ hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* 
 hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32_t* row_ptr,
                        int32_t* col_idx, hipStream_t stream) {
     const int64_t rows = (int64_t)g.B * g.H * g.Nt;
-    const size_t lds = (size_t)g.Nt * 5 + 16;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), lds, stream, g.Nt, k, rows,
-                       s, mask, row_ptr, col_idx);
+    const int chunks = (g.Nt + 63) / 64;
+    const unsigned wave_blocks = (unsigned)((rows + 3) / 4);
+#define BSTA_TOPK_WAVE(CC)                                                                     \
+    hipLaunchKernelGGL(topk_wave_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream, g.Nt, k, \
+                       rows, s, mask, row_ptr, col_idx)
+    if (chunks <= 8) BSTA_TOPK_WAVE(8);
+    else if (chunks <= 16) BSTA_TOPK_WAVE(16);
+    else if (chunks <= 24) BSTA_TOPK_WAVE(24);
+    else if (chunks <= 32) BSTA_TOPK_WAVE(32);
+    else {
+        const size_t lds = (size_t)g.Nt * 5 + 16;
+        hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), lds, stream, g.Nt, k,
+                           rows, s, mask, row_ptr, col_idx);
+    }
+#undef BSTA_TOPK_WAVE
     return hipGetLastError();
 }
 

@@ -135,6 +135,72 @@ def test_topk_zero_query_tie_break(bsta):
     assert np.all(m[..., :4] == 1) and np.all(m[..., 4:] == 0)
 
 
+# Rows of Nt tiles from a 4 x 4 x 4Nt grid (tile j covers x in [4j, 4j+4)):
+# one width in each register bucket of the wave-per-row top-k kernel (at most
+# 8, 16, 24 and 32 scores per lane) and one past them (the LDS kernel).
+WIDE_NT = [300, 700, 1200, 1900, 2100]
+
+
+def _select_wide(m, w, q_bits, k_bits):
+    g = _geom(m, w)
+    qt, kt = m.attn_tile(g, H.to_dev(q_bits)), m.attn_tile(g, H.to_dev(k_bits))
+    sel = m.attn_select_blocks(g, qt, kt, m.SELECT_TOPK, w.topk)
+    return sel.block_mask.cpu().numpy(), sel.row_ptr.cpu().numpy(), sel.col_idx.cpu().numpy()
+
+
+def _oracle_scores(w, q_bits, k_bits):
+    qt = workloads.bf16_to_f32(tiling.tile(q_bits, w.T, w.Y, w.X))
+    kt = workloads.bf16_to_f32(tiling.tile(k_bits, w.T, w.Y, w.X))
+    return select.scores(select.pool(qt, w.T, w.Y, w.X), select.pool(kt, w.T, w.Y, w.X))
+
+
+@pytest.mark.parametrize("nt", WIDE_NT)
+def test_topk_wide_rows(bsta, nt):
+    """Random inputs: every row accepted against the oracle, CSR = GPU mask rows."""
+    w = workloads.custom(f"wide_{nt}", 1, 2, 64, 4, 4, 4 * nt, "topk", nt // 10, seed=31)
+    inp = H.inputs(w)
+    H.log(f"top-k wide rows Nt={nt} k={w.topk}")
+    gmask, rp_g, ci_g = _select_wide(bsta, w, inp["q"], inp["k"])
+    s = _oracle_scores(w, inp["q"], inp["k"])
+    exact, band = H.accept_topk_rows(gmask, s, w.topk)
+    H.log(f"  rows exact {exact}, inside tie band {band}")
+    rp, ci = select.mask_to_csr(gmask.astype(bool))
+    assert np.array_equal(rp_g, rp)
+    assert np.array_equal(ci_g[:len(ci)], ci)
+
+
+@pytest.mark.parametrize("nt", WIDE_NT)
+def test_topk_wide_rows_planted_ties(bsta, nt):
+    """Every token of key tile j is c_j * u, c_j in 1..5 (bf16-exact, so the
+    pooled key is exactly c_j * u): scores of tiles with equal c_j are equal
+    bit for bit on both sides, and wherever the row's sign of q.u is clear
+    the kept set must be the oracle's exactly (ties to the lower index)."""
+    w = workloads.custom(f"wide_ties_{nt}", 1, 1, 64, 4, 4, 4 * nt, "topk", nt // 7 + 1, seed=41)
+    H.log(f"top-k planted ties Nt={nt} k={w.topk}")
+    rng = np.random.default_rng(41)
+    u = rng.integers(-8, 9, size=w.D).astype(np.float32) / 8.0
+    c = ((np.arange(nt) * 7) % 5 + 1).astype(np.float32)
+    x = np.arange(w.L) % w.X                 # raster token -> x; tile = x // 4
+    kf = (c[x // 4][:, None] * u[None, :]).reshape(1, w.L, 1, w.D)
+    k_bits = workloads.bf16_bits(kf)
+    assert np.array_equal(workloads.bf16_to_f32(k_bits), kf)
+    q_bits = workloads.bf16_bits(rng.standard_normal((1, w.L, 1, w.D)).astype(np.float32))
+    gmask, rp_g, ci_g = _select_wide(bsta, w, q_bits, k_bits)
+    s = _oracle_scores(w, q_bits, k_bits)
+    want = select.topk_mask(s, w.topk)
+    # Row i's scores are c_j * (Pq_i . u): rank-clear rows have |Pq_i . u|
+    # well above the fp32 rounding of a 64-term dot product.
+    qt = workloads.bf16_to_f32(tiling.tile(q_bits, w.T, w.Y, w.X))
+    dot = select.pool(qt, w.T, w.Y, w.X)[0, 0] @ u.astype(np.float64)
+    clear = np.abs(dot) > 1e-3
+    assert clear.sum() > 0.9 * nt
+    assert np.array_equal(gmask[0, 0][clear], want[0, 0][clear])
+    H.accept_topk_rows(gmask, s, w.topk)
+    rp, ci = select.mask_to_csr(gmask.astype(bool))
+    assert np.array_equal(rp_g, rp)
+    assert np.array_equal(ci_g[:len(ci)], ci)
+
+
 # ---------------------------------------------------------------- windows
 
 @pytest.mark.parametrize("name", sorted(STA_SMALL))
