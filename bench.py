@@ -37,11 +37,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "eaf9040c82eb621c",
-    "fetch_kib": 55130003, "write_kib": 831504,
-    "traffic_bytes": 113757706240,
-    "l2_hit": 0.417, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.421, "clock_ghz": 1.680,
+    "src_sha256_16": "2fdb66287f463f56",
+    "fetch_kib": 55145226, "write_kib": 795142,
+    "traffic_bytes": 113751648256,
+    "l2_hit": 0.418, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.436, "clock_ghz": 1.583,
 }
 
 

@@ -157,7 +157,9 @@ __device__ inline void wait_dma(int newer) {
 }
 
 // Per-XCD sweep counters (one 128-byte line each): key tiles processed on
-// that XCD, bumped in steps of four.  Only the key order within rows
+// that XCD, bumped by 16 every 16 steps and by the rest of a row at its
+// end (few atomics on one line: loads of a line that takes many atomic
+// adds queue behind them).  Only the key order within rows
 // depends on them (see the kernel), so calls that overlap on one device, or
 // a counter that wraps, change speed, never results' validity.
 __device__ unsigned int g_sweep[8 * 32];
@@ -585,8 +587,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 else BSTA_ACQUIRE(sl);
                 // Advance the XCD's sweep clock (no return value: nothing
                 // waits for it).
-                if (rotate && (t & 3) == 3 && tid == 0)
-                    __hip_atomic_fetch_add(sweep, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (rotate && (t & 15) == 15 && tid == 0)
+                    __hip_atomic_fetch_add(sweep, 16u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const uint32_t sbv[2] = {(uint32_t)sl * SLOT_BYTES, (uint32_t)next_slot_of(sl) * SLOT_BYTES};
                 auto load_v = [&](int gidx, bf16x8 (&av)[NDB]) {
                     const uint32_t sb = sbv[gidx >> 1] + (gidx & 1) * 32 * D;
@@ -619,6 +621,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #undef BSTA_ACQUIRE
 #undef BSTA_ACQUIRE_STEADY
 #undef BSTA_ISSUE_NEXT
+        if (rotate && (n & 15) != 0 && tid == 0)
+            __hip_atomic_fetch_add(sweep, (unsigned)(n & 15), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         // Retire the last slots before the next item refills the ring.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
