@@ -10,8 +10,9 @@
 // "video_sparse_attn_h3" page.
 //
 // Precision: pooled vectors are fp32 sums of the valid bf16 rows in row
-// order, divided by the valid count; scores are fp32 dot products summed in
-// d order.  Selection is exact on those scores: radix select on
+// order, divided by the valid count; scores are fp32 dot products
+// accumulated in fp32 by the matrix cores.  Selection is exact on those
+// scores: a threshold search on
 // order-preserving 32-bit keys, equal keys resolved toward the lower index.
 #include "bsta_common.hpp"
 
@@ -67,57 +68,60 @@ __global__ __launch_bounds__(1024) void pool_kernel(
 }
 
 // ------------------------------------------------------------------ scores
-// S[bh] = Pq[bh] Pk[bh]^T, fp32, [Nt, Nt] per (batch, head).  64x64 output
-// tile per workgroup, 4x4 per thread, D staged through LDS in chunks of 32.
+// S[bh] = Pq[bh] Pk[bh]^T, fp32, [Nt, Nt] per (batch, head), on the fp32
+// matrix cores (v_mfma_f32_32x32x2_f32): a workgroup of four waves covers a
+// 64x64 output tile, each wave a 32x32 block.  Per 8 values of d, lane l
+// (row or column l%32, half h = l/32) holds the 4 values d0 + 4h + [0, 4)
+// of its row; k-step s then contracts d0 + s (lanes 0..31) with d0 + 4 + s
+// (lanes 32..63).  A and B use the same assignment, so the 4 steps cover
+// the 8 values exactly once.  Each lane loads all of its D/8 pieces of both
+// rows up front, so their latencies overlap.  Rows or columns past Nt read
+// row Nt-1 and their outputs are not stored.
+//
+// Tiles are dealt to XCDs in contiguous runs (workgroup x runs on XCD x%8),
+// so each XCD's L2 holds the pooled vectors of its own heads only.
 constexpr int kScoreTile = 64;
-constexpr int kScoreKc = 32;
 
+template <int D>
 __global__ __launch_bounds__(256) void score_kernel(
-        int Nt, int D, const float* __restrict__ pq, const float* __restrict__ pk,
+        int Nt, int64_t tiles, const float* __restrict__ pq, const float* __restrict__ pk,
         float* __restrict__ s) {
-    __shared__ float As[kScoreKc][kScoreTile + 4];
-    __shared__ float Bs[kScoreKc][kScoreTile + 4];
-    // 1-D grid: blockIdx.x = (bh * nb + bi) * nb + bj.
+    const int64_t per_xcd = (tiles + 7) / 8;
+    const int64_t w = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (w >= tiles) return;  // workgroup-uniform
+    // w = (bh * nb + bi) * nb + bj.
     const int nb = (Nt + kScoreTile - 1) / kScoreTile;
-    const int bj = blockIdx.x % nb;
-    const int rest = blockIdx.x / nb;
-    const int bi = rest % nb;
-    const int bh = rest / nb;
-    const int i0 = bi * kScoreTile;
-    const int j0 = bj * kScoreTile;
-    const float* A = pq + (int64_t)bh * Nt * D;
-    const float* Bm = pk + (int64_t)bh * Nt * D;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    float acc[4][4] = {};
-    for (int d0 = 0; d0 < D; d0 += kScoreKc) {
-        // 64 rows x 32 d of each operand: 2048 floats, 8 per thread.
-        for (int e = threadIdx.x; e < kScoreTile * kScoreKc; e += 256) {
-            int row = e / kScoreKc, dd = e - row * kScoreKc;
-            int ia = i0 + row, jb = j0 + row;
-            As[dd][row] = ia < Nt ? A[(int64_t)ia * D + d0 + dd] : 0.f;
-            Bs[dd][row] = jb < Nt ? Bm[(int64_t)jb * D + d0 + dd] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < kScoreKc; ++dd) {
-            f32x4 a = *(const f32x4*)&As[dd][ty * 4];
-            f32x4 bv = *(const f32x4*)&Bs[dd][tx * 4];
+    const int bj = (int)(w % nb);
+    const int64_t rest = w / nb;
+    const int bi = (int)(rest % nb);
+    const int64_t bh = rest / nb;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 31, h = lane >> 5;
+    const int i0 = bi * kScoreTile + (wave >> 1) * 32;
+    const int j0 = bj * kScoreTile + (wave & 1) * 32;
+    const int ia = i0 + r < Nt ? i0 + r : Nt - 1;
+    const int jb = j0 + r < Nt ? j0 + r : Nt - 1;
+    const float* arow = pq + (bh * Nt + ia) * D + 4 * h;
+    const float* brow = pk + (bh * Nt + jb) * D + 4 * h;
+    f32x4 a[D / 8], b[D / 8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) acc[u][w] = __builtin_fmaf(a[u], bv[w], acc[u][w]);
-        }
-        __syncthreads();
+    for (int c = 0; c < D / 8; ++c) {
+        a[c] = *(const f32x4*)(arow + 8 * c);
+        b[c] = *(const f32x4*)(brow + 8 * c);
     }
-    float* out = s + (int64_t)bh * Nt * Nt;
+    f32x16 acc = {};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        int i = i0 + ty * 4 + u;
-        if (i >= Nt) continue;
+    for (int c = 0; c < D / 8; ++c)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            int j = j0 + tx * 4 + w;
-            if (j < Nt) out[(int64_t)i * Nt + j] = acc[u][w];
+        for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][k], b[c][k], acc, 0, 0, 0);
+    // Register q of lane l holds row 8(q/4) + 4h + q%4, column l%32.
+    float* out = s + bh * Nt * Nt;
+    const int j = j0 + r;
+    if (j < Nt) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = i0 + 8 * (q >> 2) + 4 * h + (q & 3);
+            if (i < Nt) out[(int64_t)i * Nt + j] = acc[q];
         }
     }
 }
@@ -365,10 +369,15 @@ hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, fl
 
 hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,
                          hipStream_t stream) {
-    const int nb = (g.Nt + kScoreTile - 1) / kScoreTile;
-    const int64_t blocks = (int64_t)nb * nb * g.B * g.H;
-    hipLaunchKernelGGL(score_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g.Nt, g.D,
-                       pq, pk, s);
+    const int64_t nb = (g.Nt + kScoreTile - 1) / kScoreTile;
+    const int64_t tiles = nb * nb * g.B * g.H;
+    const unsigned blocks = (unsigned)(8 * ((tiles + 7) / 8));
+    if (g.D == 128)
+        hipLaunchKernelGGL(score_kernel<128>, dim3(blocks), dim3(256), 0, stream, g.Nt, tiles, pq,
+                           pk, s);
+    else
+        hipLaunchKernelGGL(score_kernel<64>, dim3(blocks), dim3(256), 0, stream, g.Nt, tiles, pq,
+                           pk, s);
     return hipGetLastError();
 }
 
