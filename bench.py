@@ -38,10 +38,10 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
     "src_sha256_16": "2fdb66287f463f56",
-    "fetch_kib": 55145226, "write_kib": 795142,
-    "traffic_bytes": 113751648256,
-    "l2_hit": 0.418, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.436, "clock_ghz": 1.583,
+    "fetch_kib": 54103872, "write_kib": 796123,
+    "traffic_bytes": 111619959808,
+    "l2_hit": 0.430, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.433, "clock_ghz": 1.649,
 }
 
 
@@ -152,20 +152,29 @@ def main():
     qt, kt, vt, ot = (torch.empty((w.B, lpad, w.H, w.D), dtype=torch.bfloat16, device=dev)
                       for _ in range(4))
     o = torch.empty_like(q)
-    sel = bsta.attn_select_blocks(g, None if mode == bsta.SELECT_STA else qt,
-                                  None if mode == bsta.SELECT_STA else kt, mode, w.topk, win,
-                                  want_mask=False)
+    sel = bsta.attn_select_alloc(g, mode, w.topk, win, want_mask=False, device=dev)
+    # Top-k: Q and K are pooled in the tiling pass (attn_tile_pool writes the
+    # pooled vectors into the selection's workspace) and the selection skips
+    # its own pooling pass.
+    fused = mode == bsta.SELECT_TOPK
+    pq, pk = sel.pooled(g) if fused else (None, None)
+    sel_mode = (bsta.SELECT_TOPK | bsta.SELECT_PREPOOLED) if fused else mode
     names = ["tile_qkv", "select", "attn_fwd", "untile"]
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        bsta.attn_tile(g, q, out=qt)
-        bsta.attn_tile(g, k, out=kt)
+        if fused:
+            bsta.attn_tile_pool(g, q, pq, out=qt)
+            bsta.attn_tile_pool(g, k, pk, out=kt)
+        else:
+            bsta.attn_tile(g, q, out=qt)
+            bsta.attn_tile(g, k, out=kt)
         bsta.attn_tile(g, v, out=vt)
         if ev:
             ev[1].record()
-        bsta.attn_select_blocks(g, qt, kt, mode, w.topk, win, out=sel)
+        bsta.attn_select_blocks(g, None if fused else qt, None if fused else kt, sel_mode, w.topk,
+                                win, out=sel)
         if ev:
             ev[2].record()
         bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
@@ -202,6 +211,22 @@ def main():
     ms = {n: float(np.median(per[n])) for n in names}
     print(f"[bench] per-call median ms {ms}", file=sys.stderr, flush=True)
 
+    # The unfused selection (its own pooling pass over the tiled Q and K), for
+    # the pooling kernel's standalone rate; not part of the step.
+    unfused_ms = None
+    if fused:
+        sel_u = bsta.attn_select_alloc(g, mode, w.topk, want_mask=False, device=dev)
+        per_u = []
+        for _ in range(n_calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsta.attn_select_blocks(g, qt, kt, mode, w.topk, out=sel_u)
+            e1.record()
+            torch.cuda.synchronize()
+            per_u.append(e0.elapsed_time(e1))
+        unfused_ms = float(np.median(per_u))
+        del sel_u
+
     # Cold-L2 row for the attention call: a 512 MB write before each call
     # evicts the key/value tiles a previous call left in the caches.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -223,7 +248,8 @@ def main():
     dense_flop = 4.0 * w.D * w.B * w.H * float(w.L) ** 2
     attn_tflops = flop / (ms["attn_fwd"] * 1e-3) / 1e12
     elem = w.B * w.H * w.D * 2
-    tile_bytes = 3 * elem * (w.L + lpad)
+    pooled_bytes = 2 * w.B * w.H * nt * w.D * 4 if fused else 0
+    tile_bytes = 3 * elem * (w.L + lpad) + pooled_bytes
     untile_bytes = elem * (w.L + lpad)
     pool_bytes = 2 * elem * w.L + 2 * w.B * w.H * nt * w.D * 4
     out = {
@@ -270,8 +296,14 @@ def main():
                                  "frac_mfma_peak": flop / (cold_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                  "note": "512 MB write before each call"},
             "tile_qkv": {"ms": ms["tile_qkv"], "gbps": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9,
-                         "frac_hbm_peak": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9 / PEAK_HBM_GBPS},
-            "select": {"ms": ms["select"], "pool_bytes": pool_bytes},
+                         "frac_hbm_peak": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "note": ("attn_tile_pool for Q and K (pooling fused), attn_tile for V"
+                                  if fused else "attn_tile for Q, K and V")},
+            "select": {"ms": ms["select"],
+                       "note": "scores + top-k (prepooled)" if fused else "window CSR"},
+            "select_unfused": ({"ms": unfused_ms, "pool_bytes": pool_bytes,
+                                "note": "pool + scores + top-k from the tiled Q and K; not in the step"}
+                               if fused else None),
             "untile": {"ms": ms["untile"], "gbps": untile_bytes / (ms["untile"] * 1e-3) / 1e9},
         },
     }

@@ -3,6 +3,7 @@
 Python face of libbsta.so.  The four calls of the path keep the C names:
 
     attn_tile(g, x)                      raster [B,L,H,D] -> tiles [B,Lpad,H,D]
+    attn_tile_pool(g, x, pooled=...)     the same, also writing the per-tile means
     attn_select_blocks(g, qt, kt, ...)   pooled scores -> top-k / window -> CSR
     attn_block_sparse_fwd(g, qt, kt, vt, row_ptr, col_idx)
     attn_untile(g, yt)                   tiles -> raster
@@ -20,10 +21,11 @@ import math
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import SELECT_STA, SELECT_TOPK, BstaError
+from ._lib import SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, BstaError
 
 __all__ = [
-    "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "attn_tile", "attn_untile",
+    "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_PREPOOLED", "attn_tile",
+    "attn_tile_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
     "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
 ]
@@ -120,6 +122,21 @@ def attn_tile(g: Geometry, x, out=None):
     return out
 
 
+def attn_tile_pool(g: Geometry, x, pooled, out=None):
+    """attn_tile plus the per-tile means of the valid rows (fp32 [B, H, Nt, D])
+    written to ``pooled`` in the same pass; returns the tiled tensor."""
+    torch = _torch()
+    _expect(x, (g.B, g.L, g.H, g.D), torch.bfloat16, "x")
+    nt, lpad = attn_geometry(g)
+    if out is None:
+        out = torch.empty((g.B, lpad, g.H, g.D), dtype=torch.bfloat16, device=x.device)
+    _expect(out, (g.B, lpad, g.H, g.D), torch.bfloat16, "x_tiled")
+    _expect(pooled, (g.B, g.H, nt, g.D), torch.float32, "pooled")
+    _lib.check(_lib.load().attn_tile_pool(ctypes.byref(g.c), _ptr(x), _ptr(out), _ptr(pooled),
+                                          _stream()))
+    return out
+
+
 def attn_untile(g: Geometry, y_tiled, out=None):
     torch = _torch()
     lpad = attn_geometry(g)[1]
@@ -151,24 +168,39 @@ class Selection:
         return self.workspace[2 * n:2 * n + g.B * g.H * nt * nt].view(g.B, g.H, nt, nt)
 
 
+def attn_select_alloc(g: Geometry, mode: int = SELECT_TOPK, topk: int = 0, windows=None,
+                      want_mask: bool = True, device="cuda") -> Selection:
+    """Output buffers and workspace for attn_select_blocks.  With the top-k
+    mode, ``Selection.pooled(g)`` views are where attn_tile_pool writes."""
+    torch = _torch()
+    nt = attn_geometry(g)[0]
+    cap = attn_select_capacity(g, mode, topk, windows)
+    wsb = attn_workspace_bytes(g, mode)
+    return Selection(
+        row_ptr=torch.empty(g.B * g.H * nt + 1, dtype=torch.int32, device=device),
+        col_idx=torch.empty(max(cap, 1), dtype=torch.int32, device=device),
+        block_mask=(torch.empty((g.B, g.H, nt, nt), dtype=torch.uint8, device=device)
+                    if want_mask else None),
+        workspace=(torch.empty(wsb // 4, dtype=torch.float32, device=device) if wsb > 0 else None))
+
+
 def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, topk: int = 0,
                        windows: Optional[Sequence[Sequence[int]]] = None, want_mask: bool = True,
                        out: Optional[Selection] = None) -> Selection:
+    """Coarse stage.  ``mode`` may be SELECT_TOPK | SELECT_PREPOOLED when
+    ``out`` (from attn_select_alloc) already holds the pooled Q and K written
+    by attn_tile_pool; q_tiled and k_tiled are then not read (may be None)."""
     torch = _torch()
     nt, lpad = attn_geometry(g)
-    dev = (q_tiled if q_tiled is not None else torch.empty(0, device="cuda")).device
+    prepooled = bool(mode & SELECT_PREPOOLED)
     if mode == SELECT_TOPK:
         _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
         _expect(k_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "k_tiled")
-    cap = attn_select_capacity(g, mode, topk, windows)
-    wsb = attn_workspace_bytes(g, mode)
+    if prepooled and (out is None or out.workspace is None):
+        raise ValueError("SELECT_PREPOOLED needs `out` holding the pooled Q and K")
     if out is None:
-        out = Selection(
-            row_ptr=torch.empty(g.B * g.H * nt + 1, dtype=torch.int32, device=dev),
-            col_idx=torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-            block_mask=(torch.empty((g.B, g.H, nt, nt), dtype=torch.uint8, device=dev)
-                        if want_mask else None),
-            workspace=(torch.empty(wsb // 4, dtype=torch.float32, device=dev) if wsb > 0 else None))
+        dev = (q_tiled if q_tiled is not None else torch.empty(0, device="cuda")).device
+        out = attn_select_alloc(g, mode, topk, windows, want_mask, dev)
     _keep, w = _windows_arg(windows)
     ws = out.workspace
     status = _lib.load().attn_select_blocks(
@@ -213,8 +245,16 @@ def attn_set_deterministic(enable: bool) -> bool:
 
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
                            windows=None):
-    """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile."""
-    qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
-    sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
+    """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile.
+    In top-k mode Q and K are pooled while they are tiled."""
+    if mode == SELECT_TOPK:
+        sel = attn_select_alloc(g, mode, topk, want_mask=False, device=q.device)
+        pq, pk = sel.pooled(g)
+        qt, kt = attn_tile_pool(g, q, pq), attn_tile_pool(g, k, pk)
+        vt = attn_tile(g, v)
+        sel = attn_select_blocks(g, None, None, SELECT_TOPK | SELECT_PREPOOLED, topk, out=sel)
+    else:
+        qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
+        sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
     ot = attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx)
     return attn_untile(g, ot)

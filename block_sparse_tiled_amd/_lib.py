@@ -22,10 +22,11 @@ BSTA_ERR_CAPACITY = -4
 BSTA_ERR_HIP = -5
 SELECT_TOPK = 0
 SELECT_STA = 1
+SELECT_PREPOOLED = 0x100
 MAX_STA_HEADS = 256
 
 EXPORTS = (
-    "attn_geometry", "attn_tile", "attn_untile", "attn_select_capacity",
+    "attn_geometry", "attn_tile", "attn_tile_pool", "attn_untile", "attn_select_capacity",
     "attn_workspace_bytes", "attn_select_blocks", "attn_block_sparse_fwd",
     "attn_status_string", "attn_last_error", "attn_set_deterministic",
 )
@@ -61,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "attn_geometry": (i32, [G, ctypes.POINTER(i32), ctypes.POINTER(i64), P]),
         "attn_tile": (i32, [G, P, P, P]),
+        "attn_tile_pool": (i32, [G, P, P, P, P]),
         "attn_untile": (i32, [G, P, P, P]),
         "attn_select_capacity": (i64, [G, i32, i32, P]),
         "attn_workspace_bytes": (i64, [G, i32]),

@@ -19,6 +19,8 @@
 namespace bsta {
 hipError_t launch_permute(const Geo& g, const void* src, void* dst, bool to_tiles,
                           hipStream_t stream);
+hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, float* pooled,
+                            hipStream_t stream);
 hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
                        hipStream_t stream);
 hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,
@@ -123,8 +125,19 @@ int32_t check_windows(const Geo& g, const int32_t* w, int64_t* per_batch) {
 }
 
 // CSR entry count of a selection, or a negative status.
-int64_t capacity_of(const Geo& g, int32_t mode, int32_t topk, const int32_t* windows) {
+// The selection kind without the BSTA_SELECT_PREPOOLED flag, or -1 when the
+// flag is set on anything but top-k.
+int32_t base_mode(int32_t mode) {
+    if (mode & BSTA_SELECT_PREPOOLED) {
+        const int32_t m = mode & ~BSTA_SELECT_PREPOOLED;
+        return m == BSTA_SELECT_TOPK ? m : -1;
+    }
+    return mode;
+}
+
+int64_t capacity_of(const Geo& g, int32_t mode_in, int32_t topk, const int32_t* windows) {
     int64_t nnz;
+    const int32_t mode = base_mode(mode_in);
     if (mode == BSTA_SELECT_TOPK) {
         if (topk < 1 || topk > g.Nt)
             return fail(BSTA_ERR_SHAPE, "topk=%d outside [1, Nt=%d]", topk, g.Nt);
@@ -135,16 +148,18 @@ int64_t capacity_of(const Geo& g, int32_t mode, int32_t topk, const int32_t* win
         if (st != BSTA_OK) return st;
         nnz = (int64_t)g.B * g.Nt * per_batch;
     } else {
-        return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode);
+        return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode_in);
     }
     if (nnz > 0x7fffffffLL)
         return fail(BSTA_ERR_SHAPE, "%lld CSR entries overflow int32 row_ptr", (long long)nnz);
     return nnz;
 }
 
-int64_t workspace_of(const Geo& g, int32_t mode) {
+int64_t workspace_of(const Geo& g, int32_t mode_in) {
+    const int32_t mode = base_mode(mode_in);
     if (mode == BSTA_SELECT_STA) return 0;
-    if (mode != BSTA_SELECT_TOPK) return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode);
+    if (mode != BSTA_SELECT_TOPK)
+        return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode_in);
     const int64_t pooled = (int64_t)2 * g.B * g.H * g.Nt * g.D;
     const int64_t scores = (int64_t)g.B * g.H * g.Nt * g.Nt;
     return (pooled + scores) * (int64_t)sizeof(float);
@@ -207,6 +222,17 @@ int32_t attn_tile(const bsta_geom* gin, const void* x, void* x_tiled, void* stre
     return hip_status(bsta::launch_permute(g, x, x_tiled, true, (hipStream_t)stream), "attn_tile");
 }
 
+int32_t attn_tile_pool(const bsta_geom* gin, const void* x, void* x_tiled, float* pooled,
+                       void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (x == nullptr || x_tiled == nullptr || pooled == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_tile_pool: NULL tensor");
+    return hip_status(bsta::launch_tile_pool(g, x, x_tiled, pooled, (hipStream_t)stream),
+                      "attn_tile_pool");
+}
+
 int32_t attn_untile(const bsta_geom* gin, const void* y_tiled, void* y, void* stream) {
     Geo g;
     int32_t st = make_geo(gin, &g);
@@ -232,10 +258,12 @@ int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void
         return fail(BSTA_ERR_CAPACITY, "col_capacity %lld < %lld entries needed",
                     (long long)col_capacity, (long long)need);
     hipStream_t s = (hipStream_t)stream;
+    const bool prepooled = (mode & BSTA_SELECT_PREPOOLED) != 0;
+    mode = base_mode(mode);
     if (mode == BSTA_SELECT_STA)
         return hip_status(bsta::launch_sta(g, sta_windows_host, block_mask, row_ptr, col_idx, s),
                           "attn_select_blocks(window)");
-    if (q_tiled == nullptr || k_tiled == nullptr)
+    if (!prepooled && (q_tiled == nullptr || k_tiled == nullptr))
         return fail(BSTA_ERR_NULL, "attn_select_blocks: NULL q_tiled or k_tiled in top-k mode");
     if (g.Nt > kMaxTopkTiles)
         return fail(BSTA_ERR_SHAPE, "top-k selection supports at most %d tiles, got %d",
@@ -248,7 +276,7 @@ int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void
     float* pq = (float*)workspace;
     float* pk = pq + (int64_t)g.B * g.H * g.Nt * g.D;
     float* sc = pk + (int64_t)g.B * g.H * g.Nt * g.D;
-    hipError_t e = bsta::launch_pool(g, q_tiled, k_tiled, pq, pk, s);
+    hipError_t e = prepooled ? hipSuccess : bsta::launch_pool(g, q_tiled, k_tiled, pq, pk, s);
     if (e == hipSuccess) e = bsta::launch_scores(g, pq, pk, sc, s);
     if (e == hipSuccess) e = bsta::launch_topk(g, topk, sc, block_mask, row_ptr, col_idx, s);
     return hip_status(e, "attn_select_blocks(top-k)");

@@ -10,6 +10,10 @@
  *   attn_block_sparse_fwd  softmax(q k^T / sqrt(D)) v over the selected tiles
  *   attn_untile          tile order -> raster order
  *
+ * On the top-k path attn_tile_pool may replace attn_tile for Q and K: it
+ * also writes the pooled vectors, and attn_select_blocks then runs with
+ * BSTA_SELECT_PREPOOLED and skips its own pooling pass.
+ *
  * Conventions shared by every call:
  *   - Tensors are bfloat16, contiguous, in the layout [B, L, H, D] that the
  *     FastVideo attention backends use ("bsa_attn" page, forward: query, key
@@ -57,6 +61,9 @@ enum {
 };
 
 enum { BSTA_SELECT_TOPK = 0, BSTA_SELECT_STA = 1 };
+/* Flag for BSTA_SELECT_TOPK: the workspace already holds pooled Q and K
+ * (written by attn_tile_pool); see attn_select_blocks. */
+enum { BSTA_SELECT_PREPOOLED = 0x100 };
 
 /* Largest head count a sliding-tile-window call accepts (windows travel as
  * kernel arguments). */
@@ -88,6 +95,23 @@ int32_t attn_geometry(const bsta_geom* g, int32_t* num_tiles, int64_t* padded_le
  * x and x_tiled must not overlap.
  */
 int32_t attn_tile(const bsta_geom* g, const void* x, void* x_tiled, void* stream);
+
+/*
+ * attn_tile_pool: attn_tile and, in the same pass over x, the per-tile mean
+ * pooling of the top-k coarse stage ("sla" page, get_block_map and
+ * mean_pool): pooled[b,h,j] is the fp32 mean of the n_j valid rows of tile
+ * j, summed in slot order, bit for bit the value attn_select_blocks computes
+ * from x_tiled.  Reading x once instead of reading x_tiled again saves one
+ * pass over Q and K on the top-k path.
+ *   x        [in]  bf16 [B, L, H, D]
+ *   x_tiled  [out] bf16 [B, Lpad, H, D], as from attn_tile
+ *   pooled   [out] fp32 [B, H, Nt, D]; for attn_select_blocks with
+ *            BSTA_SELECT_PREPOOLED, the first (Q) or second (K) slab of its
+ *            workspace
+ * x, x_tiled and pooled must not overlap.
+ */
+int32_t attn_tile_pool(const bsta_geom* g, const void* x, void* x_tiled, float* pooled,
+                       void* stream);
 
 /*
  * attn_untile: tile -> raster order ("bsa_attn" page, postprocess_output and
@@ -127,7 +151,11 @@ int64_t attn_workspace_bytes(const bsta_geom* g, int32_t mode);
  * of the CSR lists the kept key tiles of query tile i in ascending order.
  *   q_tiled, k_tiled  [in]  bf16 [B, Lpad, H, D] from attn_tile (pad rows 0);
  *                           unused (may be NULL) in window mode
- *   mode              BSTA_SELECT_TOPK or BSTA_SELECT_STA
+ *   mode              BSTA_SELECT_TOPK or BSTA_SELECT_STA; BSTA_SELECT_TOPK |
+ *                     BSTA_SELECT_PREPOOLED skips the pooling: the
+ *                     workspace already holds pooled Q then pooled K (from
+ *                     attn_tile_pool), and q_tiled, k_tiled are unused (may
+ *                     be NULL)
  *   topk              1 <= k <= Nt (top-k mode)
  *   sta_windows_host  [in, host int32 [H][3]] windows (window mode),
  *                     1 <= w <= tiles on that axis; H <= BSTA_MAX_STA_HEADS

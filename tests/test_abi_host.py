@@ -70,6 +70,15 @@ def test_capacity_and_workspace(lib):
     assert lib.attn_select_capacity(ctypes.byref(g), 1, 0, win) == 2 * nt * (9 + 27 + 75)
     assert lib.attn_workspace_bytes(ctypes.byref(g), 0) == 4 * (2 * 2 * 3 * nt * 128 + 2 * 3 * nt * nt)
     assert lib.attn_workspace_bytes(ctypes.byref(g), 1) == 0
+    # The prepooled flag changes neither the CSR size nor the workspace (it
+    # only says the workspace already holds pooled Q and K) ...
+    pre = _lib.SELECT_TOPK | _lib.SELECT_PREPOOLED
+    assert lib.attn_select_capacity(ctypes.byref(g), pre, 7, None) == 2 * 3 * nt * 7
+    assert lib.attn_workspace_bytes(ctypes.byref(g), pre) == lib.attn_workspace_bytes(ctypes.byref(g), 0)
+    # ... and applies to top-k only.
+    sta_pre = _lib.SELECT_STA | _lib.SELECT_PREPOOLED
+    assert lib.attn_select_capacity(ctypes.byref(g), sta_pre, 0, win) == _lib.BSTA_ERR_UNSUPPORTED
+    assert lib.attn_workspace_bytes(ctypes.byref(g), sta_pre) == _lib.BSTA_ERR_UNSUPPORTED
 
 
 def _err(lib):
@@ -91,6 +100,9 @@ def test_tile_errors(lib):
     assert lib.attn_tile(ctypes.byref(_g()), FAKE, None, None) == _lib.BSTA_ERR_NULL
     assert lib.attn_untile(ctypes.byref(_g()), None, FAKE, None) == _lib.BSTA_ERR_NULL
     assert lib.attn_tile(ctypes.byref(_g(D=32)), FAKE, FAKE, None) == _lib.BSTA_ERR_UNSUPPORTED
+    for x, xt, pooled in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        assert lib.attn_tile_pool(ctypes.byref(_g()), x, xt, pooled, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_tile_pool(ctypes.byref(_g(D=32)), FAKE, FAKE, FAKE, None) == _lib.BSTA_ERR_UNSUPPORTED
 
 
 def _select(lib, g, mode=0, topk=2, win=None, rp=FAKE, ci=FAKE, cap=10 ** 9, ws=FAKE, wsb=10 ** 12,
@@ -109,6 +121,10 @@ def test_select_errors(lib):
     assert _select(lib, g, ci=None) == _lib.BSTA_ERR_NULL
     assert _select(lib, g, q=None) == _lib.BSTA_ERR_NULL
     assert _select(lib, g, ws=None) == _lib.BSTA_ERR_NULL
+    pre = _lib.SELECT_TOPK | _lib.SELECT_PREPOOLED
+    assert _select(lib, g, mode=pre, ws=None, q=None, k=None) == _lib.BSTA_ERR_NULL
+    assert "workspace" in _err(lib)
+    assert _select(lib, g, mode=_lib.SELECT_STA | _lib.SELECT_PREPOOLED) == _lib.BSTA_ERR_UNSUPPORTED
     need = 1 * 2 * 8 * 2
     assert _select(lib, g, cap=need - 1) == _lib.BSTA_ERR_CAPACITY
     wsb = lib.attn_workspace_bytes(ctypes.byref(g), 0)

@@ -201,6 +201,59 @@ def test_topk_wide_rows_planted_ties(bsta, nt):
     assert np.array_equal(ci_g[:len(ci)], ci)
 
 
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_tile_pool_fused(bsta, name):
+    """attn_tile_pool: the tiled tensor bit for bit attn_tile's (stale rows of
+    a reused buffer overwritten), the pooled vectors bit for bit those the
+    select call computes itself, and a prepooled selection identical to the
+    unfused one."""
+    import torch
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"tile+pool {name}")
+    g = _geom(bsta, w)
+    q, k = H.to_dev(inp["q"]), H.to_dev(inp["k"])
+    qt, kt = bsta.attn_tile(g, q), bsta.attn_tile(g, k)
+    ref = bsta.attn_select_blocks(g, qt, kt, bsta.SELECT_TOPK, w.topk)
+    sel = bsta.attn_select_alloc(g, bsta.SELECT_TOPK, w.topk, device=q.device)
+    pq, pk = sel.pooled(g)
+    qt2 = bsta.attn_tile_pool(g, q, pq, out=torch.full_like(qt, 7.0))
+    kt2 = bsta.attn_tile_pool(g, k, pk, out=torch.full_like(kt, 7.0))
+    sel = bsta.attn_select_blocks(g, None, None, bsta.SELECT_TOPK | bsta.SELECT_PREPOOLED, w.topk,
+                                  out=sel)
+    torch.cuda.synchronize()
+    for a, b in ((qt2, qt), (kt2, kt)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rpq, rpk = ref.pooled(g)
+    for a, b in ((pq, rpq), (pk, rpk)):
+        assert torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+    assert torch.equal(sel.row_ptr, ref.row_ptr)
+    nnz = int(ref.row_ptr[-1])
+    assert torch.equal(sel.col_idx[:nnz], ref.col_idx[:nnz])
+    assert torch.equal(sel.block_mask, ref.block_mask)
+
+
+@pytest.mark.parametrize("name", ["smooth_40", "ragged_d64", "c1"])
+def test_block_sparse_attention_fused_route(bsta, name):
+    """The one-call path (Q and K pooled while tiled, prepooled selection)
+    equals the four separate calls bit for bit, with the key walk in CSR
+    order (deterministic mode); the separate calls are held to the oracle by
+    the tests above."""
+    import torch
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"fused route {name}")
+    g = _geom(bsta, w)
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        o = bsta.block_sparse_attention(g, *(H.to_dev(inp[n]) for n in ("q", "k", "v")),
+                                        mode=bsta.SELECT_TOPK, topk=w.topk)
+        r = _run_gpu(bsta, w, inp)
+    finally:
+        bsta.attn_set_deterministic(prev)
+    assert torch.equal(o.view(torch.int16), r["o"].view(torch.int16))
+
+
 # ---------------------------------------------------------------- windows
 
 @pytest.mark.parametrize("name", sorted(STA_SMALL))
