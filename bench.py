@@ -37,11 +37,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "2fdb66287f463f56",
-    "fetch_kib": 54103872, "write_kib": 796123,
-    "traffic_bytes": 111619959808,
-    "l2_hit": 0.430, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.433, "clock_ghz": 1.649,
+    "src_sha256_16": "9afa624e7fcfc32e",
+    "fetch_kib": 51143357, "write_kib": 793928,
+    "traffic_bytes": 105554577408,
+    "l2_hit": 0.461, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.443, "clock_ghz": 1.625,
 }
 
 
@@ -159,7 +159,9 @@ def main():
     fused = mode == bsta.SELECT_TOPK
     pq, pk = sel.pooled(g) if fused else (None, None)
     sel_mode = (bsta.SELECT_TOPK | bsta.SELECT_PREPOOLED) if fused else mode
-    names = ["tile_qkv", "select", "attn_fwd", "untile"]
+    # The attention call writes its output in raster order itself
+    # (attn_block_sparse_fwd_raster), so the step has no untile pass.
+    names = ["tile_qkv", "select", "attn_fwd"]
 
     def step(ev=None):
         if ev:
@@ -177,12 +179,9 @@ def main():
                                 win, out=sel)
         if ev:
             ev[2].record()
-        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
+        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
         if ev:
             ev[3].record()
-        bsta.attn_untile(g, ot, out=o)
-        if ev:
-            ev[4].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -203,7 +202,7 @@ def main():
     n_calls = max(args.steps, 20)
     per = {n: [] for n in names}
     for _ in range(n_calls):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         step(ev)
         torch.cuda.synchronize()
         for idx, n in enumerate(names):
@@ -227,6 +226,19 @@ def main():
         unfused_ms = float(np.median(per_u))
         del sel_u
 
+    # The standalone untile pass (not in the step: the attention writes raster
+    # order itself), for its HBM rate.
+    bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
+    per_ut = []
+    for _ in range(n_calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bsta.attn_untile(g, ot, out=o)
+        e1.record()
+        torch.cuda.synchronize()
+        per_ut.append(e0.elapsed_time(e1))
+    untile_ms = float(np.median(per_ut))
+
     # Cold-L2 row for the attention call: a 512 MB write before each call
     # evicts the key/value tiles a previous call left in the caches.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -235,7 +247,7 @@ def main():
         flush.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
+        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
         e1.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
@@ -291,7 +303,8 @@ def main():
             "attn_fwd": {"ms": ms["attn_fwd"], "tflops": attn_tflops,
                          "dense_equiv_tflops": dense_flop / (ms["attn_fwd"] * 1e-3) / 1e12,
                          "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
-                         "calls": n_calls, "stat": "median"},
+                         "calls": n_calls, "stat": "median",
+                         "note": "attn_block_sparse_fwd_raster (output in raster order)"},
             "attn_fwd_cold_l2": {"ms": cold_ms, "tflops": flop / (cold_ms * 1e-3) / 1e12,
                                  "frac_mfma_peak": flop / (cold_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                  "note": "512 MB write before each call"},
@@ -304,7 +317,8 @@ def main():
             "select_unfused": ({"ms": unfused_ms, "pool_bytes": pool_bytes,
                                 "note": "pool + scores + top-k from the tiled Q and K; not in the step"}
                                if fused else None),
-            "untile": {"ms": ms["untile"], "gbps": untile_bytes / (ms["untile"] * 1e-3) / 1e9},
+            "untile": {"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
+                       "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
         },
     }
     if not args.no_cpu_baseline:

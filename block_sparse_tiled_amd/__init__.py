@@ -213,7 +213,10 @@ def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, t
 
 def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                           softmax_scale: Optional[float] = None, causal: bool = False,
-                          out=None, lse=None, want_lse: bool = False):
+                          out=None, lse=None, want_lse: bool = False, raster: bool = False):
+    """Block-sparse attention over the tiled tensors.  The output is tiled
+    [B, Lpad, H, D], or with ``raster=True`` written straight to raster order
+    [B, L, H, D] (attn_block_sparse_fwd_raster: no separate untile pass)."""
     torch = _torch()
     nt, lpad = attn_geometry(g)
     for name, t in (("q_tiled", q_tiled), ("k_tiled", k_tiled), ("v_tiled", v_tiled)):
@@ -223,13 +226,16 @@ def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_i
         raise ValueError("col_idx: expected contiguous int32")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(g.D)
+    rows = g.L if raster else lpad
     if out is None:
-        out = torch.empty_like(q_tiled)
-    _expect(out, (g.B, lpad, g.H, g.D), torch.bfloat16, "o_tiled")
+        out = torch.empty((g.B, rows, g.H, g.D), dtype=torch.bfloat16, device=q_tiled.device)
+    _expect(out, (g.B, rows, g.H, g.D), torch.bfloat16, "o" if raster else "o_tiled")
     if lse is None and want_lse:
         lse = torch.empty((g.B, g.H, lpad), dtype=torch.float32, device=q_tiled.device)
     _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
-    _lib.check(_lib.load().attn_block_sparse_fwd(
+    lib = _lib.load()
+    fn = lib.attn_block_sparse_fwd_raster if raster else lib.attn_block_sparse_fwd
+    _lib.check(fn(
         ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(row_ptr),
         _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(out),
         _ptr(lse), _stream()))
@@ -246,7 +252,8 @@ def attn_set_deterministic(enable: bool) -> bool:
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
                            windows=None):
     """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile.
-    In top-k mode Q and K are pooled while they are tiled."""
+    In top-k mode Q and K are pooled while they are tiled; the attention
+    writes its output in raster order directly."""
     if mode == SELECT_TOPK:
         sel = attn_select_alloc(g, mode, topk, want_mask=False, device=q.device)
         pq, pk = sel.pooled(g)
@@ -256,5 +263,4 @@ def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: 
     else:
         qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
         sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
-    ot = attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx)
-    return attn_untile(g, ot)
+    return attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)

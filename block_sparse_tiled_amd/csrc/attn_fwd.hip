@@ -183,7 +183,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
         const int32_t* __restrict__ col_idx, int64_t col_len, float scale_log2,
-        __bf16* __restrict__ o, float* __restrict__ lse, int64_t items_per_xcd, int rotate) {
+        __bf16* __restrict__ o, float* __restrict__ lse, int64_t items_per_xcd, int rotate,
+        int raster) {
     constexpr int NDC = D / 16;                    // MFMA k-steps for S (16 d each)
     constexpr int NDB = D / 32;                    // 32-row d blocks of O^T
     constexpr int HALF_ELEMS = 32 * D;             // one half-tile slot
@@ -632,17 +633,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float l_tot = l_run + wave_xor32(l_run);
         const bool valid = qi < ni && l_tot > 0.f;
         const float inv = valid ? 1.0f / l_tot : 0.f;
-        __bf16* orow = o + (batch_row0 + (int64_t)i * 64 + qi) * rs + head_off;
+        // Output row: slot i*64 + qi of the tiled tensor, or with `raster`
+        // the token that slot holds in [B, L, H, D] (a pad slot has none).
+        int64_t orow_idx = batch_row0 + (int64_t)i * 64 + qi;
+        bool has_row = true;
+        if (raster) {
+            const int64_t tok = slot_to_token(g, (int64_t)i * 64 + qi);
+            has_row = tok >= 0;
+            orow_idx = (int64_t)b * g.L + (tok < 0 ? 0 : tok);
+        }
+        __bf16* orow = o + orow_idx * rs + head_off;
+        if (has_row) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 outv;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    bf16x4 outv;
 #pragma unroll
-                for (int u = 0; u < 4; ++u)  // pad rows: +0.0
-                    outv[u] = (__bf16)(valid ? oacc[db][r4 * 4 + u] * inv : 0.f);
-                *(bf16x4*)(orow + db * 32 + r4 * 8 + half * 4) = outv;
-            }
+                    for (int u = 0; u < 4; ++u)  // pad rows: +0.0
+                        outv[u] = (__bf16)(valid ? oacc[db][r4 * 4 + u] * inv : 0.f);
+                    *(bf16x4*)(orow + db * 32 + r4 * 8 + half * 4) = outv;
+                }
+        }
         if (lse != nullptr && half == 0) {
             const float val = valid ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
             lse[(int64_t)bh * g.Lpad + (int64_t)i * 64 + qi] = val;
@@ -676,7 +688,8 @@ int resident_per_xcd(const void* kernel) {
 
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, bool rotate, hipStream_t stream) {
+                           float scale, void* o, float* lse, bool rotate, bool raster,
+                           hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     const void* kernel =
         g.D == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
@@ -688,11 +701,13 @@ hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const voi
     if (g.D == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0);
+                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0,
+                           raster ? 1 : 0);
     else
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0);
+                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0,
+                           raster ? 1 : 0);
     return hipGetLastError();
 }
 

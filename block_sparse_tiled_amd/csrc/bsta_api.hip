@@ -31,7 +31,8 @@ hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32
                       int32_t* col_idx, hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, bool rotate, hipStream_t stream);
+                           float scale, void* o, float* lse, bool rotate, bool raster,
+                           hipStream_t stream);
 }  // namespace bsta
 
 using bsta::Geo;
@@ -167,6 +168,35 @@ int64_t workspace_of(const Geo& g, int32_t mode_in) {
 
 }  // namespace
 
+namespace {
+int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_tiled,
+                         const void* k_tiled, const void* v_tiled, const int32_t* row_ptr,
+                         const int32_t* col_idx, int64_t col_len, float softmax_scale,
+                         int32_t causal, void* o, float* lse, bool raster, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o == nullptr ||
+        row_ptr == nullptr || col_idx == nullptr)
+        return fail(BSTA_ERR_NULL, "%s: NULL tensor or index pointer", name);
+    if (causal != 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "causal=%d: block-sparse attention is bidirectional only",
+                    causal);
+    const double expected = 1.0 / sqrt((double)g.D);
+    const double diff = fabs((double)softmax_scale - expected);
+    const double tol = fmax(1e-4 * fmax(fabs((double)softmax_scale), expected), 1e-5);
+    if (!(diff <= tol))
+        return fail(BSTA_ERR_UNSUPPORTED, "softmax_scale %g must be 1/sqrt(D) = %g",
+                    (double)softmax_scale, expected);
+    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
+    return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
+                                            col_len, softmax_scale, o, lse,
+                                            g_deterministic.load(std::memory_order_relaxed) == 0,
+                                            raster, (hipStream_t)stream),
+                      name);
+}
+}  // namespace
+
 extern "C" {
 
 const char* attn_status_string(int32_t status) {
@@ -282,31 +312,22 @@ int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void
     return hip_status(e, "attn_select_blocks(top-k)");
 }
 
+
 int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
                               int64_t col_len, float softmax_scale, int32_t causal,
                               void* o_tiled, float* lse, void* stream) {
-    Geo g;
-    int32_t st = make_geo(gin, &g);
-    if (st != BSTA_OK) return st;
-    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o_tiled == nullptr ||
-        row_ptr == nullptr || col_idx == nullptr)
-        return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd: NULL tensor or index pointer");
-    if (causal != 0)
-        return fail(BSTA_ERR_UNSUPPORTED, "causal=%d: block-sparse attention is bidirectional only",
-                    causal);
-    const double expected = 1.0 / sqrt((double)g.D);
-    const double diff = fabs((double)softmax_scale - expected);
-    const double tol = fmax(1e-4 * fmax(fabs((double)softmax_scale), expected), 1e-5);
-    if (!(diff <= tol))
-        return fail(BSTA_ERR_UNSUPPORTED, "softmax_scale %g must be 1/sqrt(D) = %g",
-                    (double)softmax_scale, expected);
-    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
-    return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
-                                            col_len, softmax_scale, o_tiled, lse,
-                                            g_deterministic.load(std::memory_order_relaxed) == 0,
-                                            (hipStream_t)stream),
-                      "attn_block_sparse_fwd");
+    return block_sparse_fwd("attn_block_sparse_fwd", gin, q_tiled, k_tiled, v_tiled, row_ptr,
+                            col_idx, col_len, softmax_scale, causal, o_tiled, lse, false, stream);
+}
+
+int32_t attn_block_sparse_fwd_raster(const bsta_geom* gin, const void* q_tiled,
+                                     const void* k_tiled, const void* v_tiled,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_len, float softmax_scale, int32_t causal, void* o,
+                                     float* lse, void* stream) {
+    return block_sparse_fwd("attn_block_sparse_fwd_raster", gin, q_tiled, k_tiled, v_tiled,
+                            row_ptr, col_idx, col_len, softmax_scale, causal, o, lse, true, stream);
 }
 
 int32_t attn_set_deterministic(int32_t enable) {

@@ -11,35 +11,6 @@
 
 namespace bsta {
 
-// Raster token of slot s (s in [0, Lpad)), or -1 for a pad slot.
-__device__ inline int64_t slot_to_token(const Geo& g, int64_t s) {
-    int j = (int)(s >> 6);
-    int r = (int)(s & 63);
-    TileInfo t = tile_info(g, j);
-    if (r >= t.n) return -1;
-    int plane = t.sy * t.sx;
-    int dt = r / plane;
-    int rem = r - dt * plane;
-    int dy = rem / t.sx;
-    int dx = rem - dy * t.sx;
-    int tt = 4 * t.a + dt, yy = 4 * t.b + dy, xx = 4 * t.c + dx;
-    return ((int64_t)tt * g.Y + yy) * g.X + xx;
-}
-
-// Slot of raster token l.
-__device__ inline int64_t token_to_slot(const Geo& g, int64_t l) {
-    int64_t plane = (int64_t)g.Y * g.X;
-    int tt = (int)(l / plane);
-    int rem = (int)(l - (int64_t)tt * plane);
-    int yy = rem / g.X;
-    int xx = rem - yy * g.X;
-    int a = tt >> 2, b = yy >> 2, c = xx >> 2;
-    int sy = axis_extent(g.Y, b), sx = axis_extent(g.X, c);
-    int j = (a * g.nY + b) * g.nX + c;
-    int r = ((tt & 3) * sy + (yy & 3)) * sx + (xx & 3);
-    return (int64_t)j * kTileElems + r;
-}
-
 // Wide rows (64 to 1024 vectors of 16 bytes): LPR lanes per output row, so
 // a 256-thread workgroup copies 256/LPR rows.
 // The row's source is computed once per row; each lane loads its whole share

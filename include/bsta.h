@@ -12,7 +12,9 @@
  *
  * On the top-k path attn_tile_pool may replace attn_tile for Q and K: it
  * also writes the pooled vectors, and attn_select_blocks then runs with
- * BSTA_SELECT_PREPOOLED and skips its own pooling pass.
+ * BSTA_SELECT_PREPOOLED and skips its own pooling pass.  Likewise
+ * attn_block_sparse_fwd_raster writes the output in raster order and
+ * replaces attn_block_sparse_fwd followed by attn_untile.
  *
  * Conventions shared by every call:
  *   - Tensors are bfloat16, contiguous, in the layout [B, L, H, D] that the
@@ -205,6 +207,22 @@ int32_t attn_block_sparse_fwd(const bsta_geom* g, const void* q_tiled, const voi
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
                               int64_t col_len, float softmax_scale, int32_t causal,
                               void* o_tiled, float* lse, void* stream);
+
+/*
+ * attn_block_sparse_fwd_raster: attn_block_sparse_fwd followed by
+ * attn_untile in one pass ("bsa_attn" page, forward then
+ * postprocess_output): the output row of each valid query slot is written
+ * straight to the token it holds in raster order, and pad slots write
+ * nothing, which saves a read and a write of the output.  Arguments and key
+ * order as attn_block_sparse_fwd, except
+ *   o    [out] bf16 [B, L, H, D], raster order (every row written once)
+ *   lse  [out, fp32 [B, H, Lpad], may be NULL] in slot order, as above
+ */
+int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
+                                     const void* k_tiled, const void* v_tiled,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_len, float softmax_scale, int32_t causal, void* o,
+                                     float* lse, void* stream);
 
 /*
  * attn_set_deterministic (host only, no HIP call): process-wide key order of

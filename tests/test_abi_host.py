@@ -142,25 +142,27 @@ def test_select_errors(lib):
     assert _select(lib, many, mode=1, win=w) == _lib.BSTA_ERR_SHAPE
 
 
-def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16):
+def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16, fn="attn_block_sparse_fwd"):
     if scale is None:
         scale = 1.0 / math.sqrt(g.D)
-    return lib.attn_block_sparse_fwd(ctypes.byref(g), q, FAKE, FAKE, rp, FAKE, col_len, scale,
-                                     causal, o, None, None)
+    return getattr(lib, fn)(ctypes.byref(g), q, FAKE, FAKE, rp, FAKE, col_len, scale,
+                            causal, o, None, None)
 
 
-def test_fwd_errors(lib):
+@pytest.mark.parametrize("fn", ["attn_block_sparse_fwd", "attn_block_sparse_fwd_raster"])
+def test_fwd_errors(lib, fn):
     g = _g(D=128)
-    assert _fwd(lib, g, causal=1) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, causal=1, fn=fn) == _lib.BSTA_ERR_UNSUPPORTED
     assert "bidirectional" in _err(lib)
-    assert _fwd(lib, g, scale=0.125) == _lib.BSTA_ERR_UNSUPPORTED
-    assert _fwd(lib, g, scale=1.0) == _lib.BSTA_ERR_UNSUPPORTED
-    assert _fwd(lib, g, scale=float("nan")) == _lib.BSTA_ERR_UNSUPPORTED
-    assert _fwd(lib, g, q=None) == _lib.BSTA_ERR_NULL
-    assert _fwd(lib, g, o=None) == _lib.BSTA_ERR_NULL
-    assert _fwd(lib, g, rp=None) == _lib.BSTA_ERR_NULL
-    assert _fwd(lib, g, col_len=-1) == _lib.BSTA_ERR_SHAPE
-    assert _fwd(lib, _g(D=80)) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, scale=0.125, fn=fn) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, scale=1.0, fn=fn) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, scale=float("nan"), fn=fn) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _fwd(lib, g, q=None, fn=fn) == _lib.BSTA_ERR_NULL
+    assert fn in _err(lib)
+    assert _fwd(lib, g, o=None, fn=fn) == _lib.BSTA_ERR_NULL
+    assert _fwd(lib, g, rp=None, fn=fn) == _lib.BSTA_ERR_NULL
+    assert _fwd(lib, g, col_len=-1, fn=fn) == _lib.BSTA_ERR_SHAPE
+    assert _fwd(lib, _g(D=80), fn=fn) == _lib.BSTA_ERR_UNSUPPORTED
 
 
 def test_scale_tolerance_rule(lib):

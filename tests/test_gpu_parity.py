@@ -254,6 +254,33 @@ def test_block_sparse_attention_fused_route(bsta, name):
     assert torch.equal(o.view(torch.int16), r["o"].view(torch.int16))
 
 
+@pytest.mark.parametrize("name", sorted(SMALL) + sorted(STA_SMALL))
+def test_fwd_raster_equals_fwd_then_untile(bsta, name):
+    """attn_block_sparse_fwd_raster (output written in raster order, pad slots
+    skipped) equals attn_block_sparse_fwd followed by attn_untile bit for bit,
+    with the key walk in CSR order; every raster row is written (the buffer
+    starts as garbage) and the slot-order lse is the same."""
+    import torch
+    if name in STA_SMALL:
+        w, windows = STA_SMALL[name]
+    else:
+        w, windows = SMALL[name], None
+    inp = H.inputs(w)
+    H.log(f"raster output {name}")
+    g = _geom(bsta, w)
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        r = _run_gpu(bsta, w, inp, windows=windows, want_mask=False)
+        o = torch.full((w.B, w.L, w.H, w.D), 7.0, dtype=torch.bfloat16, device="cuda")
+        o, lse = bsta.attn_block_sparse_fwd(g, r["qt"], r["kt"], r["vt"], r["sel"].row_ptr,
+                                            r["sel"].col_idx, out=o, want_lse=True, raster=True)
+        torch.cuda.synchronize()
+    finally:
+        bsta.attn_set_deterministic(prev)
+    assert torch.equal(o.view(torch.int16), r["o"].view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), r["lse"].view(torch.int32))
+
+
 # ---------------------------------------------------------------- windows
 
 @pytest.mark.parametrize("name", sorted(STA_SMALL))
