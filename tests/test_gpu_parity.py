@@ -281,6 +281,37 @@ def test_fwd_raster_equals_fwd_then_untile(bsta, name):
     assert torch.equal(lse.view(torch.int32), r["lse"].view(torch.int32))
 
 
+@pytest.mark.parametrize("name", ["ragged_d128", "smooth_40"])
+def test_heads_first_layout_equals_standard(bsta, name):
+    """A heads-first [B, H, L, D] layout is the geometry (B*H, 1): every call
+    runs unchanged on it.  Tiles, CSR and output (CSR-order key walk) equal
+    those of the standard [B, L, H, D] layout, head by head, bit for bit."""
+    import torch
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"heads-first {name}")
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        r = _run_gpu(bsta, w, inp, want_mask=False)
+        gh = bsta.Geometry(w.B * w.H, 1, w.D, w.T, w.Y, w.X)
+        hf = {n: H.to_dev(inp[n]).permute(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D).contiguous()
+              for n in ("q", "k", "v")}
+        qt, kt, vt = (bsta.attn_tile(gh, hf[n]) for n in ("q", "k", "v"))
+        sel = bsta.attn_select_blocks(gh, qt, kt, bsta.SELECT_TOPK, w.topk, want_mask=False)
+        o = bsta.attn_block_sparse_fwd(gh, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+        torch.cuda.synchronize()
+    finally:
+        bsta.attn_set_deterministic(prev)
+    # Heads-first row order (b, h, i) is the standard CSR row order.
+    assert torch.equal(sel.row_ptr, r["sel"].row_ptr)
+    nnz = int(r["sel"].row_ptr[-1])
+    assert torch.equal(sel.col_idx[:nnz], r["sel"].col_idx[:nnz])
+    std_tiles = r["qt"].permute(0, 2, 1, 3).reshape(w.B * w.H, -1, 1, w.D)
+    assert torch.equal(qt.view(torch.int16), std_tiles.contiguous().view(torch.int16))
+    std_o = r["o"].permute(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D)
+    assert torch.equal(o.view(torch.int16), std_o.contiguous().view(torch.int16))
+
+
 # ---------------------------------------------------------------- windows
 
 @pytest.mark.parametrize("name", sorted(STA_SMALL))
