@@ -5,7 +5,7 @@ Python face of libbsta.so.  The four calls of the path keep the C names:
     attn_tile(g, x)                      raster [B,L,H,D] -> tiles [B,Lpad,H,D]
     attn_tile_pool(g, x, pooled=...)     the same, also writing the per-tile means
     attn_select_blocks(g, qt, kt, ...)   pooled scores -> top-k / window -> CSR
-    attn_block_sparse_fwd(g, qt, kt, vt, row_ptr, col_idx)
+    attn_block_sparse_fwd(g, qt, kt, vt, row_ptr, col_idx)   (raster=True: raster output)
     attn_untile(g, yt)                   tiles -> raster
 
 ``g`` is a ``Geometry``.  Tensors are torch bfloat16 tensors on the ROCm

@@ -12,26 +12,29 @@
 //   1. K and V arrive in LDS by direct global->LDS DMA (global_load_lds_
 //      dwordx4, 1 KB per instruction; each half-tile is issued whole by one
 //      wave, the low halves by wave 0 and the high halves by wave 1)
-//      into a ring of five half-tile slots (32 keys x D): K low half, K high
-//      half, V low, V high, then the next tile.  Before a slot is read, one
-//      workgroup barrier both publishes it and retires the previous slot,
-//      which is then refilled with the half-tile five places ahead, so up to
-//      four half-tiles are in flight while one is read.  Rows are XOR-
-//      swizzled in 16-byte chunks so every read below is free of bank
-//      conflicts (64 banks).
+//      into a ring of five half-tile slots (32 keys x D), consumed in pairs:
+//      K(t+1) low and high, then V(t) low and high.  Before a pair is read,
+//      one workgroup barrier publishes it and retires the previous pair,
+//      whose slots are refilled right away, so up to three half-tiles are in
+//      flight while a pair is read.  Rows are XOR-swizzled in 16-byte chunks
+//      so every read below is free of bank conflicts (64 banks).
 //   2. S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N): each
 //      lane ends up holding the scores of a single query.
 //   3. Online softmax in the exp2 domain (log2(e)/sqrt(D) folded into the
-//      scale); the row max needs one cross-lane exchange (lane ^ 32), the row
-//      sum stays per lane until the end.  The reference max is raised (and
-//      O, l rescaled) only when a row max exceeds it by more than 2^8.
+//      scale) against a reference max m taken from the first tile with a
+//      valid key; the row sum stays per lane until the end.  m is raised
+//      (and O, l rescaled; the row max then needs one cross-lane exchange,
+//      lane ^ 32) only when some lane's probability sum for a tile exceeds
+//      2^64 or is not finite, which keeps every p within fp32 and bf16.
 //   4. O^T += V^T P^T on the same MFMA.  The accumulator layout of step 2 is
 //      the B-operand layout this product needs, up to a fixed permutation of
 //      the 16 keys of each k-step; the A operand (V^T) comes from row-major V
 //      through the LDS transpose read ds_read_b64_tr_b16, four keys at a time
 //      in exactly that permuted order.
 // Partial key tiles (n_j < 64) mask keys r >= n_j to -inf; padded query rows
-// are written as +0.0.  Out-of-range tile ids contribute nothing.
+// are written as +0.0.  Out-of-range tile ids contribute nothing.  The output
+// goes to the tiled tensor, or (raster) straight to each token's row of the
+// [B, L, H, D] tensor, pad slots writing nothing.
 //
 // Lane layouts used (gfx950, checked on hardware):
 //   v_mfma_f32_32x32x16_bf16: A[m][k] in lane m + 32*(k/8), element k%8;
