@@ -37,11 +37,10 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "6c7eb211395ec80e",
-    "fetch_kib": 51753441, "write_kib": 792911,
-    "traffic_bytes": 106802988032,
-    "l2_hit": 0.453, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.446, "clock_ghz": 1.572,
+    "src_sha256_16": "23e2e59dfbcf7165",
+    "fetch_kib": 40463375, "write_kib": 791147, "traffic_bytes": 83679126528,
+    "l2_hit": 0.573, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.470, "clock_ghz": 1.626,
 }
 
 

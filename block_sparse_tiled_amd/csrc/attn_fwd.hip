@@ -8,7 +8,9 @@
 // Work decomposition: a workgroup of two wave64s owns one query tile (64
 // rows); wave w owns query rows 32w..32w+31 for the whole key list.  Four
 // such workgroups share a CU, so each SIMD runs two waves whose softmax and
-// MFMA phases overlap.  Per selected key tile:
+// MFMA phases overlap (a wave raises its priority for the score/softmax
+// phase below, so that phase's VALU work issues first).  Per selected key
+// tile:
 //   1. K and V arrive in LDS by direct global->LDS DMA (global_load_lds_
 //      dwordx4, 1 KB per instruction; each half-tile is issued whole by one
 //      wave, the low halves by wave 0 and the high halves by wave 1)
@@ -544,6 +546,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // groups per chunk pair when D = 64).
                 constexpr int NG = 2 * NDC / 4;
                 int sl;
+                // This phase (scores of t+1 interleaved with the
+                // probabilities of t) runs at raised wave priority, so its
+                // VALU-heavy stream issues ahead of the other resident wave,
+                // whose MFMAs keep the matrix pipe busy meanwhile; 3-6%
+                // faster than equal priorities at 40 heads x 1200 tiles,
+                // top-120 rows.
+                __builtin_amdgcn_s_setprio(1);
                 if (steady) BSTA_ACQUIRE_STEADY(sl, wave == 0);
                 else BSTA_ACQUIRE(sl);
                 scores(sl, sc_next, [&](int gi) {
@@ -555,6 +564,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int c = 0; c < 4; ++c) probs_chunk(sc_cur, c, neg_m, pf[c], ps[c]);
             }
+            __builtin_amdgcn_s_setprio(0);
             float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
             // The reference max starts from the first tile with a valid key
             // (m_init, wave-uniform); after that the probabilities are
