@@ -23,6 +23,13 @@ Readings taken where the pages are silent:
   * STA windows are shifted (clamped centre) windows: a window of w tiles
     starting at clamp(a - floor(w/2), 0, n - w) on each axis, so every row
     holds exactly prod(window) tiles and the full-grid window is dense.
+  * cumulative-threshold selection ("bsa_attn" page, forward: the key-value
+    block selection takes a cumulative threshold and a minimum block count;
+    the rule itself is not on the page): the pooled scores of a row, scaled
+    by the attention's 1/sqrt(D), go through a softmax over key tiles; the
+    tiles are taken in descending score order (ties to the lower index) and
+    a row keeps the shortest such prefix whose probability mass reaches the
+    threshold, but never fewer than min(min_blocks, Nt) tiles.
 """
 from __future__ import annotations
 
@@ -75,6 +82,51 @@ def kth_values(s: np.ndarray, k: int):
     upper = desc[..., k - 1]
     lower = desc[..., k] if k < nt else np.full(s.shape[:-1], -np.inf)
     return upper, lower
+
+
+def cumulative_counts(s: np.ndarray, D: int, threshold: float, min_blocks: int = 0) -> np.ndarray:
+    """Tiles kept per row by the cumulative-threshold rule: int64 [...].
+
+    p = softmax(S / sqrt(D)) over the row's key tiles (float64); with the
+    tiles in descending score order, the count is the first prefix length
+    whose summed p reaches `threshold` (Nt if none does, which only rounding
+    can cause), raised to min(min_blocks, Nt).
+    """
+    if not (0.0 < threshold <= 1.0):
+        raise ValueError(f"threshold {threshold} outside (0, 1]")
+    if min_blocks < 0:
+        raise ValueError(f"min_blocks {min_blocks} < 0")
+    nt = s.shape[-1]
+    z = s.astype(np.float64) / np.sqrt(float(D))
+    p = np.exp(z - z.max(axis=-1, keepdims=True))
+    p = p / p.sum(axis=-1, keepdims=True)
+    order = np.argsort(-s, axis=-1, kind="stable")
+    mass = np.cumsum(np.take_along_axis(p, order, axis=-1), axis=-1)
+    counts = np.minimum((mass < threshold).sum(axis=-1) + 1, nt)
+    return np.maximum(counts, min(min_blocks, nt))
+
+
+def prefix_mask(s: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """Keep the counts[r] best-scored tiles of every row r; ties to the lower index."""
+    nt = s.shape[-1]
+    order = np.argsort(-s, axis=-1, kind="stable")
+    rank = np.empty_like(order)
+    np.put_along_axis(rank, order, np.broadcast_to(np.arange(nt), order.shape), axis=-1)
+    return rank < np.asarray(counts)[..., None]
+
+
+def cumulative_mask(s: np.ndarray, D: int, threshold: float, min_blocks: int = 0) -> np.ndarray:
+    """Block mask of the cumulative-threshold selection: bool, shape of s."""
+    return prefix_mask(s, cumulative_counts(s, D, threshold, min_blocks))
+
+
+def cumulative_masses(s: np.ndarray, D: int) -> np.ndarray:
+    """Probability mass of the top-c prefix of every row, c = 1..Nt (float64)."""
+    z = s.astype(np.float64) / np.sqrt(float(D))
+    p = np.exp(z - z.max(axis=-1, keepdims=True))
+    p = p / p.sum(axis=-1, keepdims=True)
+    order = np.argsort(-s, axis=-1, kind="stable")
+    return np.cumsum(np.take_along_axis(p, order, axis=-1), axis=-1)
 
 
 def topk_from_ratio(ratio: float, nt: int) -> int:

@@ -230,6 +230,86 @@ def test_boundary_gap():
     assert up[0] == 1.0 and lo[0] == 0.5
 
 
+def test_cumulative_golden_rows():
+    g = _golden("select_examples.json")["cumulative_rows"]
+    for case in g["cases"]:
+        s = np.array([case["scores"]])
+        m = select.cumulative_mask(s, g["D"], case["threshold"], case["min_blocks"])
+        assert list(np.nonzero(m[0])[0]) == case["selected"], case
+
+
+def _softmax_py(row, D):
+    z = [v / math.sqrt(D) for v in row]
+    top = max(z)
+    e = [math.exp(v - top) for v in z]
+    tot = math.fsum(e)
+    return [v / tot for v in e]
+
+
+def test_cumulative_brute_force_subsets():
+    """The count is the least c for which SOME c-subset of tiles holds at
+    least the threshold's mass (all subsets enumerated), raised to the
+    minimum; the kept set is the c-subset of largest mass."""
+    rng = np.random.default_rng(21)
+    for _ in range(150):
+        n = int(rng.integers(1, 8))
+        D = int(rng.choice([16, 64, 128]))
+        row = rng.standard_normal(n) * float(rng.choice([1.0, 8.0, 30.0]))
+        tau = float(rng.uniform(0.01, 1.0))
+        mb = int(rng.integers(0, n + 2))
+        p = _softmax_py(row, D)
+        best = {c: max(itertools.combinations(range(n), c), key=lambda sub: math.fsum(p[j] for j in sub))
+                for c in range(1, n + 1)}
+        c = next((c for c in range(1, n + 1) if math.fsum(p[j] for j in best[c]) >= tau), n)
+        c = max(c, min(mb, n))
+        got = select.cumulative_mask(row[None], D, tau, mb)[0]
+        assert int(select.cumulative_counts(row[None], D, tau, mb)[0]) == c
+        assert tuple(np.nonzero(got)[0]) == tuple(sorted(best[c]))
+
+
+def test_cumulative_small_threshold_is_topk():
+    """A threshold below every tile's probability keeps max(1, min_blocks)
+    tiles: the top-k selection with that k."""
+    rng = np.random.default_rng(22)
+    s = rng.integers(-3, 4, size=(3, 5, 40)).astype(np.float64)   # ties included
+    for mb in (0, 1, 7, 40, 55):
+        k = max(1, min(mb, 40))
+        assert np.array_equal(select.cumulative_mask(s, 64, 1e-30, mb), select.topk_mask(s, k))
+
+
+def test_cumulative_invariants():
+    rng = np.random.default_rng(23)
+    s = rng.standard_normal((4, 200)) * 20.0
+    D = 128
+    p = np.exp(s / math.sqrt(D) - (s / math.sqrt(D)).max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    prev = np.zeros(4, dtype=np.int64)
+    for tau in (0.05, 0.2, 0.5, 0.8, 0.95, 1.0):
+        m = select.cumulative_mask(s, D, tau)
+        cnt = m.sum(-1)
+        assert np.all(cnt >= prev)            # a higher threshold never keeps fewer
+        prev = cnt
+        kept = np.where(m, p, 0.0).sum(-1)
+        assert np.all(kept >= tau - 1e-12)
+        # dropping the weakest kept tile falls below the threshold
+        weakest = np.where(m, p, np.inf).min(-1)
+        assert np.all(kept - weakest < tau)
+        # every kept tile outscores every dropped one
+        assert np.all(np.where(m, s, np.inf).min(-1) >= np.where(m, -np.inf, s).max(-1))
+    masses = select.cumulative_masses(s, D)
+    assert np.allclose(masses[:, -1], 1.0, atol=1e-12)
+    assert np.all(np.diff(masses, axis=-1) >= 0)
+
+
+def test_cumulative_rejects_bad_arguments():
+    s = np.zeros((1, 4))
+    for tau in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            select.cumulative_counts(s, 64, tau)
+    with pytest.raises(ValueError):
+        select.cumulative_counts(s, 64, 0.5, -1)
+
+
 def test_topk_from_ratio():
     assert select.topk_from_ratio(0.1, 1200) == 120
     assert select.topk_from_ratio(0.125, 256) == 32
