@@ -28,6 +28,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+# Threshold of the cumulative-threshold selection timed beside the step: on
+# the synthetic 40-head 1200-tile workload it keeps about 10% of the key
+# tiles, the density of its top-120 selection.
+CUM_THRESHOLD = 0.15
 METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI355X"
 
 # Counter readings of the attention kernel on the default workload, from the
@@ -254,6 +258,38 @@ def main():
     cold_ms = float(np.median(cold))
     print(f"[bench] attention cold-L2 median ms {cold_ms:.3f}", file=sys.stderr, flush=True)
 
+    # The cumulative-threshold selection (attn_select_cumulative) on the same
+    # pooled Q and K, and the attention over its variable-length rows; not
+    # part of the step.
+    cum = None
+    if fused and nt <= 2048:
+        sel_c = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, want_mask=False, device=dev)
+        cq, ck = sel_c.pooled(g)
+        cq.copy_(pq)
+        ck.copy_(pk)
+        per_c, per_ca = [], []
+        for _ in range(n_calls):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            bsta.attn_select_cumulative(g, None, None, CUM_THRESHOLD, 0, prepooled=True, out=sel_c)
+            e[1].record()
+            bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel_c.row_ptr, sel_c.col_idx, out=o,
+                                       raster=True)
+            e[2].record()
+            torch.cuda.synchronize()
+            per_c.append(e[0].elapsed_time(e[1]))
+            per_ca.append(e[1].elapsed_time(e[2]))
+        nnz_c = int(sel_c.row_ptr[-1].item())
+        c_ms, ca_ms = float(np.median(per_c)), float(np.median(per_ca))
+        cum = {"ms": c_ms, "threshold": CUM_THRESHOLD, "min_blocks": 0,
+               "selected_tile_pairs": nnz_c, "density": nnz_c / float(w.B * w.H * nt * nt),
+               "attn_ms": ca_ms,
+               "attn_tflops": attention_flop(w, nnz_c) / (ca_ms * 1e-3) / 1e12,
+               "note": "scores + cumulative-threshold counts + row scan + selection (prepooled); "
+                       "attention over its rows; not in the step"}
+        print(f"[bench] cumulative selection {cum}", file=sys.stderr, flush=True)
+        del sel_c
+
     flop = attention_flop(w, nnz)
     prof = measured_attn() if args.workload == "c3" and not args.deterministic else None
     dense_flop = 4.0 * w.D * w.B * w.H * float(w.L) ** 2
@@ -318,6 +354,7 @@ def main():
                                if fused else None),
             "untile": {"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
                        "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
+            "select_cumulative": cum,
         },
     }
     if not args.no_cpu_baseline:

@@ -21,10 +21,11 @@ import math
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, BstaError
+from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, BstaError
 
 __all__ = [
-    "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_PREPOOLED", "attn_tile",
+    "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
+    "attn_select_cumulative", "attn_tile",
     "attn_tile_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
     "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
@@ -211,6 +212,34 @@ def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, t
     return out
 
 
+def attn_select_cumulative(g: Geometry, q_tiled, k_tiled, threshold: float, min_blocks: int = 0,
+                           prepooled: bool = False, want_mask: bool = True,
+                           out: Optional[Selection] = None) -> Selection:
+    """Coarse stage with a cumulative probability threshold: each query tile
+    keeps the shortest run of its best key tiles whose softmax(S/sqrt(D))
+    mass reaches ``threshold`` (and at least ``min_blocks``).  Row lengths
+    vary: ``row_ptr[-1]`` is the entry count, and ``col_idx`` is sized for
+    the worst case.  With ``prepooled``, ``out`` (from attn_select_alloc with
+    SELECT_CUMULATIVE) already holds the pooled Q and K from attn_tile_pool."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    if not prepooled:
+        _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
+        _expect(k_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "k_tiled")
+    elif out is None or out.workspace is None:
+        raise ValueError("prepooled needs `out` holding the pooled Q and K")
+    if out is None:
+        out = attn_select_alloc(g, SELECT_CUMULATIVE, 0, None, want_mask, q_tiled.device)
+    ws = out.workspace
+    status = _lib.load().attn_select_cumulative(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), SELECT_PREPOOLED if prepooled else 0,
+        float(threshold), int(min_blocks), _ptr(out.block_mask), _ptr(out.row_ptr),
+        _ptr(out.col_idx), out.col_idx.numel(), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _lib.check(status)
+    return out
+
+
 def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                           softmax_scale: Optional[float] = None, causal: bool = False,
                           out=None, lse=None, want_lse: bool = False, raster: bool = False):
@@ -250,16 +279,24 @@ def attn_set_deterministic(enable: bool) -> bool:
 
 
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
-                           windows=None):
+                           windows=None, threshold: Optional[float] = None, min_blocks: int = 0):
     """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile.
-    In top-k mode Q and K are pooled while they are tiled; the attention
-    writes its output in raster order directly."""
-    if mode == SELECT_TOPK:
+    ``mode`` is SELECT_TOPK (``topk``), SELECT_STA (``windows``) or
+    SELECT_CUMULATIVE (``threshold``, ``min_blocks``).  With top-k and the
+    cumulative threshold Q and K are pooled while they are tiled; the
+    attention writes its output in raster order directly."""
+    if mode in (SELECT_TOPK, SELECT_CUMULATIVE):
         sel = attn_select_alloc(g, mode, topk, want_mask=False, device=q.device)
         pq, pk = sel.pooled(g)
         qt, kt = attn_tile_pool(g, q, pq), attn_tile_pool(g, k, pk)
         vt = attn_tile(g, v)
-        sel = attn_select_blocks(g, None, None, SELECT_TOPK | SELECT_PREPOOLED, topk, out=sel)
+        if mode == SELECT_TOPK:
+            sel = attn_select_blocks(g, None, None, SELECT_TOPK | SELECT_PREPOOLED, topk, out=sel)
+        else:
+            if threshold is None:
+                raise ValueError("SELECT_CUMULATIVE needs a threshold")
+            sel = attn_select_cumulative(g, None, None, threshold, min_blocks, prepooled=True,
+                                         out=sel)
     else:
         qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
         sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)

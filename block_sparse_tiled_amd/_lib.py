@@ -22,12 +22,14 @@ BSTA_ERR_CAPACITY = -4
 BSTA_ERR_HIP = -5
 SELECT_TOPK = 0
 SELECT_STA = 1
+SELECT_CUMULATIVE = 2
 SELECT_PREPOOLED = 0x100
 MAX_STA_HEADS = 256
 
 EXPORTS = (
     "attn_geometry", "attn_tile", "attn_tile_pool", "attn_untile", "attn_select_capacity",
-    "attn_workspace_bytes", "attn_select_blocks", "attn_block_sparse_fwd",
+    "attn_workspace_bytes", "attn_select_blocks", "attn_select_cumulative",
+    "attn_block_sparse_fwd",
     "attn_block_sparse_fwd_raster",
     "attn_status_string", "attn_last_error", "attn_set_deterministic",
 )
@@ -68,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "attn_select_capacity": (i64, [G, i32, i32, P]),
         "attn_workspace_bytes": (i64, [G, i32]),
         "attn_select_blocks": (i32, [G, P, P, i32, i32, P, P, P, P, i64, P, i64, P]),
+        "attn_select_cumulative": (i32, [G, P, P, i32, ctypes.c_float, i32, P, P, P, i64, P, i64, P]),
         "attn_block_sparse_fwd": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P]),
         "attn_block_sparse_fwd_raster": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P]),
         "attn_status_string": (ctypes.c_char_p, [i32]),

@@ -29,6 +29,9 @@ hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32
                        int32_t* col_idx, hipStream_t stream);
 hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32_t* row_ptr,
                       int32_t* col_idx, hipStream_t stream);
+hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, const float* s,
+                              uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
+                              hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
                            float scale, void* o, float* lse, bool rotate, bool raster,
@@ -47,6 +50,9 @@ std::atomic<int> g_deterministic{0};
 // Largest tile count top-k selection accepts (its per-row keys and flags
 // live in LDS: 5 bytes per tile).
 constexpr int kMaxTopkTiles = 12288;
+// Largest tile count the cumulative-threshold selection accepts (one wave
+// holds a row in registers, 32 scores per lane).
+constexpr int kMaxCumulativeTiles = 2048;
 // Largest grid side (tile coordinates travel as int16 in window mode).
 constexpr int kMaxDim = 1 << 15;
 
@@ -131,7 +137,7 @@ int32_t check_windows(const Geo& g, const int32_t* w, int64_t* per_batch) {
 int32_t base_mode(int32_t mode) {
     if (mode & BSTA_SELECT_PREPOOLED) {
         const int32_t m = mode & ~BSTA_SELECT_PREPOOLED;
-        return m == BSTA_SELECT_TOPK ? m : -1;
+        return m == BSTA_SELECT_TOPK || m == BSTA_SELECT_CUMULATIVE ? m : -1;
     }
     return mode;
 }
@@ -148,6 +154,9 @@ int64_t capacity_of(const Geo& g, int32_t mode_in, int32_t topk, const int32_t* 
         int32_t st = check_windows(g, windows, &per_batch);
         if (st != BSTA_OK) return st;
         nnz = (int64_t)g.B * g.Nt * per_batch;
+    } else if (mode == BSTA_SELECT_CUMULATIVE) {
+        // Data-dependent row lengths: room for every row to keep all tiles.
+        nnz = (int64_t)g.B * g.H * g.Nt * g.Nt;
     } else {
         return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode_in);
     }
@@ -159,7 +168,7 @@ int64_t capacity_of(const Geo& g, int32_t mode_in, int32_t topk, const int32_t* 
 int64_t workspace_of(const Geo& g, int32_t mode_in) {
     const int32_t mode = base_mode(mode_in);
     if (mode == BSTA_SELECT_STA) return 0;
-    if (mode != BSTA_SELECT_TOPK)
+    if (mode != BSTA_SELECT_TOPK && mode != BSTA_SELECT_CUMULATIVE)
         return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode_in);
     const int64_t pooled = (int64_t)2 * g.B * g.H * g.Nt * g.D;
     const int64_t scores = (int64_t)g.B * g.H * g.Nt * g.Nt;
@@ -290,6 +299,9 @@ int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void
     hipStream_t s = (hipStream_t)stream;
     const bool prepooled = (mode & BSTA_SELECT_PREPOOLED) != 0;
     mode = base_mode(mode);
+    if (mode == BSTA_SELECT_CUMULATIVE)
+        return fail(BSTA_ERR_UNSUPPORTED,
+                    "attn_select_blocks: the cumulative-threshold mode is attn_select_cumulative");
     if (mode == BSTA_SELECT_STA)
         return hip_status(bsta::launch_sta(g, sta_windows_host, block_mask, row_ptr, col_idx, s),
                           "attn_select_blocks(window)");
@@ -312,6 +324,48 @@ int32_t attn_select_blocks(const bsta_geom* gin, const void* q_tiled, const void
     return hip_status(e, "attn_select_blocks(top-k)");
 }
 
+int32_t attn_select_cumulative(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
+                               int32_t flags, float threshold, int32_t min_blocks,
+                               uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (flags != 0 && flags != BSTA_SELECT_PREPOOLED)
+        return fail(BSTA_ERR_UNSUPPORTED, "attn_select_cumulative: flags %d unknown", flags);
+    const bool prepooled = flags == BSTA_SELECT_PREPOOLED;
+    if (row_ptr == nullptr || col_idx == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_select_cumulative: NULL row_ptr or col_idx");
+    if (!prepooled && (q_tiled == nullptr || k_tiled == nullptr))
+        return fail(BSTA_ERR_NULL, "attn_select_cumulative: NULL q_tiled or k_tiled");
+    if (!(threshold > 0.f && threshold <= 1.f))
+        return fail(BSTA_ERR_SHAPE, "threshold %g outside (0, 1]", (double)threshold);
+    if (min_blocks < 0) return fail(BSTA_ERR_SHAPE, "min_blocks %d < 0", min_blocks);
+    if (g.Nt > kMaxCumulativeTiles)
+        return fail(BSTA_ERR_SHAPE, "cumulative selection supports at most %d tiles, got %d",
+                    kMaxCumulativeTiles, g.Nt);
+    const int64_t need = capacity_of(g, BSTA_SELECT_CUMULATIVE, 0, nullptr);
+    if (need < 0) return (int32_t)need;
+    if (col_capacity < need)
+        return fail(BSTA_ERR_CAPACITY, "col_capacity %lld < %lld entries (every row may keep all tiles)",
+                    (long long)col_capacity, (long long)need);
+    const int64_t ws = workspace_of(g, BSTA_SELECT_CUMULATIVE);
+    if (workspace == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_select_cumulative: NULL workspace");
+    if (workspace_bytes < ws)
+        return fail(BSTA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                    (long long)workspace_bytes, (long long)ws);
+    hipStream_t s = (hipStream_t)stream;
+    float* pq = (float*)workspace;
+    float* pk = pq + (int64_t)g.B * g.H * g.Nt * g.D;
+    float* sc = pk + (int64_t)g.B * g.H * g.Nt * g.D;
+    hipError_t e = prepooled ? hipSuccess : bsta::launch_pool(g, q_tiled, k_tiled, pq, pk, s);
+    if (e == hipSuccess) e = bsta::launch_scores(g, pq, pk, sc, s);
+    if (e == hipSuccess)
+        e = bsta::launch_cumulative(g, threshold, min_blocks, sc, block_mask, row_ptr, col_idx, s);
+    return hip_status(e, "attn_select_cumulative");
+}
 
 int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,

@@ -245,15 +245,11 @@ __global__ __launch_bounds__(256) void topk_kernel(
 // equal to it the first k - (count above) in j order; with j = 64c + l,
 // walking c upward and ranking lanes by mbcnt visits j in increasing order,
 // so the same ballots give the tie ranks and the ascending CSR positions.
+// Writes the k kept ids to out[0, k) and the row's mask (if any).
 template <int C>
-__global__ __launch_bounds__(256) void topk_wave_kernel(
-        int Nt, int k, int64_t rows, const float* __restrict__ s,
-        uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr,
-        int32_t* __restrict__ col_idx) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // wave-uniform
-    const float* srow = s + row * Nt;
+__device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ srow,
+                                       uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
+                                       int lane) {
     uint32_t key[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -278,8 +274,6 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(
         above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key[c] > thr));
     }
     const int take_eq = k - above;
-    int32_t* out = col_idx + row * k;
-    uint8_t* mrow = mask ? mask + row * Nt : nullptr;
     int base = 0, eq_base = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -298,10 +292,161 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(
         if (sel && pos < k) out[pos] = j;
         if (mrow && valid) mrow[j] = sel;
     }
+}
+
+// Top-k: every row keeps k tiles; CSR row r starts at r*k.
+template <int C>
+__global__ __launch_bounds__(256) void topk_wave_kernel(
+        int Nt, int k, int64_t rows, const float* __restrict__ s,
+        uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr,
+        int32_t* __restrict__ col_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    select_row_wave<C>(Nt, k, s + row * Nt, mask ? mask + row * Nt : nullptr, col_idx + row * k,
+                       lane);
     if (lane == 0) {
         row_ptr[row] = (int32_t)(row * k);
         if (row == rows - 1) row_ptr[rows] = (int32_t)(rows * k);
     }
+}
+
+// ------------------------------------------------------------------ cumulative threshold
+// Reading of the "bsa_attn" page's key-value block selection (a cumulative
+// threshold and a minimum block count; the rule is not on the page): with
+// p_j = softmax_j(S_ij / sqrt(D)) over a row's key tiles, taken in
+// descending score order (ties to the lower index), a row keeps the
+// shortest prefix whose mass reaches threshold * sum_j p_j, and at least
+// min(min_blocks, Nt) tiles.  Every such row is a top-c row of the same
+// ranking, so the ids are written by select_row_wave with c = the row's
+// count.
+
+// Sum over the wave, taken from lane 0 so that every lane sees the same
+// value (the butterfly gives each lane its own rounding order).
+__device__ inline float wave_sum_uniform(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+__device__ inline float wave_max_uniform(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// One wave per CSR row: counts[row] = tiles kept.  p is fp32 exp2 of the
+// scaled score minus the row max (the max tile has p = 1, so the total is at
+// least 1).  The kept prefix ends at the largest key x whose tiles at or
+// above x hold at least threshold * total, found bit by bit from the top as
+// in select_row_wave; all masses come from the same per-lane order and
+// summation tree, and adding non-negative terms is monotone in every term,
+// so the mass is non-increasing in x and the search is exact on these fp32
+// values.  Of the tiles tied at x (equal scores, equal p), the lowest-index
+// ones are added one at a time until the mass is reached.
+template <int C>
+__global__ __launch_bounds__(256) void cumulative_count_kernel(
+        int Nt, int64_t rows, const float* __restrict__ s, float scale_log2, float threshold,
+        int kmin, int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const float* srow = s + row * Nt;
+    float sv[C];
+    uint32_t key[C];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * 64 + lane;
+        sv[c] = j < Nt ? srow[j] : -INFINITY;
+        key[c] = j < Nt ? score_key(sv[c]) : 0u;
+        mloc = fmaxf(mloc, sv[c]);
+    }
+    const float mx = wave_max_uniform(mloc);
+    float p[C];
+    float loc = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        p[c] = c * 64 + lane < Nt ? __builtin_amdgcn_exp2f((sv[c] - mx) * scale_log2) : 0.f;
+        loc += p[c];
+    }
+    const float target = threshold * wave_sum_uniform(loc);
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) m += key[c] >= cand ? p[c] : 0.f;
+        if (wave_sum_uniform(m) >= target) thr = cand;
+    }
+    float m_above = 0.f, p_eq = 0.f;
+    int above = 0, eq = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const bool valid = c * 64 + lane < Nt;
+        m_above += valid && key[c] > thr ? p[c] : 0.f;
+        above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key[c] > thr));
+        const uint64_t em = __builtin_amdgcn_ballot_w64(valid && key[c] == thr);
+        eq += __builtin_popcountll(em);
+        if (em != 0 && p_eq == 0.f) {
+            const int src = __builtin_ctzll(em);
+            p_eq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[c]), src));
+        }
+    }
+    float acc = wave_sum_uniform(m_above);
+    int take = 0;
+    while (take < eq && acc < target) {  // wave-uniform
+        acc += p_eq;
+        ++take;
+    }
+    if (take == 0 && eq > 0) take = 1;
+    int cnt = above + take;
+    cnt = cnt > kmin ? cnt : kmin;
+    cnt = cnt < Nt ? cnt : Nt;
+    if (lane == 0) counts[row] = cnt;
+}
+
+// In-place scan of row counts into CSR offsets: on entry row_ptr[r + 1]
+// holds the count of row r; on exit row_ptr[r] is the start of row r and
+// row_ptr[rows] the total.  One workgroup of 1024 threads, each over a
+// contiguous run of rows.
+__global__ __launch_bounds__(1024) void scan_counts_kernel(int64_t rows,
+                                                           int32_t* __restrict__ row_ptr) {
+    __shared__ int64_t part[1024];
+    const int64_t per = (rows + 1023) / 1024;
+    const int64_t r0 = (int64_t)threadIdx.x * per;
+    const int64_t r1 = r0 + per < rows ? r0 + per : rows;
+    int64_t sum = 0;
+    for (int64_t r = r0; r < r1; ++r) sum += row_ptr[r + 1];
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 1024 partial sums.
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int64_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int64_t run = part[threadIdx.x] - sum;  // exclusive prefix of this run
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t c = row_ptr[r + 1];
+        run += c;
+        row_ptr[r + 1] = (int32_t)run;
+    }
+    if (threadIdx.x == 0) row_ptr[0] = 0;
+}
+
+// Writes each row's ids given its CSR range (row_ptr from the scan).
+template <int C>
+__global__ __launch_bounds__(256) void prefix_select_kernel(
+        int Nt, int64_t rows, const float* __restrict__ s, uint8_t* __restrict__ mask,
+        const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const int32_t p0 = row_ptr[row];
+    const int k = row_ptr[row + 1] - p0;
+    select_row_wave<C>(Nt, k, s + row * Nt, mask ? mask + row * Nt : nullptr, col_idx + p0, lane);
 }
 
 // ------------------------------------------------------------------ STA
@@ -399,6 +544,31 @@ hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32
                            rows, s, mask, row_ptr, col_idx);
     }
 #undef BSTA_TOPK_WAVE
+    return hipGetLastError();
+}
+
+hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, const float* s,
+                              uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
+                              hipStream_t stream) {
+    const int64_t rows = (int64_t)g.B * g.H * g.Nt;
+    const int chunks = (g.Nt + 63) / 64;
+    const unsigned wave_blocks = (unsigned)((rows + 3) / 4);
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
+    const int kmin = min_blocks < g.Nt ? min_blocks : g.Nt;
+#define BSTA_CUM(CC)                                                                           \
+    do {                                                                                       \
+        hipLaunchKernelGGL(cumulative_count_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream, \
+                           g.Nt, rows, s, scale_log2, threshold, kmin, row_ptr + 1);           \
+        hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, rows, row_ptr);  \
+        hipLaunchKernelGGL(prefix_select_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream,   \
+                           g.Nt, rows, s, mask, row_ptr, col_idx);                             \
+    } while (0)
+    if (chunks <= 8) BSTA_CUM(8);
+    else if (chunks <= 16) BSTA_CUM(16);
+    else if (chunks <= 24) BSTA_CUM(24);
+    else if (chunks <= 32) BSTA_CUM(32);
+    else return hipErrorInvalidValue;  // the caller rejects Nt > 2048 first
+#undef BSTA_CUM
     return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@
  *   attn_select_blocks   per-tile mean pooling of Q and K, pooled scores, top-k
  *                        key tiles per query tile (or a sliding tile window),
  *                        block mask and CSR index map
+ *                        (attn_select_cumulative: the same with a cumulative
+ *                        probability threshold instead of a fixed k)
  *   attn_block_sparse_fwd  softmax(q k^T / sqrt(D)) v over the selected tiles
  *   attn_untile          tile order -> raster order
  *
@@ -62,9 +64,10 @@ enum {
     BSTA_ERR_HIP = -5           /* a HIP launch failed                      */
 };
 
-enum { BSTA_SELECT_TOPK = 0, BSTA_SELECT_STA = 1 };
-/* Flag for BSTA_SELECT_TOPK: the workspace already holds pooled Q and K
- * (written by attn_tile_pool); see attn_select_blocks. */
+enum { BSTA_SELECT_TOPK = 0, BSTA_SELECT_STA = 1, BSTA_SELECT_CUMULATIVE = 2 };
+/* Flag for BSTA_SELECT_TOPK and BSTA_SELECT_CUMULATIVE: the workspace
+ * already holds pooled Q and K (written by attn_tile_pool); see
+ * attn_select_blocks and attn_select_cumulative. */
 enum { BSTA_SELECT_PREPOOLED = 0x100 };
 
 /* Largest head count a sliding-tile-window call accepts (windows travel as
@@ -126,16 +129,18 @@ int32_t attn_untile(const bsta_geom* g, const void* y_tiled, void* y, void* stre
 /*
  * attn_select_capacity (host only): number of CSR entries a selection
  * produces, B*H*Nt*k for top-k and Nt*B*sum_h prod(window_h) for windows;
- * a negative status on bad arguments.
+ * for BSTA_SELECT_CUMULATIVE, whose row lengths depend on the data, the
+ * bound B*H*Nt*Nt; a negative status on bad arguments.
  */
 int64_t attn_select_capacity(const bsta_geom* g, int32_t mode, int32_t topk,
                              const int32_t* sta_windows_host);
 
 /*
  * attn_workspace_bytes (host only): bytes of device workspace
- * attn_select_blocks needs in the given mode (0 for windows; for top-k the
- * pooled Q and K, fp32 [2, B, H, Nt, D], then the pooled scores fp32
- * [B, H, Nt, Nt]); a negative status on bad arguments.
+ * attn_select_blocks needs in the given mode (0 for windows; for top-k and
+ * for the cumulative threshold the pooled Q and K, fp32 [2, B, H, Nt, D],
+ * then the pooled scores fp32 [B, H, Nt, Nt]); a negative status on bad
+ * arguments.
  */
 int64_t attn_workspace_bytes(const bsta_geom* g, int32_t mode);
 
@@ -175,6 +180,43 @@ int32_t attn_select_blocks(const bsta_geom* g, const void* q_tiled, const void* 
                            uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
                            int64_t col_capacity, void* workspace, int64_t workspace_bytes,
                            void* stream);
+
+/*
+ * attn_select_cumulative: the coarse stage with a cumulative probability
+ * threshold.  The "bsa_attn" page's forward selects key-value blocks from a
+ * cumulative threshold and a minimum block count without showing the rule;
+ * the reading implemented here: pooling and pooled scores S as in top-k
+ * mode, then per query tile p_j = softmax_j(S_ij / sqrt(D)) over the key
+ * tiles; with the tiles in descending score order (ties to the lower
+ * index), the row keeps the shortest prefix whose mass reaches
+ * threshold * sum_j p_j, and at least min(min_blocks, Nt) tiles.  The CSR
+ * row lengths therefore vary; row_ptr is their running sum.
+ *   q_tiled, k_tiled  [in]  bf16 [B, Lpad, H, D] from attn_tile; unused (may
+ *                           be NULL) with BSTA_SELECT_PREPOOLED
+ *   flags             0 or BSTA_SELECT_PREPOOLED (the workspace already
+ *                     holds pooled Q then pooled K, from attn_tile_pool)
+ *   threshold         in (0, 1]
+ *   min_blocks        >= 0 (values above Nt keep every tile)
+ *   block_mask        [out, uint8 [B, H, Nt, Nt], may be NULL] 1 = kept
+ *   row_ptr           [out, int32 [B*H*Nt + 1]]; row_ptr[B*H*Nt] is the
+ *                     number of entries written
+ *   col_idx           [out, int32 [col_capacity]], ascending per row
+ *   col_capacity      >= B*H*Nt*Nt (attn_select_capacity with
+ *                     BSTA_SELECT_CUMULATIVE), since any row may keep
+ *                     every tile
+ *   workspace         [scratch, >= attn_workspace_bytes(g,
+ *                     BSTA_SELECT_CUMULATIVE)]; afterwards it holds the
+ *                     pooled Q, K and scores
+ * Requires Nt <= 2048 (a row of scores lives in one wave's registers);
+ * larger grids return BSTA_ERR_SHAPE.  Probabilities and their sums are
+ * fp32, so a row whose prefix mass lies within rounding of the threshold
+ * may keep one tile more or less than an exact computation would.
+ */
+int32_t attn_select_cumulative(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
+                               int32_t flags, float threshold, int32_t min_blocks,
+                               uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                               void* stream);
 
 /*
  * attn_block_sparse_fwd: fused block-sparse flash attention forward

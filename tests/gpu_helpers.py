@@ -79,6 +79,43 @@ def accept_topk_rows(gpu_mask: np.ndarray, oracle_scores: np.ndarray, k: int):
     return len(s2) - len(diff_rows), len(diff_rows)
 
 
+# Probability-mass band of the cumulative-threshold selection (fp32 sums on
+# the GPU against the oracle's float64 prefix masses).
+MASS_BAND = 1e-4
+
+
+def accept_cumulative_rows(gpu_mask: np.ndarray, oracle_scores: np.ndarray, D: int,
+                           threshold: float, min_blocks: int):
+    """Check every row of a GPU cumulative-threshold mask against the oracle.
+
+    A row keeping c tiles is accepted when c >= max(1, min(min_blocks, Nt));
+    the oracle's float64 mass of its best c tiles reaches threshold -
+    MASS_BAND (or c = Nt); the best c - 1 stay below threshold + MASS_BAND
+    (or c is the minimum); and the set is the top-c set up to the top-k tie
+    band.  Returns (rows whose count equals the oracle's, rows within the
+    band) and raises AssertionError on the first failing row.
+    """
+    nt = oracle_scores.shape[-1]
+    s2 = oracle_scores.reshape(-1, nt)
+    gm2 = gpu_mask.astype(bool).reshape(-1, nt)
+    cnt = gm2.sum(axis=1)
+    kmin = max(1, min(min_blocks, nt))
+    masses = select.cumulative_masses(s2, D)
+    ocnt = select.cumulative_counts(s2, D, threshold, min_blocks)
+    for r in np.nonzero(cnt != ocnt)[0]:
+        c = int(cnt[r])
+        assert c >= kmin, f"row {r}: {c} tiles kept, below the minimum {kmin}"
+        assert c == nt or masses[r, c - 1] >= threshold - MASS_BAND, \
+            f"row {r}: {c} tiles hold mass {masses[r, c - 1]:.6f} < {threshold}"
+        assert c == kmin or masses[r, c - 2] < threshold + MASS_BAND, \
+            f"row {r}: {c - 1} tiles already hold {masses[r, c - 2]:.6f} >= {threshold}"
+    for c in np.unique(cnt):
+        rows = np.nonzero(cnt == c)[0]
+        accept_topk_rows(gm2[rows], s2[rows], int(c))
+    same = int((cnt == ocnt).sum())
+    return same, len(cnt) - same
+
+
 def compare_outputs(gpu: np.ndarray, ref: np.ndarray, what: str = "output"):
     """Max-abs and mean-abs bounds between two float arrays of valid rows."""
     err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))

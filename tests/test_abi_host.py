@@ -142,6 +142,51 @@ def test_select_errors(lib):
     assert _select(lib, many, mode=1, win=w) == _lib.BSTA_ERR_SHAPE
 
 
+def test_cumulative_capacity_and_workspace(lib):
+    g = _g(B=2, H=3, D=128, T=16, Y=48, X=80)
+    nt = geometry.num_tiles(16, 48, 80)
+    cum = _lib.SELECT_CUMULATIVE
+    # Row lengths depend on the data: room for every row to keep all tiles.
+    assert lib.attn_select_capacity(ctypes.byref(g), cum, 0, None) == 2 * 3 * nt * nt
+    assert lib.attn_workspace_bytes(ctypes.byref(g), cum) == lib.attn_workspace_bytes(ctypes.byref(g), 0)
+    pre = cum | _lib.SELECT_PREPOOLED
+    assert lib.attn_workspace_bytes(ctypes.byref(g), pre) == lib.attn_workspace_bytes(ctypes.byref(g), 0)
+
+
+def _cum(lib, g, flags=0, tau=0.5, mb=0, rp=FAKE, ci=FAKE, cap=10 ** 12, ws=FAKE, wsb=10 ** 12,
+         q=FAKE, k=FAKE):
+    return lib.attn_select_cumulative(ctypes.byref(g), q, k, flags, tau, mb, None, rp, ci, cap, ws,
+                                      wsb, None)
+
+
+def test_cumulative_errors(lib):
+    g = _g()  # 8 tiles
+    for tau in (0.0, -0.25, 1.5, float("nan")):
+        assert _cum(lib, g, tau=tau) == _lib.BSTA_ERR_SHAPE
+        assert "threshold" in _err(lib)
+    assert _cum(lib, g, mb=-1) == _lib.BSTA_ERR_SHAPE
+    assert _cum(lib, g, flags=7) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _cum(lib, g, rp=None) == _lib.BSTA_ERR_NULL
+    assert _cum(lib, g, ci=None) == _lib.BSTA_ERR_NULL
+    assert _cum(lib, g, q=None) == _lib.BSTA_ERR_NULL
+    assert _cum(lib, g, k=None) == _lib.BSTA_ERR_NULL
+    assert _cum(lib, g, ws=None) == _lib.BSTA_ERR_NULL
+    assert _cum(lib, g, flags=_lib.SELECT_PREPOOLED, q=None, k=None, ws=None) == _lib.BSTA_ERR_NULL
+    assert "workspace" in _err(lib)
+    need = 1 * 2 * 8 * 8
+    assert _cum(lib, g, cap=need - 1) == _lib.BSTA_ERR_CAPACITY
+    wsb = lib.attn_workspace_bytes(ctypes.byref(g), _lib.SELECT_CUMULATIVE)
+    assert _cum(lib, g, wsb=wsb - 1) == _lib.BSTA_ERR_CAPACITY
+    big = _g(T=64, Y=64, X=40)  # 16 * 16 * 10 = 2560 tiles, above one wave's 2048
+    assert _cum(lib, big) == _lib.BSTA_ERR_SHAPE
+    assert "2048" in _err(lib)
+    assert lib.attn_geometry(ctypes.byref(_g(D=96)), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _cum(lib, _g(D=96)) == _lib.BSTA_ERR_UNSUPPORTED
+    # attn_select_blocks does not take this mode (it has no threshold argument).
+    assert _select(lib, g, mode=_lib.SELECT_CUMULATIVE) == _lib.BSTA_ERR_UNSUPPORTED
+    assert "attn_select_cumulative" in _err(lib)
+
+
 def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16, fn="attn_block_sparse_fwd"):
     if scale is None:
         scale = 1.0 / math.sqrt(g.D)

@@ -339,6 +339,145 @@ def test_sta_end_to_end(bsta, name):
     _check_tiled_output(w, r, ref, rlse)
 
 
+# ---------------------------------------------------------------- cumulative threshold
+
+CUM_CASES = [("c1", 0.5, 0), ("ragged_d128", 0.3, 0), ("ragged_d128", 0.9, 2),
+             ("ragged_d64", 0.6, 0), ("smooth_40", 0.2, 0), ("smooth_40", 0.95, 5),
+             ("lowrank_48", 0.5, 3), ("one_token", 0.5, 0), ("dense_all", 1.0, 0)]
+
+
+def _check_cumulative(w, sel, s, tau, mb):
+    gmask = sel.block_mask.cpu().numpy()
+    same, band = H.accept_cumulative_rows(gmask, s, w.D, tau, mb)
+    H.log(f"  rows with the oracle's count {same}, inside the mass band {band}")
+    rp, ci = select.mask_to_csr(gmask.astype(bool))
+    assert np.array_equal(sel.row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(sel.col_idx.cpu().numpy()[:len(ci)], ci)
+    return gmask.astype(bool)
+
+
+@pytest.mark.parametrize("name,tau,mb", CUM_CASES)
+def test_cumulative_select(bsta, name, tau, mb):
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"cumulative {name} threshold {tau} min {mb}")
+    g = _geom(bsta, w)
+    qt, kt = bsta.attn_tile(g, H.to_dev(inp["q"])), bsta.attn_tile(g, H.to_dev(inp["k"]))
+    sel = bsta.attn_select_cumulative(g, qt, kt, tau, mb)
+    _check_cumulative(w, sel, _oracle_scores(w, inp["q"], inp["k"]), tau, mb)
+
+
+@pytest.mark.parametrize("nt", WIDE_NT[:4])
+def test_cumulative_wide_rows(bsta, nt):
+    """Random inputs in each register bucket of the one-wave row kernels."""
+    w = workloads.custom(f"cwide_{nt}", 1, 2, 64, 4, 4, 4 * nt, "topk", 1, seed=41)
+    inp = H.inputs(w)
+    s = _oracle_scores(w, inp["q"], inp["k"])
+    g = _geom(bsta, w)
+    qt, kt = bsta.attn_tile(g, H.to_dev(inp["q"])), bsta.attn_tile(g, H.to_dev(inp["k"]))
+    for tau, mb in ((0.1, 0), (0.5, 7), (0.99, 0)):
+        H.log(f"cumulative wide Nt={nt} threshold {tau} min {mb}")
+        sel = bsta.attn_select_cumulative(g, qt, kt, tau, mb)
+        _check_cumulative(w, sel, s, tau, mb)
+
+
+@pytest.mark.parametrize("nt", [300, 1200])
+def test_cumulative_all_ties(bsta, nt):
+    """Q = 0: every score is 0, p = 1/Nt, and a row keeps tiles 0..c-1 with c
+    the first count whose mass c/Nt reaches the threshold."""
+    import torch
+    w = workloads.custom(f"cties_{nt}", 1, 2, 64, 4, 4, 4 * nt, "topk", 1, seed=42)
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q = torch.zeros((w.B, w.L, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    qt, kt = bsta.attn_tile(g, q), bsta.attn_tile(g, H.to_dev(inp["k"]))
+    for tau in (0.25, 0.5, 0.7):
+        sel = bsta.attn_select_cumulative(g, qt, kt, tau, 0)
+        m = sel.block_mask.cpu().numpy().reshape(-1, nt).astype(bool)
+        c = int(np.ceil(tau * nt - 1e-9))
+        cnt = m.sum(axis=1)
+        assert np.all(np.abs(cnt - c) <= 1), (tau, np.unique(cnt))
+        for r in range(len(m)):
+            assert np.all(m[r, :cnt[r]]) and not np.any(m[r, cnt[r]:])
+
+
+def test_cumulative_small_threshold_equals_topk(bsta):
+    """A threshold below every probability keeps max(1, min_blocks) tiles: the
+    same CSR, bit for bit, as top-k with that k (one selection kernel)."""
+    w = SMALL["smooth_40"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    qt, kt = bsta.attn_tile(g, H.to_dev(inp["q"])), bsta.attn_tile(g, H.to_dev(inp["k"]))
+    for mb in (0, 1, 6):
+        c = bsta.attn_select_cumulative(g, qt, kt, 1e-30, mb)
+        t = bsta.attn_select_blocks(g, qt, kt, bsta.SELECT_TOPK, max(1, mb))
+        n = int(t.row_ptr[-1].item())
+        assert np.array_equal(c.row_ptr.cpu().numpy(), t.row_ptr.cpu().numpy())
+        assert np.array_equal(c.col_idx[:n].cpu().numpy(), t.col_idx[:n].cpu().numpy())
+        assert np.array_equal(c.block_mask.cpu().numpy(), t.block_mask.cpu().numpy())
+
+
+def test_cumulative_prepooled_equals_pooling(bsta):
+    import torch
+    w = SMALL["ragged_d128"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q, k = H.to_dev(inp["q"]), H.to_dev(inp["k"])
+    qt, kt = bsta.attn_tile(g, q), bsta.attn_tile(g, k)
+    a = bsta.attn_select_cumulative(g, qt, kt, 0.6, 1)
+    sel = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, device="cuda")
+    pq, pk = sel.pooled(g)
+    bsta.attn_tile_pool(g, q, pq)
+    bsta.attn_tile_pool(g, k, pk)
+    b = bsta.attn_select_cumulative(g, None, None, 0.6, 1, prepooled=True, out=sel)
+    torch.cuda.synchronize()
+    n = int(a.row_ptr[-1].item())
+    assert np.array_equal(a.row_ptr.cpu().numpy(), b.row_ptr.cpu().numpy())
+    assert np.array_equal(a.col_idx[:n].cpu().numpy(), b.col_idx[:n].cpu().numpy())
+
+
+def test_cumulative_fused_route(bsta):
+    """block_sparse_attention with SELECT_CUMULATIVE (Q and K pooled while
+    tiled, prepooled selection) equals the separate calls bit for bit in
+    deterministic mode."""
+    import torch
+    w = SMALL["smooth_40"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        o = bsta.block_sparse_attention(g, q, k, v, mode=bsta.SELECT_CUMULATIVE, threshold=0.4,
+                                        min_blocks=2)
+        qt, kt, vt = bsta.attn_tile(g, q), bsta.attn_tile(g, k), bsta.attn_tile(g, v)
+        sel = bsta.attn_select_cumulative(g, qt, kt, 0.4, 2)
+        o2 = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+        torch.cuda.synchronize()
+    finally:
+        bsta.attn_set_deterministic(prev)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,tau,mb", [("smooth_40", 0.5, 2), ("ragged_d64", 0.8, 0)])
+def test_cumulative_end_to_end(bsta, name, tau, mb):
+    """Variable-length CSR rows from the cumulative selection feed the
+    attention; the oracle attends under the GPU's (validated) mask."""
+    import torch
+    w = SMALL[name]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = bsta.attn_tile(g, q), bsta.attn_tile(g, k), bsta.attn_tile(g, v)
+    sel = bsta.attn_select_cumulative(g, qt, kt, tau, mb)
+    o = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+    torch.cuda.synchronize()
+    _, tf = _oracle_tiled(w, inp)
+    s = select.scores(select.pool(tf["q"], w.T, w.Y, w.X), select.pool(tf["k"], w.T, w.Y, w.X))
+    gmask = _check_cumulative(w, sel, s, tau, mb)
+    ref, _ = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X)
+    H.compare_outputs(H.bf16_dev_to_f32(o), tiling.untile(ref, w.T, w.Y, w.X))
+
+
 # ---------------------------------------------------------------- attention
 
 def _check_tiled_output(w, r, ref_tiled, ref_lse):
