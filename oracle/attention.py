@@ -10,6 +10,11 @@ pad positions zero, "video_sparse_attn_h3" page, tile()).
 
 Everything is float64.  The log-sum-exp of a valid row is the natural log of
 the softmax denominator of the scaled scores; a padded row has lse = -inf.
+
+The backward pass (gradients of sum(dO * O) with respect to Q, K and V) is
+the chain rule through the same masked softmax; the bsa_attn page notes the
+method targets training, and the video_sparse_attn_h3 page's tile() keeps
+a gradient route through its gather.
 """
 from __future__ import annotations
 
@@ -59,6 +64,65 @@ def block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale=None, rows=None):
         out[b, i * E:i * E + occ[i], h, :] = o
         lse[b, h, i * E:i * E + occ[i]] = l
     return out, lse
+
+
+def tile_attention_backward(q, keys, vals, do, scale: float):
+    """Gradients of sum(do * o) for o = softmax(q keys^T * scale) vals.
+
+    The chain rule through the softmax, written out: with P the softmax
+    probabilities and dP = do vals^T, the score gradient is
+    dS = P * (dP - rowsum(do * o)) (rowsum(do * o) = rowsum(P * dP)), so
+    dq = dS keys * scale, dkeys = dS^T q * scale and dvals = P^T do.
+    Returns (dq, dkeys, dvals).
+    """
+    s = (q @ keys.T) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    o = p @ vals
+    dp = do @ vals.T
+    delta = (do * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)
+    return (ds @ keys) * scale, (ds.T @ q) * scale, p.T @ do
+
+
+def block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X, scale=None):
+    """Gradients of the block-sparse attention of tile-ordered tensors.
+
+    For the loss sum(dot * out) with out = block_sparse_attention(...):
+    query tile i of head h attends over the valid tokens of the key tiles
+    mask[b, h, i] keeps, so its rows receive dq from those keys, and each
+    kept key/value tile receives dk, dv from every query tile that keeps it.
+    Padded slots (query or key) get zero gradient.  Inputs [B, Lpad, H, D];
+    returns float64 (dq, dk, dv) of that shape.
+    """
+    B, lpad, H, D = qt.shape
+    E = geometry.TILE_ELEMS
+    occ = geometry.occupancy(T, Y, X)
+    nt = len(occ)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.zeros((B, lpad, H, D), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nt):
+                sel = np.nonzero(mask[b, h, i])[0]
+                if len(sel) == 0:
+                    continue
+                keys = np.concatenate([kt[b, j * E:j * E + occ[j], h, :] for j in sel]).astype(np.float64)
+                vals = np.concatenate([vt[b, j * E:j * E + occ[j], h, :] for j in sel]).astype(np.float64)
+                rows = slice(i * E, i * E + occ[i])
+                gq, gk, gv = tile_attention_backward(qt[b, rows, h, :].astype(np.float64), keys, vals,
+                                                     dot[b, rows, h, :].astype(np.float64), scale)
+                dq[b, rows, h, :] = gq
+                at = 0
+                for j in sel:
+                    cols = slice(j * E, j * E + occ[j])
+                    dk[b, cols, h, :] += gk[at:at + occ[j]]
+                    dv[b, cols, h, :] += gv[at:at + occ[j]]
+                    at += occ[j]
+    return dq, dk, dv
 
 
 def token_tile_ids(T: int, Y: int, X: int) -> np.ndarray:

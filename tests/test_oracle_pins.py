@@ -485,6 +485,106 @@ def test_single_tile_matches_textbook_and_logsumexp():
         assert np.allclose(lse[0, 0, i * 64:i * 64 + occ[i]], logsumexp(s, axis=1), atol=1e-12)
 
 
+# ---------------------------------------------------------------- backward
+
+def _bwd_case(grid, H=2, D=16, B=1, k=3, seed=0):
+    T, Y, X = grid
+    rng = np.random.default_rng(seed)
+    L = T * Y * X
+    q, kk, v, do = (rng.standard_normal((B, L, H, D)) for _ in range(4))
+    nt = geometry.num_tiles(T, Y, X)
+    s = rng.standard_normal((B, H, nt, nt))
+    mask = select.topk_mask(s, min(k, nt))
+    return q, kk, v, do, mask
+
+
+@pytest.mark.parametrize("grid,k", [((5, 6, 7), 2), ((8, 8, 4), 3), ((3, 9, 5), 1)])
+def test_backward_equals_autograd(grid, k):
+    """torch autograd (float64) through the dense token-masked attention."""
+    T, Y, X = grid
+    q, kk, v, do, mask = _bwd_case(grid, k=k, seed=7)
+    B, L, H, D = q.shape
+    tid = attention.token_tile_ids(T, Y, X)
+    qt_, kt_, vt_ = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, kk, v))
+    out = torch.zeros((B, L, H, D), dtype=torch.float64)
+    outs = []
+    for b in range(B):
+        for h in range(H):
+            tokmask = torch.tensor(np.where(mask[b, h][tid][:, tid], 0.0, -np.inf))
+            sc = qt_[b, :, h] @ kt_[b, :, h].T / math.sqrt(D) + tokmask
+            outs.append(torch.softmax(sc, dim=-1) @ vt_[b, :, h])
+    out = torch.stack(outs).reshape(B, H, L, D).permute(0, 2, 1, 3)
+    (out * torch.tensor(do)).sum().backward()
+    tq, tk, tv, tdo = (tiling.tile(a, T, Y, X) for a in (q, kk, v, do))
+    dq, dk, dv = attention.block_sparse_attention_backward(tq, tk, tv, tdo, mask, T, Y, X)
+    for got, ref in ((dq, qt_.grad), (dk, kt_.grad), (dv, vt_.grad)):
+        assert np.allclose(tiling.untile(got, T, Y, X), ref.numpy(), rtol=1e-10, atol=1e-10)
+    # pad slots receive nothing
+    valid = np.zeros(tq.shape[1], dtype=bool)
+    valid[geometry.token_slots(T, Y, X)] = True
+    for g in (dq, dk, dv):
+        assert np.all(g[:, ~valid] == 0)
+
+
+def test_backward_finite_differences():
+    """Central differences of sum(dO * O) from the oracle's forward."""
+    grid = (5, 4, 6)
+    T, Y, X = grid
+    q, kk, v, do, mask = _bwd_case(grid, D=8, k=2, seed=9)
+    tq, tk, tv, tdo = (tiling.tile(a, T, Y, X) for a in (q, kk, v, do))
+    grads = attention.block_sparse_attention_backward(tq, tk, tv, tdo, mask, T, Y, X)
+    slots = geometry.token_slots(T, Y, X)
+    rng = np.random.default_rng(3)
+
+    def loss(a, b_, c):
+        return float((attention.block_sparse_attention(a, b_, c, mask, T, Y, X)[0] * tdo).sum())
+
+    eps = 1e-6
+    for which in range(3):
+        for _ in range(6):
+            slot = int(rng.choice(slots))
+            h, d = int(rng.integers(2)), int(rng.integers(8))
+            args = [tq.copy(), tk.copy(), tv.copy()]
+            args[which][0, slot, h, d] += eps
+            up = loss(*args)
+            args[which][0, slot, h, d] -= 2 * eps
+            dn = loss(*args)
+            fd = (up - dn) / (2 * eps)
+            assert abs(fd - grads[which][0, slot, h, d]) <= 1e-6 * (1 + abs(fd)), (which, slot, h, d)
+
+
+def test_backward_closed_forms():
+    grid = (4, 8, 8)
+    T, Y, X = grid
+    q, kk, v, do, mask = _bwd_case(grid, k=3, seed=5)
+    tq, tk, tv, tdo = (tiling.tile(a, T, Y, X) for a in (q, kk, v, do))
+    # dO = 0: no gradient anywhere.
+    z = attention.block_sparse_attention_backward(tq, tk, tv, np.zeros_like(tdo), mask, T, Y, X)
+    assert all(np.all(g == 0) for g in z)
+    # Equal value rows make the output independent of the scores: dQ = dK = 0,
+    # and every query's dO is shared out over its keys with weights summing
+    # to one, so dV sums (over keys) to dO summed over the queries.
+    vc = np.broadcast_to(np.arange(16.0), tv.shape).copy()
+    dq, dk, dv = attention.block_sparse_attention_backward(tq, tk, vc, tdo, mask, T, Y, X)
+    assert np.allclose(dq, 0, atol=1e-12) and np.allclose(dk, 0, atol=1e-12)
+    assert np.allclose(dv.sum(axis=1), _dv_total(tdo, mask, T, Y, X), atol=1e-9)
+
+
+def _dv_total(tdo, mask, T, Y, X):
+    """Sum over queries of dO, each query tile counted once per (row with a
+    non-empty selection): [B, H, D]."""
+    E = geometry.TILE_ELEMS
+    occ = geometry.occupancy(T, Y, X)
+    B, _, H, D = tdo.shape
+    tot = np.zeros((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            for i in range(len(occ)):
+                if mask[b, h, i].any():
+                    tot[b, h] += tdo[b, i * E:i * E + occ[i], h].sum(axis=0)
+    return tot
+
+
 def test_sta_full_window_equals_dense():
     T, Y, X = 8, 8, 12
     q, kk, v = _random_case((T, Y, X), H=2, D=8, B=2, seed=6)
