@@ -290,6 +290,38 @@ def main():
         print(f"[bench] cumulative selection {cum}", file=sys.stderr, flush=True)
         del sel_c
 
+    # The backward (attn_block_sparse_bwd) on the step's selection, with a
+    # seeded synthetic output gradient; not part of the step.  Its
+    # algorithmic work is five products per selected pair (S, dP, dV, dQ,
+    # dK), 2.5 times the forward's two.
+    bwd = None
+    if nt <= 4096:
+        _, lse_b = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot,
+                                              want_lse=True)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        dot_b = torch.randn((w.B, lpad, w.H, w.D), generator=gen, device=dev).to(torch.bfloat16)
+        grads = tuple(torch.empty_like(qt) for _ in range(3))
+        bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot_b, lse_b, sel.row_ptr, sel.col_idx,
+                                   out=grads)
+        per_b = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot_b, lse_b, sel.row_ptr, sel.col_idx,
+                                       out=grads)
+            e1.record()
+            torch.cuda.synchronize()
+            per_b.append(e0.elapsed_time(e1))
+        b_ms = float(np.median(per_b))
+        b_flop = 2.5 * attention_flop(w, nnz)
+        bwd = {"ms": b_ms, "tflops": b_flop / (b_ms * 1e-3) / 1e12,
+               "frac_mfma_peak": b_flop / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "algorithmic_flop": b_flop, "calls": 5, "stat": "median",
+               "note": "attn_block_sparse_bwd (delta, CSR transpose, dQ, dK/dV) on the step's "
+                       "selection; not in the step"}
+        print(f"[bench] backward {bwd}", file=sys.stderr, flush=True)
+        del grads, dot_b, lse_b
+
     flop = attention_flop(w, nnz)
     prof = measured_attn() if args.workload == "c3" and not args.deterministic else None
     dense_flop = 4.0 * w.D * w.B * w.H * float(w.L) ** 2
@@ -355,6 +387,7 @@ def main():
             "untile": {"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
                        "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
             "select_cumulative": cum,
+            "attn_bwd": bwd,
         },
     }
     if not args.no_cpu_baseline:

@@ -25,7 +25,7 @@ from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, 
 
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
-    "attn_select_cumulative", "attn_tile",
+    "attn_select_cumulative", "attn_block_sparse_bwd", "attn_tile",
     "attn_tile_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
     "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
@@ -269,6 +269,38 @@ def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_i
         _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(out),
         _ptr(lse), _stream()))
     return (out, lse) if want_lse or lse is not None else out
+
+
+def attn_block_sparse_bwd(g: Geometry, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                          col_idx, softmax_scale: Optional[float] = None, out=None):
+    """Gradients (dq, dk, dv), tiled bf16 [B, Lpad, H, D], of sum(do * o) for
+    o = attn_block_sparse_fwd(...) (tiled output) with its lse.  ``out`` may
+    give the three output tensors."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    for name, t in (("q_tiled", q_tiled), ("k_tiled", k_tiled), ("v_tiled", v_tiled),
+                    ("o_tiled", o_tiled), ("do_tiled", do_tiled)):
+        _expect(t, (g.B, lpad, g.H, g.D), torch.bfloat16, name)
+    _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
+    _expect(row_ptr, (g.B * g.H * nt + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
+        raise ValueError("col_idx: expected contiguous int32")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(g.D)
+    if out is None:
+        out = tuple(torch.empty_like(q_tiled) for _ in range(3))
+    for name, t in zip(("dq", "dk", "dv"), out):
+        _expect(t, (g.B, lpad, g.H, g.D), torch.bfloat16, name)
+    lib = _lib.load()
+    wsb = lib.attn_bwd_workspace_bytes(ctypes.byref(g.c), col_idx.numel())
+    _lib.check(wsb)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q_tiled.device)
+    _lib.check(lib.attn_block_sparse_bwd(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(o_tiled),
+        _ptr(do_tiled), _ptr(lse), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+        float(softmax_scale), 0, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws), wsb,
+        _stream()))
+    return out
 
 
 def attn_set_deterministic(enable: bool) -> bool:

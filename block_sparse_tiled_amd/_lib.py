@@ -30,7 +30,7 @@ EXPORTS = (
     "attn_geometry", "attn_tile", "attn_tile_pool", "attn_untile", "attn_select_capacity",
     "attn_workspace_bytes", "attn_select_blocks", "attn_select_cumulative",
     "attn_block_sparse_fwd",
-    "attn_block_sparse_fwd_raster",
+    "attn_block_sparse_fwd_raster", "attn_bwd_workspace_bytes", "attn_block_sparse_bwd",
     "attn_status_string", "attn_last_error", "attn_set_deterministic",
 )
 
@@ -73,6 +73,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "attn_select_cumulative": (i32, [G, P, P, i32, ctypes.c_float, i32, P, P, P, i64, P, i64, P]),
         "attn_block_sparse_fwd": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P]),
         "attn_block_sparse_fwd_raster": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P]),
+        "attn_bwd_workspace_bytes": (i64, [G, i64]),
+        "attn_block_sparse_bwd": (i32, [G, P, P, P, P, P, P, P, P, i64, ctypes.c_float, i32, P, P, P,
+                                        P, i64, P]),
         "attn_status_string": (ctypes.c_char_p, [i32]),
         "attn_last_error": (ctypes.c_char_p, []),
         "attn_set_deterministic": (i32, [i32]),

@@ -32,6 +32,12 @@ hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32
 hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, const float* s,
                               uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t stream);
+hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                           float scale, void* dq, void* dk, void* dv, float* delta,
+                           int32_t* col_start, int32_t* col_cnt, int32_t* row_idx,
+                           hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
                            float scale, void* o, float* lse, bool rotate, bool raster,
@@ -53,6 +59,9 @@ constexpr int kMaxTopkTiles = 12288;
 // Largest tile count the cumulative-threshold selection accepts (one wave
 // holds a row in registers, 32 scores per lane).
 constexpr int kMaxCumulativeTiles = 2048;
+// Largest tile count the backward accepts (its CSR transpose keeps three
+// ints per tile in LDS).
+constexpr int kMaxBwdTiles = 4096;
 // Largest grid side (tile coordinates travel as int16 in window mode).
 constexpr int kMaxDim = 1 << 15;
 
@@ -178,6 +187,36 @@ int64_t workspace_of(const Geo& g, int32_t mode_in) {
 }  // namespace
 
 namespace {
+// Backward workspace: delta fp32 [B*H*Lpad], col_start and col_cnt int32
+// [B*H*Nt] each, row_idx int32 [col_len]; every part 256-byte aligned.
+struct BwdLayout {
+    int64_t delta, col_start, col_cnt, row_idx, total;
+};
+
+BwdLayout bwd_layout(const Geo& g, int64_t col_len) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    BwdLayout l;
+    l.delta = 0;
+    l.col_start = up(l.delta + (int64_t)g.B * g.H * g.Lpad * 4);
+    l.col_cnt = up(l.col_start + (int64_t)g.B * g.H * g.Nt * 4);
+    l.row_idx = up(l.col_cnt + (int64_t)g.B * g.H * g.Nt * 4);
+    l.total = up(l.row_idx + (col_len > 0 ? col_len : 0) * 4);
+    return l;
+}
+
+int32_t check_scale(const Geo& g, float softmax_scale, int32_t causal) {
+    if (causal != 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "causal=%d: block-sparse attention is bidirectional only",
+                    causal);
+    const double expected = 1.0 / sqrt((double)g.D);
+    const double diff = fabs((double)softmax_scale - expected);
+    const double tol = fmax(1e-4 * fmax(fabs((double)softmax_scale), expected), 1e-5);
+    if (!(diff <= tol))
+        return fail(BSTA_ERR_UNSUPPORTED, "softmax_scale %g must be 1/sqrt(D) = %g",
+                    (double)softmax_scale, expected);
+    return BSTA_OK;
+}
+
 int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_tiled,
                          const void* k_tiled, const void* v_tiled, const int32_t* row_ptr,
                          const int32_t* col_idx, int64_t col_len, float softmax_scale,
@@ -188,15 +227,8 @@ int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_t
     if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o == nullptr ||
         row_ptr == nullptr || col_idx == nullptr)
         return fail(BSTA_ERR_NULL, "%s: NULL tensor or index pointer", name);
-    if (causal != 0)
-        return fail(BSTA_ERR_UNSUPPORTED, "causal=%d: block-sparse attention is bidirectional only",
-                    causal);
-    const double expected = 1.0 / sqrt((double)g.D);
-    const double diff = fabs((double)softmax_scale - expected);
-    const double tol = fmax(1e-4 * fmax(fabs((double)softmax_scale), expected), 1e-5);
-    if (!(diff <= tol))
-        return fail(BSTA_ERR_UNSUPPORTED, "softmax_scale %g must be 1/sqrt(D) = %g",
-                    (double)softmax_scale, expected);
+    st = check_scale(g, softmax_scale, causal);
+    if (st != BSTA_OK) return st;
     if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
     return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                                             col_len, softmax_scale, o, lse,
@@ -382,6 +414,51 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* gin, const void* q_tiled,
                                      float* lse, void* stream) {
     return block_sparse_fwd("attn_block_sparse_fwd_raster", gin, q_tiled, k_tiled, v_tiled,
                             row_ptr, col_idx, col_len, softmax_scale, causal, o, lse, true, stream);
+}
+
+int64_t attn_bwd_workspace_bytes(const bsta_geom* gin, int64_t col_len) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
+    ok();
+    return bwd_layout(g, col_len).total;
+}
+
+int32_t attn_block_sparse_bwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
+                              const void* v_tiled, const void* o_tiled, const void* do_tiled,
+                              const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_len, float softmax_scale, int32_t causal,
+                              void* dq_tiled, void* dk_tiled, void* dv_tiled, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o_tiled == nullptr ||
+        do_tiled == nullptr || lse == nullptr || row_ptr == nullptr || col_idx == nullptr ||
+        dq_tiled == nullptr || dk_tiled == nullptr || dv_tiled == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_block_sparse_bwd: NULL tensor, lse or index pointer");
+    st = check_scale(g, softmax_scale, causal);
+    if (st != BSTA_OK) return st;
+    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
+    if (col_len > 0x7fffffffLL)
+        return fail(BSTA_ERR_SHAPE, "col_len %lld overflows int32 offsets", (long long)col_len);
+    if (g.Nt > kMaxBwdTiles)
+        return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
+                    g.Nt);
+    const BwdLayout l = bwd_layout(g, col_len);
+    if (workspace == nullptr) return fail(BSTA_ERR_NULL, "attn_block_sparse_bwd: NULL workspace");
+    if (workspace_bytes < l.total)
+        return fail(BSTA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                    (long long)workspace_bytes, (long long)l.total);
+    char* ws = (char*)workspace;
+    return hip_status(
+            bsta::launch_attn_bwd(g, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                                  col_idx, col_len, softmax_scale, dq_tiled, dk_tiled, dv_tiled,
+                                  (float*)(ws + l.delta), (int32_t*)(ws + l.col_start),
+                                  (int32_t*)(ws + l.col_cnt), (int32_t*)(ws + l.row_idx),
+                                  (hipStream_t)stream),
+            "attn_block_sparse_bwd");
 }
 
 int32_t attn_set_deterministic(int32_t enable) {

@@ -17,6 +17,7 @@
  * BSTA_SELECT_PREPOOLED and skips its own pooling pass.  Likewise
  * attn_block_sparse_fwd_raster writes the output in raster order and
  * replaces attn_block_sparse_fwd followed by attn_untile.
+ * attn_block_sparse_bwd gives the gradients of the forward for training.
  *
  * Conventions shared by every call:
  *   - Tensors are bfloat16, contiguous, in the layout [B, L, H, D] that the
@@ -265,6 +266,49 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
                                      const int32_t* row_ptr, const int32_t* col_idx,
                                      int64_t col_len, float softmax_scale, int32_t causal, void* o,
                                      float* lse, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes (host only): bytes of device workspace
+ * attn_block_sparse_bwd needs for a CSR of col_len entries (per-query
+ * rowsum(dO*O) and the CSR's transpose); a negative status on bad arguments.
+ */
+int64_t attn_bwd_workspace_bytes(const bsta_geom* g, int64_t col_len);
+
+/*
+ * attn_block_sparse_bwd: gradients of the block-sparse attention of
+ * attn_block_sparse_fwd for training (the "bsa_attn" page's method targets
+ * training; the "video_sparse_attn_h3" page keeps a gradient route through
+ * its tiling).  For the loss sum(dO * O) over the tiled output O:
+ *   dS = P * (dO V^T - rowsum(dO * O)),  dQ = dS K * softmax_scale,
+ *   dK = dS^T Q * softmax_scale,  dV = P^T dO,
+ * with P the softmax probabilities of each query row over the valid keys of
+ * its CSR row's tiles, recomputed from the forward's lse.
+ *   q_tiled, k_tiled, v_tiled [in] bf16 [B, Lpad, H, D], as given to the
+ *            forward
+ *   o_tiled  [in] bf16 [B, Lpad, H, D], the forward's tiled output
+ *   do_tiled [in] bf16 [B, Lpad, H, D], gradient of the loss w.r.t. O (pad
+ *            rows are ignored)
+ *   lse      [in] fp32 [B, H, Lpad], the forward's lse
+ *   row_ptr, col_idx, col_len  the forward's CSR; each row must list
+ *            distinct tile ids (every selection here does).  Ranges are
+ *            clamped and out-of-range ids skipped as in the forward; a
+ *            repeated id gives undefined gradients but no access outside
+ *            the arrays.
+ *   softmax_scale, causal  as the forward (1/sqrt(D), 0)
+ *   dq_tiled, dk_tiled, dv_tiled [out] bf16 [B, Lpad, H, D]; pad rows and
+ *            key tiles that no row selects are written as +0.0
+ *   workspace [scratch, >= attn_bwd_workspace_bytes(g, col_len)]
+ * Requires Nt <= 4096 (BSTA_ERR_SHAPE otherwise).  Gradients accumulate in
+ * fp32, key tiles in CSR row order for dQ and query tiles in ascending
+ * order for dK and dV, so equal inputs give bitwise equal gradients; P and
+ * dS are rounded to bf16 for the second products.
+ */
+int32_t attn_block_sparse_bwd(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
+                              const void* v_tiled, const void* o_tiled, const void* do_tiled,
+                              const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_len, float softmax_scale, int32_t causal,
+                              void* dq_tiled, void* dk_tiled, void* dv_tiled, void* workspace,
+                              int64_t workspace_bytes, void* stream);
 
 /*
  * attn_set_deterministic (host only, no HIP call): process-wide key order of

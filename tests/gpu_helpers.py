@@ -116,6 +116,58 @@ def accept_cumulative_rows(gpu_mask: np.ndarray, oracle_scores: np.ndarray, D: i
     return same, len(cnt) - same
 
 
+def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X):
+    """Per-element error bounds for the GPU gradients (float64, tiled shapes).
+
+    The GPU rounds P and dS to bf16 (unit roundoff 2^-9) before the second
+    products, computes rowsum(dO*O) from the bf16 output, and rounds each
+    gradient once to bf16.  Summing the absolute values of the terms gives
+    |err dV| <= u * sum_q P |dO| + u |dV|,
+    |err dS| <= u * (|dS| + P * sum_d |dO O|),
+    |err dQ| <= scale * sum_keys |err dS| |K| + u |dQ|, and the same for dK
+    over the queries with |Q|.  The bound uses u = 2^-8 (twice bf16's unit
+    roundoff) and returns (bound_dq, bound_dk, bound_dv).
+    """
+    from oracle import geometry as ogeo
+    u = 2.0 ** -8
+    B, lpad, Hh, D = qt.shape
+    E = ogeo.TILE_ELEMS
+    occ = ogeo.occupancy(T, Y, X)
+    scale = 1.0 / np.sqrt(D)
+    bq, bk, bv = (np.zeros((B, lpad, Hh, D)) for _ in range(3))
+    gq, gk, gv = (np.zeros((B, lpad, Hh, D)) for _ in range(3))
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(len(occ)):
+                sel = np.nonzero(mask[b, h, i])[0]
+                if len(sel) == 0:
+                    continue
+                rows = slice(i * E, i * E + occ[i])
+                q = qt[b, rows, h].astype(np.float64)
+                do = dot[b, rows, h].astype(np.float64)
+                keys = np.concatenate([kt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
+                vals = np.concatenate([vt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
+                s_ = q @ keys.T * scale
+                p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ vals
+                ds = p * (do @ vals.T - (do * o).sum(axis=1, keepdims=True))
+                eds = u * (np.abs(ds) + p * np.abs(do * o).sum(axis=1, keepdims=True))
+                bq[b, rows, h] = scale * eds @ np.abs(keys)
+                gq[b, rows, h] = scale * ds @ keys
+                cbk, cbv = scale * eds.T @ np.abs(q), u * p.T @ np.abs(do)
+                cgk, cgv = scale * ds.T @ q, p.T @ do
+                at = 0
+                for j in sel:
+                    cols = slice(j * E, j * E + occ[j])
+                    bk[b, cols, h] += cbk[at:at + occ[j]]
+                    bv[b, cols, h] += cbv[at:at + occ[j]]
+                    gk[b, cols, h] += cgk[at:at + occ[j]]
+                    gv[b, cols, h] += cgv[at:at + occ[j]]
+                    at += occ[j]
+    return bq + u * np.abs(gq), bk + u * np.abs(gk), bv + u * np.abs(gv)
+
+
 def compare_outputs(gpu: np.ndarray, ref: np.ndarray, what: str = "output"):
     """Max-abs and mean-abs bounds between two float arrays of valid rows."""
     err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))

@@ -187,6 +187,38 @@ def test_cumulative_errors(lib):
     assert "attn_select_cumulative" in _err(lib)
 
 
+def _bwd(lib, g, scale=None, causal=0, ptrs=None, col_len=16, ws=FAKE, wsb=10 ** 12):
+    if scale is None:
+        scale = 1.0 / math.sqrt(g.D)
+    p = [FAKE] * 11 if ptrs is None else ptrs
+    return lib.attn_block_sparse_bwd(ctypes.byref(g), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                                     col_len, scale, causal, p[8], p[9], p[10], ws, wsb, None)
+
+
+def test_bwd_workspace_and_errors(lib):
+    g = _g(B=2, H=3, D=128, T=16, Y=48, X=80)
+    nt = geometry.num_tiles(16, 48, 80)
+    lpad = 64 * nt
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = up(up(up(2 * 3 * lpad * 4) + 2 * 3 * nt * 4) + 2 * 3 * nt * 4) + up(1000 * 4)
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(g), 1000) == want
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(g), -1) == _lib.BSTA_ERR_SHAPE
+    s = _g()
+    for n in range(11):
+        ptrs = [FAKE] * 11
+        ptrs[n] = None
+        assert _bwd(lib, s, ptrs=ptrs) == _lib.BSTA_ERR_NULL, n
+    assert _bwd(lib, s, ws=None) == _lib.BSTA_ERR_NULL
+    assert _bwd(lib, s, causal=1) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd(lib, s, scale=0.5) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd(lib, s, col_len=-1) == _lib.BSTA_ERR_SHAPE
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(s), 16)
+    assert _bwd(lib, s, wsb=need - 1) == _lib.BSTA_ERR_CAPACITY
+    big = _g(T=64, Y=64, X=68)  # 16 * 16 * 17 = 4352 tiles, above 4096
+    assert _bwd(lib, big) == _lib.BSTA_ERR_SHAPE
+    assert "4096" in _err(lib)
+
+
 def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16, fn="attn_block_sparse_fwd"):
     if scale is None:
         scale = 1.0 / math.sqrt(g.D)

@@ -478,6 +478,144 @@ def test_cumulative_end_to_end(bsta, name, tau, mb):
     H.compare_outputs(H.bf16_dev_to_f32(o), tiling.untile(ref, w.T, w.Y, w.X))
 
 
+# ---------------------------------------------------------------- backward
+
+def _run_bwd(m, w, inp, seed=99):
+    """Forward (tiled output and lse) and backward on the GPU, dO seeded."""
+    import torch
+    g = _geom(m, w)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = m.attn_tile(g, q), m.attn_tile(g, k), m.attn_tile(g, v)
+    mode = m.SELECT_STA if w.mode == "sta" else m.SELECT_TOPK
+    sel = m.attn_select_blocks(g, qt, kt, mode, w.topk, inp.get("windows_list"))
+    ot, lse = m.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, want_lse=True)
+    rng = np.random.default_rng(seed)
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    dot = m.attn_tile(g, H.to_dev(do_bits))
+    grads = m.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot, lse, sel.row_ptr, sel.col_idx)
+    torch.cuda.synchronize()
+    return dict(g=g, qt=qt, kt=kt, vt=vt, ot=ot, lse=lse, dot=dot, sel=sel, grads=grads,
+                do_bits=do_bits)
+
+
+def _check_grads(w, grads, tf, dtf, mask, heads=None):
+    """GPU gradients against the oracle under the per-element bound; pad
+    slots exactly zero.  `heads` restricts the check to some heads."""
+    hs = list(range(w.H)) if heads is None else heads
+    sub = lambda a: a[:, :, hs]  # noqa: E731
+    args = [sub(tf["q"]), sub(tf["k"]), sub(tf["v"]), sub(dtf)]
+    ref = oatt.block_sparse_attention_backward(*args, mask[:, hs], w.T, w.Y, w.X)
+    H.log("  oracle gradients done")
+    bnd = H.backward_error_bounds(*args, mask[:, hs], w.T, w.Y, w.X)
+    H.log("  error bounds done")
+    valid = np.zeros(ref[0].shape[1], dtype=bool)
+    valid[geometry.token_slots(w.T, w.Y, w.X)] = True
+    for nm, gt, rf, bd in zip(("dq", "dk", "dv"), grads, ref, bnd):
+        bits = H.from_dev(gt)[:, :, hs]
+        got = workloads.bf16_to_f32(bits).astype(np.float64)
+        err = np.abs(got[:, valid] - rf[:, valid])
+        ratio = float((err / (bd[:, valid] + 1e-6)).max())
+        H.log(f"  {nm}: max err {err.max():.3g}, max err/bound {ratio:.3f}")
+        assert np.all(err <= bd[:, valid] + 1e-6), f"{nm}: error above its bound (ratio {ratio:.3f})"
+        assert np.all(bits[:, ~valid] == 0), f"{nm}: pad slots must be +0.0"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_backward(bsta, name):
+    w = SMALL[name]
+    inp = H.inputs(w)
+    H.log(f"backward {name}")
+    r = _run_bwd(bsta, w, inp)
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(r["do_bits"], w.T, w.Y, w.X))
+    _check_grads(w, r["grads"], tf, dtf, r["sel"].block_mask.cpu().numpy().astype(bool))
+
+
+@pytest.mark.parametrize("name", sorted(STA_SMALL))
+def test_backward_sta(bsta, name):
+    w, win = STA_SMALL[name]
+    inp = dict(H.inputs(w), windows_list=win)
+    H.log(f"backward {name}")
+    r = _run_bwd(bsta, w, inp)
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(r["do_bits"], w.T, w.Y, w.X))
+    _check_grads(w, r["grads"], tf, dtf, select.sta_mask(w.T, w.Y, w.X, np.array(win), w.B))
+
+
+def test_backward_deterministic(bsta):
+    """Fixed summation orders: two calls give bitwise equal gradients."""
+    import torch
+    w = SMALL["smooth_40"]
+    r = _run_bwd(bsta, w, H.inputs(w))
+    again = bsta.attn_block_sparse_bwd(r["g"], r["qt"], r["kt"], r["vt"], r["ot"], r["dot"], r["lse"],
+                                       r["sel"].row_ptr, r["sel"].col_idx)
+    torch.cuda.synchronize()
+    for a, b in zip(r["grads"], again):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_backward_unselected_tiles_and_bad_ids(bsta):
+    """Key tiles no row selects get zero dK and dV; empty rows get zero dQ;
+    out-of-range ids are skipped as in the forward."""
+    import torch
+    w = SMALL["ragged_d64"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    nt, lpad = bsta.attn_geometry(g)
+    rows = w.B * w.H * nt
+    rng = np.random.default_rng(8)
+    lists = []
+    for r_ in range(rows):
+        if r_ % 5 == 0:
+            lists.append([])                                   # empty row
+        else:
+            ids = sorted(rng.choice(nt - 2, size=3, replace=False).tolist())  # tiles nt-2, nt-1 never used
+            if r_ % 7 == 0:
+                ids = ids + [nt + 5, -1]                       # out of range: skipped
+            lists.append(ids)
+    rp = np.zeros(rows + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([len(x) for x in lists])
+    ci = np.array([j for x in lists for j in x], dtype=np.int32)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = bsta.attn_tile(g, q), bsta.attn_tile(g, k), bsta.attn_tile(g, v)
+    rpd, cid = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    ot, lse = bsta.attn_block_sparse_fwd(g, qt, kt, vt, rpd, cid, want_lse=True)
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    dot = bsta.attn_tile(g, H.to_dev(do_bits))
+    grads = bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot, lse, rpd, cid)
+    torch.cuda.synchronize()
+    mask = np.zeros((w.B, w.H, nt, nt), dtype=bool)
+    for r_, ids in enumerate(lists):
+        b, rest = divmod(r_, w.H * nt)
+        h, i = divmod(rest, nt)
+        for j in ids:
+            if 0 <= j < nt:
+                mask[b, h, i, j] = True
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits, w.T, w.Y, w.X))
+    _check_grads(w, grads, tf, dtf, mask)
+    dk = H.from_dev(grads[1])
+    assert np.all(dk[:, (nt - 2) * 64:] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_backward_full_size_c3_heads(bsta):
+    """The 40-head 1200-tile top-120 workload at full size; every gradient
+    of one head against the oracle (the heads are independent)."""
+    w = workloads.WORKLOADS["c3"]
+    inp = H.inputs(w)
+    H.log("backward c3 full size")
+    r = _run_bwd(bsta, w, inp)
+    heads = [w.H - 1]
+    tf = {n: workloads.bf16_to_f32(tiling.tile(inp[n][:, :, heads], w.T, w.Y, w.X))
+          for n in ("q", "k", "v")}
+    dtf = workloads.bf16_to_f32(tiling.tile(r["do_bits"][:, :, heads], w.T, w.Y, w.X))
+    mask = r["sel"].block_mask.cpu().numpy().astype(bool)[:, heads]
+    grads = tuple(t[:, :, heads] for t in r["grads"])
+    wsub = workloads.custom("c3_heads", w.B, len(heads), w.D, w.T, w.Y, w.X, "topk", w.topk)
+    _check_grads(wsub, grads, tf, dtf, mask)
+
+
 # ---------------------------------------------------------------- attention
 
 def _check_tiled_output(w, r, ref_tiled, ref_lse):
