@@ -285,7 +285,7 @@ def main():
                "selected_tile_pairs": nnz_c, "density": nnz_c / float(w.B * w.H * nt * nt),
                "attn_ms": ca_ms,
                "attn_tflops": attention_flop(w, nnz_c) / (ca_ms * 1e-3) / 1e12,
-               "note": "scores + cumulative-threshold counts + row scan + selection (prepooled); "
+               "note": "scores + cumulative-threshold counts and ids + row scan + compaction (prepooled); "
                        "attention over its rows; not in the step"}
         print(f"[bench] cumulative selection {cum}", file=sys.stderr, flush=True)
         del sel_c

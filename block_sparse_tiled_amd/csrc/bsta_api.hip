@@ -29,7 +29,7 @@ hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32
                        int32_t* col_idx, hipStream_t stream);
 hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32_t* row_ptr,
                       int32_t* col_idx, hipStream_t stream);
-hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, const float* s,
+hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, float* s,
                               uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t stream);
 hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v,

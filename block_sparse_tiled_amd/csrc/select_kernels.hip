@@ -246,16 +246,11 @@ __global__ __launch_bounds__(256) void topk_kernel(
 // walking c upward and ranking lanes by mbcnt visits j in increasing order,
 // so the same ballots give the tie ranks and the ascending CSR positions.
 // Writes the k kept ids to out[0, k) and the row's mask (if any).
+// The k-th largest key of a row held as key[c] = lane's score j = 64c + l
+// (0 for padding): returns it, and in *take_eq how many keys equal to it
+// are kept (the lowest-index ones) so that exactly k are kept.
 template <int C>
-__device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ srow,
-                                       uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
-                                       int lane) {
-    uint32_t key[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int j = c * 64 + lane;
-        key[c] = j < Nt ? score_key(srow[j]) : 0u;
-    }
+__device__ inline uint32_t kth_key(const uint32_t (&key)[C], int Nt, int k, int lane, int* take_eq) {
     // Padding slots hold key 0 and every candidate below is >= 1, so they
     // never count; a real key 0 is handled by the explicit validity test in
     // the final pass.
@@ -273,7 +268,19 @@ __device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ 
         const bool valid = c * 64 + lane < Nt;
         above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key[c] > thr));
     }
-    const int take_eq = k - above;
+    *take_eq = k - above;
+    return thr;
+}
+
+// Writes the kept ids of a row (keys above thr, and the first take_eq keys
+// equal to it in j order) to out[0, ...) in ascending j, and the row's mask
+// (if any).  With j = 64c + l, walking c upward and ranking lanes by mbcnt
+// visits j in increasing order, so the same ballots give the tie ranks and
+// the output positions.  Returns the number written.
+template <int C>
+__device__ inline int write_kept(const uint32_t (&key)[C], int Nt, uint32_t thr, int take_eq,
+                                 int limit, uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
+                                 int lane) {
     int base = 0, eq_base = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -289,9 +296,31 @@ __device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ 
         const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
         base += __builtin_popcountll(sm);
-        if (sel && pos < k) out[pos] = j;
+        if (sel && pos < limit) out[pos] = j;
         if (mrow && valid) mrow[j] = sel;
     }
+    return base;
+}
+
+// One wave per CSR row, for rows of at most 64*C scores: lane l holds
+// scores j = 64c + l, c < C, in registers (coalesced loads, no LDS, no
+// barriers).  The k-th largest key is found bit by bit from the top: a bit
+// is kept when at least k keys are at or above the candidate (one ballot and
+// popcount per register).  Then keys above it are kept, and of the keys
+// equal to it the first k - (count above) in j order.
+template <int C>
+__device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ srow,
+                                       uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
+                                       int lane) {
+    uint32_t key[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * 64 + lane;
+        key[c] = j < Nt ? score_key(srow[j]) : 0u;
+    }
+    int take_eq;
+    const uint32_t thr = kth_key<C>(key, Nt, k, lane, &take_eq);
+    write_kept<C>(key, Nt, thr, take_eq, k, mrow, out, lane);
 }
 
 // Top-k: every row keeps k tiles; CSR row r starts at r*k.
@@ -318,8 +347,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(
 // descending score order (ties to the lower index), a row keeps the
 // shortest prefix whose mass reaches threshold * sum_j p_j, and at least
 // min(min_blocks, Nt) tiles.  Every such row is a top-c row of the same
-// ranking, so the ids are written by select_row_wave with c = the row's
-// count.
+// ranking; its ids are written by the routine top-k uses (write_kept).
 
 // Sum over the wave, taken from lane 0 so that every lane sees the same
 // value (the butterfly gives each lane its own rounding order).
@@ -335,7 +363,9 @@ __device__ inline float wave_max_uniform(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
-// One wave per CSR row: counts[row] = tiles kept.  p is fp32 exp2 of the
+// One wave per CSR row: counts[row] = tiles kept, and the kept ids, in
+// ascending order, written over the row's own scores (read into registers
+// first) for compact_rows_kernel to move into place.  p is fp32 exp2 of the
 // scaled score minus the row max (the max tile has p = 1, so the total is at
 // least 1).  The kept prefix ends at the largest key x whose tiles at or
 // above x hold at least threshold * total, found bit by bit from the top as
@@ -343,11 +373,12 @@ __device__ inline float wave_max_uniform(float v) {
 // summation tree, and adding non-negative terms is monotone in every term,
 // so the mass is non-increasing in x and the search is exact on these fp32
 // values.  Of the tiles tied at x (equal scores, equal p), the lowest-index
-// ones are added one at a time until the mass is reached.
+// ones are added one at a time until the mass is reached.  A row raised to
+// the minimum count keeps the top-kmin set instead (kth_key).
 template <int C>
 __global__ __launch_bounds__(256) void cumulative_count_kernel(
-        int Nt, int64_t rows, const float* __restrict__ s, float scale_log2, float threshold,
-        int kmin, int32_t* __restrict__ counts) {
+        int Nt, int64_t rows, float* __restrict__ s, float scale_log2, float threshold,
+        int kmin, uint8_t* __restrict__ mask, int32_t* __restrict__ counts) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // wave-uniform
@@ -401,52 +432,66 @@ __global__ __launch_bounds__(256) void cumulative_count_kernel(
     }
     if (take == 0 && eq > 0) take = 1;
     int cnt = above + take;
-    cnt = cnt > kmin ? cnt : kmin;
-    cnt = cnt < Nt ? cnt : Nt;
+    if (cnt < kmin) {  // wave-uniform
+        cnt = kmin < Nt ? kmin : Nt;
+        thr = kth_key<C>(key, Nt, cnt, lane, &take);
+    }
+    write_kept<C>(key, Nt, thr, take, Nt, mask ? mask + row * Nt : nullptr, (int32_t*)(s + row * Nt),
+                  lane);
     if (lane == 0) counts[row] = cnt;
 }
 
 // In-place scan of row counts into CSR offsets: on entry row_ptr[r + 1]
 // holds the count of row r; on exit row_ptr[r] is the start of row r and
-// row_ptr[rows] the total.  One workgroup of 1024 threads, each over a
-// contiguous run of rows.
+// row_ptr[rows] the total.  One workgroup of 1024 threads over chunks of
+// 8192 rows, eight consecutive rows per thread (independent loads), a
+// workgroup scan of the per-thread sums, and a carry between chunks.
 __global__ __launch_bounds__(1024) void scan_counts_kernel(int64_t rows,
                                                            int32_t* __restrict__ row_ptr) {
-    __shared__ int64_t part[1024];
-    const int64_t per = (rows + 1023) / 1024;
-    const int64_t r0 = (int64_t)threadIdx.x * per;
-    const int64_t r1 = r0 + per < rows ? r0 + per : rows;
-    int64_t sum = 0;
-    for (int64_t r = r0; r < r1; ++r) sum += row_ptr[r + 1];
-    part[threadIdx.x] = sum;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums.
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int64_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    constexpr int E = 8;
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    int64_t carry = 0;
+    for (int64_t base = 0; base < rows; base += 1024 * E) {
+        const int64_t r0 = base + (int64_t)tid * E;
+        int v[E];
+        int sum = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = r0 + e < rows ? row_ptr[r0 + e + 1] : 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) sum += v[e];
+        part[tid] = sum;
         __syncthreads();
-        part[threadIdx.x] += add;
-        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele, inclusive
+            const int add = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        int64_t run = carry + part[tid] - sum;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            run += v[e];
+            if (r0 + e < rows) row_ptr[r0 + e + 1] = (int32_t)run;
+        }
+        carry += part[1023];
+        __syncthreads();  // part is rewritten by the next chunk
     }
-    int64_t run = part[threadIdx.x] - sum;  // exclusive prefix of this run
-    for (int64_t r = r0; r < r1; ++r) {
-        const int64_t c = row_ptr[r + 1];
-        run += c;
-        row_ptr[r + 1] = (int32_t)run;
-    }
-    if (threadIdx.x == 0) row_ptr[0] = 0;
+    if (tid == 0) row_ptr[0] = 0;
 }
 
-// Writes each row's ids given its CSR range (row_ptr from the scan).
-template <int C>
-__global__ __launch_bounds__(256) void prefix_select_kernel(
-        int Nt, int64_t rows, const float* __restrict__ s, uint8_t* __restrict__ mask,
-        const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+// Moves each row's ids (written by cumulative_count_kernel over its scores)
+// to its CSR range; one wave per row.
+__global__ __launch_bounds__(256) void compact_rows_kernel(
+        int Nt, int64_t rows, const float* __restrict__ s, const int32_t* __restrict__ row_ptr,
+        int32_t* __restrict__ col_idx) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;  // wave-uniform
     const int32_t p0 = row_ptr[row];
-    const int k = row_ptr[row + 1] - p0;
-    select_row_wave<C>(Nt, k, s + row * Nt, mask ? mask + row * Nt : nullptr, col_idx + p0, lane);
+    const int n = row_ptr[row + 1] - p0;
+    const int32_t* src = (const int32_t*)(s + row * Nt);
+    for (int t = lane; t < n; t += 64) col_idx[p0 + t] = src[t];
 }
 
 // ------------------------------------------------------------------ STA
@@ -547,7 +592,7 @@ hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32
     return hipGetLastError();
 }
 
-hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, const float* s,
+hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, float* s,
                               uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t stream) {
     const int64_t rows = (int64_t)g.B * g.H * g.Nt;
@@ -558,10 +603,10 @@ hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, cons
 #define BSTA_CUM(CC)                                                                           \
     do {                                                                                       \
         hipLaunchKernelGGL(cumulative_count_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream, \
-                           g.Nt, rows, s, scale_log2, threshold, kmin, row_ptr + 1);           \
+                           g.Nt, rows, s, scale_log2, threshold, kmin, mask, row_ptr + 1);     \
         hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, rows, row_ptr);  \
-        hipLaunchKernelGGL(prefix_select_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream,   \
-                           g.Nt, rows, s, mask, row_ptr, col_idx);                             \
+        hipLaunchKernelGGL(compact_rows_kernel, dim3(wave_blocks), dim3(256), 0, stream, g.Nt,  \
+                           rows, (const float*)s, (const int32_t*)row_ptr, col_idx);           \
     } while (0)
     if (chunks <= 8) BSTA_CUM(8);
     else if (chunks <= 16) BSTA_CUM(16);

@@ -207,7 +207,8 @@ int32_t attn_select_blocks(const bsta_geom* g, const void* q_tiled, const void* 
  *                     every tile
  *   workspace         [scratch, >= attn_workspace_bytes(g,
  *                     BSTA_SELECT_CUMULATIVE)]; afterwards it holds the
- *                     pooled Q, K and scores
+ *                     pooled Q and K; the score rows are overwritten (each
+ *                     row's kept ids are staged there)
  * Requires Nt <= 2048 (a row of scores lives in one wave's registers);
  * larger grids return BSTA_ERR_SHAPE.  Probabilities and their sums are
  * fp32, so a row whose prefix mass lies within rounding of the threshold
