@@ -542,6 +542,29 @@ def test_backward_sta(bsta, name):
     _check_grads(w, r["grads"], tf, dtf, select.sta_mask(w.T, w.Y, w.X, np.array(win), w.B))
 
 
+def test_backward_on_cumulative_rows(bsta):
+    """Gradients over the variable-length rows of the cumulative selection."""
+    import torch
+    w = SMALL["smooth_40"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = bsta.attn_tile(g, q), bsta.attn_tile(g, k), bsta.attn_tile(g, v)
+    sel = bsta.attn_select_cumulative(g, qt, kt, 0.5, 2)
+    ot, lse = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, want_lse=True)
+    rng = np.random.default_rng(17)
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    dot = bsta.attn_tile(g, H.to_dev(do_bits))
+    grads = bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot, lse, sel.row_ptr, sel.col_idx)
+    torch.cuda.synchronize()
+    mask = sel.block_mask.cpu().numpy().astype(bool)
+    counts = mask.sum(-1)
+    assert counts.min() < counts.max(), "rows should differ in length"
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits, w.T, w.Y, w.X))
+    _check_grads(w, grads, tf, dtf, mask)
+
+
 def test_backward_deterministic(bsta):
     """Fixed summation orders: two calls give bitwise equal gradients."""
     import torch
