@@ -25,7 +25,8 @@ from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, 
 
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
-    "attn_select_cumulative", "attn_block_sparse_bwd", "attn_tile",
+    "attn_select_cumulative", "attn_block_sparse_bwd", "block_sparse_attention_trainable",
+    "attn_tile",
     "attn_tile_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
     "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
@@ -333,3 +334,41 @@ def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: 
         qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
         sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
     return attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+
+
+def _select_for(g: Geometry, qt, kt, mode, topk, windows, threshold, min_blocks):
+    if mode == SELECT_CUMULATIVE:
+        if threshold is None:
+            raise ValueError("SELECT_CUMULATIVE needs a threshold")
+        return attn_select_cumulative(g, qt, kt, threshold, min_blocks, want_mask=False)
+    return attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
+
+
+def block_sparse_attention_trainable(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
+                                     windows=None, threshold: Optional[float] = None,
+                                     min_blocks: int = 0):
+    """The whole path as a differentiable torch op on raster [B, L, H, D]
+    tensors: the forward tiles, selects and attends (keeping the tiled
+    output and lse), and backward() runs attn_block_sparse_bwd on the tiled
+    gradient and untiles dq, dk, dv.  The block selection is discrete and
+    passes no gradient."""
+    torch = _torch()
+
+    class _Fn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q_, k_, v_):
+            qt, kt, vt = attn_tile(g, q_), attn_tile(g, k_), attn_tile(g, v_)
+            sel = _select_for(g, qt, kt, mode, topk, windows, threshold, min_blocks)
+            ot, lse = attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx,
+                                            want_lse=True)
+            ctx.save_for_backward(qt, kt, vt, ot, lse, sel.row_ptr, sel.col_idx)
+            return attn_untile(g, ot)
+
+        @staticmethod
+        def backward(ctx, do):
+            qt, kt, vt, ot, lse, rp, ci = ctx.saved_tensors
+            dot = attn_tile(g, do.contiguous())
+            dq, dk, dv = attn_block_sparse_bwd(g, qt, kt, vt, ot, dot, lse, rp, ci)
+            return attn_untile(g, dq), attn_untile(g, dk), attn_untile(g, dv)
+
+    return _Fn.apply(q, k, v)

@@ -565,6 +565,40 @@ def test_backward_on_cumulative_rows(bsta):
     _check_grads(w, grads, tf, dtf, mask)
 
 
+@pytest.mark.parametrize("mode", ["topk", "cumulative"])
+def test_trainable_op_equals_direct_calls(bsta, mode):
+    """torch autograd through block_sparse_attention_trainable gives the
+    direct calls' output and gradients bit for bit (deterministic mode);
+    the direct calls are held to the oracle by the tests above."""
+    import torch
+    w = SMALL["ragged_d128"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    q, k, v = (H.to_dev(inp[n]).requires_grad_(True) for n in ("q", "k", "v"))
+    m = bsta.SELECT_TOPK if mode == "topk" else bsta.SELECT_CUMULATIVE
+    rng = np.random.default_rng(23)
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    do = H.to_dev(do_bits)
+    prev = bsta.attn_set_deterministic(True)
+    try:
+        o = bsta.block_sparse_attention_trainable(g, q, k, v, mode=m, topk=w.topk, threshold=0.5,
+                                                  min_blocks=1)
+        o.backward(do)
+        qt, kt, vt = (bsta.attn_tile(g, t.detach()) for t in (q, k, v))
+        sel = (bsta.attn_select_blocks(g, qt, kt, bsta.SELECT_TOPK, w.topk) if mode == "topk"
+               else bsta.attn_select_cumulative(g, qt, kt, 0.5, 1))
+        ot, lse = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, want_lse=True)
+        grads = bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, bsta.attn_tile(g, do), lse,
+                                           sel.row_ptr, sel.col_idx)
+        torch.cuda.synchronize()
+    finally:
+        bsta.attn_set_deterministic(prev)
+    same = lambda a, b: torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))  # noqa: E731
+    assert same(o.detach(), bsta.attn_untile(g, ot))
+    for t, gr in zip((q, k, v), grads):
+        assert same(t.grad, bsta.attn_untile(g, gr))
+
+
 def test_backward_deterministic(bsta):
     """Fixed summation orders: two calls give bitwise equal gradients."""
     import torch
