@@ -367,6 +367,34 @@ def test_cumulative_select(bsta, name, tau, mb):
     _check_cumulative(w, sel, _oracle_scores(w, inp["q"], inp["k"]), tau, mb)
 
 
+@pytest.mark.timeout(900)
+def test_cumulative_full_size_c3(bsta):
+    """The 40-head 1200-tile workload at the benchmark's threshold (0.15) and
+    route (Q and K pooled while tiled): every row of two heads against the
+    oracle, and the CSR equal to the GPU mask's rows."""
+    import torch
+    w = workloads.WORKLOADS["c3"]
+    inp = H.inputs(w)
+    H.log("cumulative c3 full size")
+    g = _geom(bsta, w)
+    sel = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, device="cuda")
+    pq, pk = sel.pooled(g)
+    bsta.attn_tile_pool(g, H.to_dev(inp["q"]), pq)
+    bsta.attn_tile_pool(g, H.to_dev(inp["k"]), pk)
+    sel = bsta.attn_select_cumulative(g, None, None, 0.15, 0, prepooled=True, out=sel)
+    torch.cuda.synchronize()
+    gmask = sel.block_mask.cpu().numpy().astype(bool)
+    rp, ci = select.mask_to_csr(gmask)
+    assert np.array_equal(sel.row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(sel.col_idx[:len(ci)].cpu().numpy(), ci)
+    for h in (0, w.H - 1):
+        qt = workloads.bf16_to_f32(tiling.tile(inp["q"][:, :, h:h + 1], w.T, w.Y, w.X))
+        kt = workloads.bf16_to_f32(tiling.tile(inp["k"][:, :, h:h + 1], w.T, w.Y, w.X))
+        s = select.scores(select.pool(qt, w.T, w.Y, w.X), select.pool(kt, w.T, w.Y, w.X))
+        same, band = H.accept_cumulative_rows(gmask[:, h:h + 1], s, w.D, 0.15, 0)
+        H.log(f"  head {h}: rows with the oracle's count {same}, inside the mass band {band}")
+
+
 @pytest.mark.parametrize("nt", WIDE_NT[:4])
 def test_cumulative_wide_rows(bsta, nt):
     """Random inputs in each register bucket of the one-wave row kernels."""
