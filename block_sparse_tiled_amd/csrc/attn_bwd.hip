@@ -284,17 +284,28 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
             load_tile<D>(rk, k + koff, rs);
             load_tile<D>(rv, v + koff, rs);
         }
+        // Operand reads are issued as a batch ahead of their products (the
+        // scheduling barriers keep the compiler from serialising each read
+        // with its product).
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            bf16x8 ka[NDC], va[NDC];
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) {
+                const int col = 16 * dc + 8 * half;
+                ka[dc] = lds_row8(kb0, LSTR, l32 + 32 * kb, col);
+                va[dc] = lds_row8(vb0, LSTR, l32 + 32 * kb, col);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             s[kb] = (f32x16){};
             dp[kb] = (f32x16){};
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
-                const int col = 16 * dc + 8 * half;
-                s[kb] = mma(lds_row8(kb0, LSTR, l32 + 32 * kb, col), qf[dc], s[kb]);
-                dp[kb] = mma(lds_row8(vb0, LSTR, l32 + 32 * kb, col), df[dc], dp[kb]);
+                s[kb] = mma(ka[dc], qf[dc], s[kb]);
+                dp[kb] = mma(va[dc], df[dc], dp[kb]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // dS^T in four bf16 chunks of 16 keys (chunk c: key block c/2,
         // registers 8*(c%2) + [0, 8)).
@@ -312,10 +323,21 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
                 dsf[c][r] = (__bf16)(pr * (dp[kb][rr] - dl));
             }
         }
+        // dQ^T += K^T dS^T, the K^T reads of step c+1 issued during step c.
+        bf16x8 kt2[2][NDB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int db = 0; db < NDB; ++db) kt2[0][db] = lds_tr8(kb0, LSTR, 0, db, lane);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mma(lds_tr8(kb0, LSTR, c, db, lane), dsf[c], acc[db]);
+        for (int c = 0; c < 4; ++c) {
+            if (c + 1 < 4) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) kt2[(c + 1) & 1][db] = lds_tr8(kb0, LSTR, c + 1, db, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[c & 1][db], dsf[c], acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // Lane holds dQ^T[d = 32*db + 8*(r/4) + 4*half + r%4][query qi].
     __bf16* out = dq + qoff;
@@ -406,16 +428,30 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
         __syncthreads();
         e = next_valid(e + 1);
         if (e < c1) prefetch(row_idx[e]);
+        // Operand reads in batches of four k-steps ahead of their products
+        // (the scheduling barriers keep each read from being serialised
+        // with its product).
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             s[mb] = (f32x16){};
             dp[mb] = (f32x16){};
 #pragma unroll
-            for (int dc = 0; dc < NDC; ++dc) {
-                const int col = 16 * dc + 8 * half;
-                s[mb] = mma(lds_row8(qb0, LSTR, l32 + 32 * mb, col), kf[dc], s[mb]);
-                dp[mb] = mma(lds_row8(db0, LSTR, l32 + 32 * mb, col), vf[dc], dp[mb]);
+            for (int d0 = 0; d0 < NDC; d0 += 4) {
+                bf16x8 qa[4], da[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int col = 16 * (d0 + u) + 8 * half;
+                    qa[u] = lds_row8(qb0, LSTR, l32 + 32 * mb, col);
+                    da[u] = lds_row8(db0, LSTR, l32 + 32 * mb, col);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    s[mb] = mma(qa[u], kf[d0 + u], s[mb]);
+                    dp[mb] = mma(da[u], vf[d0 + u], dp[mb]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // P and dS in bf16 chunks of 16 queries (chunk c: query block c/2,
@@ -442,12 +478,21 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
             }
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) {
+            bf16x8 ta[NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                adv[db] = mma(lds_tr8(db0, LSTR, c, db, lane), pf[c], adv[db]);
-                adk[db] = mma(lds_tr8(qb0, LSTR, c, db, lane), dsf[c], adk[db]);
-            }
+            for (int db = 0; db < NDB; ++db) ta[db] = lds_tr8(db0, LSTR, c, db, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) adv[db] = mma(ta[db], pf[c], adv[db]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) ta[db] = lds_tr8(qb0, LSTR, c, db, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) adk[db] = mma(ta[db], dsf[c], adk[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // Lane holds dV^T, dK^T[d = 32*db + 8*(r/4) + 4*half + r%4][key kj].
 #pragma unroll
