@@ -288,30 +288,31 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
         // scheduling barriers keep the compiler from serialising each read
         // with its product).
         f32x16 s[2], dp[2];
+        bf16x8 ka[2][NDC], va[2][NDC];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 ka[NDC], va[NDC];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
                 const int col = 16 * dc + 8 * half;
-                ka[dc] = lds_row8(kb0, LSTR, l32 + 32 * kb, col);
-                va[dc] = lds_row8(vb0, LSTR, l32 + 32 * kb, col);
+                ka[kb][dc] = lds_row8(kb0, LSTR, l32 + 32 * kb, col);
+                va[kb][dc] = lds_row8(vb0, LSTR, l32 + 32 * kb, col);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
             s[kb] = (f32x16){};
             dp[kb] = (f32x16){};
 #pragma unroll
             for (int dc = 0; dc < NDC; ++dc) {
-                s[kb] = mma(ka[dc], qf[dc], s[kb]);
-                dp[kb] = mma(va[dc], df[dc], dp[kb]);
+                s[kb] = mma(ka[kb][dc], qf[dc], s[kb]);
+                dp[kb] = mma(va[kb][dc], df[dc], dp[kb]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
         // dS^T in four bf16 chunks of 16 keys (chunk c: key block c/2,
         // registers 8*(c%2) + [0, 8)).
         bf16x8 dsf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        auto ds_chunk = [&](int c) {
             const int kb = c >> 1, r0 = (c & 1) * 8;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
@@ -322,11 +323,13 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
                                          : 0.f;
                 dsf[c][r] = (__bf16)(pr * (dp[kb][rr] - dl));
             }
-        }
-        // dQ^T += K^T dS^T, the K^T reads of step c+1 issued during step c.
+        };
+        // dQ^T += K^T dS^T: the K^T reads and the dS chunk of step c+1 are
+        // issued while the MFMAs of step c run.
         bf16x8 kt2[2][NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) kt2[0][db] = lds_tr8(kb0, LSTR, 0, db, lane);
+        ds_chunk(0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (c + 1 < 4) {
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[c & 1][db], dsf[c], acc[db]);
+            if (c + 1 < 4) ds_chunk(c + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -458,8 +462,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
         // registers 8*(c%2) + [0, 8); register rr holds query
         // 32*(c/2) + 8*(rr/4) + 4*half + rr%4).
         bf16x8 pf[4], dsf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        auto p_chunk = [&](int c) {
             const int mb = c >> 1, r0 = (c & 1) * 8;
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -476,7 +479,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
                     dsf[c][4 * rb + e] = (__bf16)(pr * (dp[mb][rr] - d4[e]));
                 }
             }
-        }
+        };
+        // dV^T += dO^T P and dK^T += Q^T dS; the P and dS chunk of step c+1
+        // is computed while the MFMAs of step c run.
+        p_chunk(0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             bf16x8 ta[NDB];
@@ -491,6 +497,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) adk[db] = mma(ta[db], dsf[c], adk[db]);
+            if (c + 1 < 4) p_chunk(c + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
