@@ -432,26 +432,27 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
         __syncthreads();
         e = next_valid(e + 1);
         if (e < c1) prefetch(row_idx[e]);
-        // Operand reads in batches of four k-steps ahead of their products
+        // Operand reads in batches of kBatch k-steps ahead of their products
         // (the scheduling barriers keep each read from being serialised
         // with its product).
+        constexpr int kBatch = NDC < 8 ? NDC : 8;
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             s[mb] = (f32x16){};
             dp[mb] = (f32x16){};
 #pragma unroll
-            for (int d0 = 0; d0 < NDC; d0 += 4) {
-                bf16x8 qa[4], da[4];
+            for (int d0 = 0; d0 < NDC; d0 += kBatch) {
+                bf16x8 qa[kBatch], da[kBatch];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kBatch; ++u) {
                     const int col = 16 * (d0 + u) + 8 * half;
                     qa[u] = lds_row8(qb0, LSTR, l32 + 32 * mb, col);
                     da[u] = lds_row8(db0, LSTR, l32 + 32 * mb, col);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kBatch; ++u) {
                     s[mb] = mma(qa[u], kf[d0 + u], s[mb]);
                     dp[mb] = mma(da[u], vf[d0 + u], dp[mb]);
                 }
