@@ -42,9 +42,9 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
     "src_sha256_16": "23e2e59dfbcf7165",
-    "fetch_kib": 44111895, "write_kib": 794140, "traffic_bytes": 91154360320,
-    "l2_hit": 0.540, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.464, "clock_ghz": 1.652,
+    "fetch_kib": 44082642, "write_kib": 794690, "traffic_bytes": 91095013376,
+    "l2_hit": 0.539, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.460, "clock_ghz": 1.684,
 }
 
 
