@@ -270,3 +270,13 @@ def test_set_deterministic_returns_previous(lib):
         assert lib.attn_set_deterministic(0) == 1
     finally:
         lib.attn_set_deterministic(first)
+
+
+def test_binding_argument_errors_before_any_gpu_call():
+    """The Python binding rejects bad combinations before it touches a GPU."""
+    import block_sparse_tiled_amd as bsta
+    g = bsta.Geometry(1, 2, 64, 8, 8, 8)
+    with pytest.raises(ValueError, match="prepooled"):
+        bsta.attn_select_cumulative(g, None, None, 0.5, prepooled=True)
+    with pytest.raises(ValueError, match="threshold"):
+        bsta._select_for(g, None, None, bsta.SELECT_CUMULATIVE, 0, None, None, 0)
