@@ -125,14 +125,6 @@ def block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X, scale=None):
     return dq, dk, dv
 
 
-def token_tile_ids(T: int, Y: int, X: int) -> np.ndarray:
-    """Tile id of every raster token, from its grid coordinates."""
-    nt, ny, nx = geometry.tile_counts(T, Y, X)
-    t, y, x = np.meshgrid(np.arange(T), np.arange(Y), np.arange(X), indexing="ij")
-    j = ((t // 4) * ny + (y // 4)) * nx + (x // 4)
-    return j.reshape(-1)
-
-
 def dense_masked_attention(q, k, v, mask, T, Y, X, scale=None):
     """Brute force in raster order with an explicit L x L 0/-inf token mask.
 
@@ -143,7 +135,7 @@ def dense_masked_attention(q, k, v, mask, T, Y, X, scale=None):
     B, L, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    tid = token_tile_ids(T, Y, X)
+    tid = geometry.token_tile_ids(T, Y, X)
     out = np.empty((B, L, H, D), dtype=np.float64)
     lse = np.empty((B, H, L), dtype=np.float64)
     for b in range(B):

@@ -1,21 +1,26 @@
-"""Tile geometry of a (T, Y, X) latent token grid cut into 4x4x4 tiles.
+"""Tile geometry of a (T, Y, X) latent token grid cut into tiles (4x4x4 by default).
 
-Follows:
-  * "video_sparse_attn" page, construct_variable_block_sizes: tile counts
-    per axis, per-axis tile extents where the last tile holds the remainder,
-    and the per-tile valid-token count as the product of the three extents,
-    flattened with the time tile outermost and the width tile innermost.
-  * "bsa_attn" page, get_tile_partition_indices: raster token ids
-    arange(T*H*W) reshaped to (T, H, W); tiles visited t-tile, then h-tile,
-    then w-tile; each tile contributes its clipped sub-block flattened in
-    row-major order.
+Written from what the pages say the geometry is, not from their listings:
+  * "bsa_attn" page (tile partition indices; pre/post-processing): tokens of
+    a (T, H, W) grid are numbered in row-major order, raster id
+    (t*Y + y)*X + x; the grid is cut into tiles, tiles are visited time tile
+    first and width tile last, and each tile lists its own tokens, clipped
+    at the grid's edge, in row-major order.
+  * "video_sparse_attn" section of the backends page (variable block sizes):
+    ceil(dim / tile) tiles per axis, the last one on an axis holding the
+    remainder; a tile's block size is its number of valid tokens.
   * "video_sparse_attn_h3" page, tile(): tiles live in a zero-padded buffer
     of tile_elems slots each.
 
+So token (t, y, x) belongs to tile (t // 4, y // 4, x // 4), numbered
+j = (a*nY + b)*nX + c, and the tile-contiguous order is a stable sort of the
+raster ids by tile id (inside a tile raster order is the sub-block's
+row-major order).  Occupancy is a count of tokens per tile id.
+
 Reading taken where the pages leave it open: inside a partial tile the valid
-tokens fill slots 0..n_j-1 in the clipped sub-block's row-major order and the
-remaining slots are padding (compact, valid first).  Grid axes are written
-(T, Y, X) here; the pages call them (T, H, W).
+tokens fill slots 0..n_j-1 in that order and the remaining slots are padding
+(compact, valid first).  Grid axes are written (T, Y, X) here; the pages
+call them (T, H, W).
 """
 from __future__ import annotations
 
@@ -41,58 +46,43 @@ def padded_len(T: int, Y: int, X: int, tile=TILE) -> int:
     return num_tiles(T, Y, X, tile) * tile[0] * tile[1] * tile[2]
 
 
-def _axis_sizes(dim_len: int, tile: int, n_tiles: int) -> np.ndarray:
-    """Extent of each tile along one axis; the last tile keeps the remainder."""
-    sizes = np.full(n_tiles, tile, dtype=np.int64)
-    remainder = dim_len - (n_tiles - 1) * tile
-    sizes[-1] = remainder if remainder > 0 else tile
-    return sizes
+def token_tile_ids(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
+    """Tile id of every raster token, from its grid coordinates: int64 [L]."""
+    _, ny, nx = tile_counts(T, Y, X, tile)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Y), np.arange(X), indexing="ij")
+    j = ((t // tile[0]) * ny + y // tile[1]) * nx + x // tile[2]
+    return j.reshape(-1).astype(np.int64)
 
 
 def occupancy(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
-    """Valid tokens per tile, int64 [Nt], tiles in (t, y, x) order."""
-    nt, ny, nx = tile_counts(T, Y, X, tile)
-    st = _axis_sizes(T, tile[0], nt)
-    sy = _axis_sizes(Y, tile[1], ny)
-    sx = _axis_sizes(X, tile[2], nx)
-    return (st[:, None, None] * sy[None, :, None] * sx[None, None, :]).reshape(-1)
+    """Valid tokens per tile (a count of the tokens carrying each tile id), int64 [Nt]."""
+    return np.bincount(token_tile_ids(T, Y, X, tile),
+                       minlength=num_tiles(T, Y, X, tile)).astype(np.int64)
 
 
-def tile_partition_indices(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
-    """Raster token ids listed in tile-contiguous (unpadded) order."""
-    ts, ys, xs = tile
-    ids = np.arange(T * Y * X, dtype=np.int64).reshape(T, Y, X)
-    parts = []
-    for a in range(math.ceil(T / ts)):
-        for b in range(math.ceil(Y / ys)):
-            for c in range(math.ceil(X / xs)):
-                parts.append(ids[a * ts:min(a * ts + ts, T),
-                                 b * ys:min(b * ys + ys, Y),
-                                 c * xs:min(c * xs + xs, X)].reshape(-1))
-    return np.concatenate(parts)
+def tile_order(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
+    """Raster token ids in tile-contiguous (unpadded) order.
 
-
-def reverse_tile_partition_indices(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
-    """Inverse of tile_partition_indices (argsort of it)."""
-    return np.argsort(tile_partition_indices(T, Y, X, tile), kind="stable")
+    A stable sort of the raster ids by tile id: tiles in increasing j, and
+    inside a tile its tokens in increasing raster id.
+    """
+    return np.argsort(token_tile_ids(T, Y, X, tile), kind="stable")
 
 
 def token_slots(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:
     """For each raster token, its slot in the zero-padded tile buffer.
 
-    Tile j owns slots [j*E, (j+1)*E) with E = prod(tile); its valid tokens take
-    the first n_j slots in the order the partition lists them.
+    Tile j owns slots [j*E, (j+1)*E) with E = prod(tile); a token's slot is
+    j*E plus its rank among its tile's tokens in tile-contiguous order.
     """
     E = tile[0] * tile[1] * tile[2]
-    perm = tile_partition_indices(T, Y, X, tile)
+    tid = token_tile_ids(T, Y, X, tile)
+    order = tile_order(T, Y, X, tile)
     occ = occupancy(T, Y, X, tile)
-    slots = np.empty(T * Y * X, dtype=np.int64)
-    pos = 0
-    for j, n in enumerate(occ):
-        slots[perm[pos:pos + n]] = j * E + np.arange(n)
-        pos += n
-    assert pos == T * Y * X
-    return slots
+    tile_start = np.concatenate([[0], np.cumsum(occ)[:-1]])   # position of each tile's first token
+    pos = np.empty(len(tid), dtype=np.int64)
+    pos[order] = np.arange(len(tid))                          # position of each token in the order
+    return tid * E + (pos - tile_start[tid])
 
 
 def tile_coords(T: int, Y: int, X: int, tile=TILE) -> np.ndarray:

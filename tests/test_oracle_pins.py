@@ -42,8 +42,8 @@ def test_partition_golden(name):
     g = _golden("geometry_examples.json")[name]
     T, Y, X = g["grid"]
     assert list(geometry.occupancy(T, Y, X)) == g["occupancy"]
-    if "tile_partition_indices" in g:
-        assert list(geometry.tile_partition_indices(T, Y, X)) == g["tile_partition_indices"]
+    if "tile_order" in g:
+        assert list(geometry.tile_order(T, Y, X)) == g["tile_order"]
     if "slots_of_tokens_64_to_79" in g:
         assert list(geometry.token_slots(T, Y, X)[64:80]) == g["slots_of_tokens_64_to_79"]
 
@@ -54,13 +54,32 @@ def test_partition_divisible_equals_rearrange(grid):
     T, Y, X = grid
     ids = np.arange(T * Y * X).reshape(T // 4, 4, Y // 4, 4, X // 4, 4)
     expected = ids.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
-    assert np.array_equal(geometry.tile_partition_indices(T, Y, X), expected)
+    assert np.array_equal(geometry.tile_order(T, Y, X), expected)
     assert np.array_equal(geometry.token_slots(T, Y, X), np.argsort(expected))
+
+
+def _extent(dim, idx):
+    """Tokens of tile idx along an axis of dim tokens cut into 4s."""
+    return min(4, dim - 4 * idx)
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (1, 1, 1), (3, 9, 2), (21, 30, 52), (4, 4, 5), (9, 13, 10)])
+def test_occupancy_closed_form(grid):
+    """n_j = s_t(a) s_y(b) s_x(c) with s(idx) = min(4, dim - 4 idx), tile j = (a nY + b) nX + c."""
+    T, Y, X = grid
+    nt, ny, nx = (math.ceil(T / 4), math.ceil(Y / 4), math.ceil(X / 4))
+    occ = geometry.occupancy(T, Y, X)
+    assert len(occ) == nt * ny * nx == geometry.num_tiles(T, Y, X)
+    for a in range(nt):
+        for b in range(ny):
+            for c in range(nx):
+                assert occ[(a * ny + b) * nx + c] == _extent(T, a) * _extent(Y, b) * _extent(X, c)
+    assert occ.sum() == T * Y * X
 
 
 @pytest.mark.parametrize("grid", [(5, 6, 7), (1, 1, 1), (3, 9, 2), (21, 30, 52), (4, 4, 5)])
 def test_geometry_brute_force(grid):
-    """Per-token tile id and rank from coordinates, independent of the loops."""
+    """Per-token tile id and rank by counting tokens in raster order."""
     T, Y, X = grid
     nt, ny, nx = (math.ceil(T / 4), math.ceil(Y / 4), math.ceil(X / 4))
     occ = geometry.occupancy(T, Y, X)
@@ -77,8 +96,24 @@ def test_geometry_brute_force(grid):
         seen.add(int(slots[l]))
     assert np.array_equal(counts, occ)
     assert len(seen) == T * Y * X
-    assert np.array_equal(geometry.reverse_tile_partition_indices(T, Y, X),
-                          np.argsort(geometry.tile_partition_indices(T, Y, X)))
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (3, 9, 2), (21, 30, 52), (7, 5, 11)])
+def test_slot_closed_form(grid):
+    """slot = 64 j + (dt s_y(b) + dy) s_x(c) + dx with (dt, dy, dx) = (t, y, x) mod 4:
+    the clipped sub-block's row-major rank, from the tile's own extents."""
+    T, Y, X = grid
+    ny, nx = math.ceil(Y / 4), math.ceil(X / 4)
+    slots = geometry.token_slots(T, Y, X)
+    order = geometry.tile_order(T, Y, X)
+    for t in range(T):
+        for y in range(Y):
+            for x in range(X):
+                a, b, c = t // 4, y // 4, x // 4
+                r = ((t % 4) * _extent(Y, b) + y % 4) * _extent(X, c) + x % 4
+                assert slots[(t * Y + y) * X + x] == 64 * ((a * ny + b) * nx + c) + r
+    # the tile-contiguous order lists the tokens by increasing slot
+    assert np.all(np.diff(slots[order]) > 0)
 
 
 # ---------------------------------------------------------------- tiling
@@ -122,7 +157,7 @@ def test_pool_matches_grouped_sum(grid):
     T, Y, X = grid
     rng = np.random.default_rng(3)
     x = rng.standard_normal((1, T * Y * X, 2, 5)).astype(np.float32)
-    tid = attention.token_tile_ids(T, Y, X)
+    tid = geometry.token_tile_ids(T, Y, X)
     nt = tid.max() + 1
     sums = np.zeros((nt, 2, 5))
     np.add.at(sums, tid, x[0].astype(np.float64))
@@ -238,6 +273,15 @@ def test_cumulative_golden_rows():
         assert list(np.nonzero(m[0])[0]) == case["selected"], case
 
 
+def test_cumulative_masses_golden():
+    """Prefix masses in descending score order at the attention's 1/sqrt(D),
+    derived by hand (select_examples.json)."""
+    g = _golden("select_examples.json")["cumulative_rows"]
+    for case in g["prefix_masses"]:
+        got = select.cumulative_masses(np.array([case["scores"]]), g["D"])[0]
+        assert np.allclose(got, case["masses"], rtol=0, atol=1e-12), case
+
+
 def _softmax_py(row, D):
     z = [v / math.sqrt(D) for v in row]
     top = max(z)
@@ -264,6 +308,9 @@ def test_cumulative_brute_force_subsets():
         c = max(c, min(mb, n))
         got = select.cumulative_mask(row[None], D, tau, mb)[0]
         assert int(select.cumulative_counts(row[None], D, tau, mb)[0]) == c
+        masses = select.cumulative_masses(row[None], D)[0]
+        for cc in range(1, n + 1):
+            assert abs(masses[cc - 1] - math.fsum(p[j] for j in best[cc])) < 1e-12
         assert tuple(np.nonzero(got)[0]) == tuple(sorted(best[c]))
 
 
@@ -504,7 +551,7 @@ def test_backward_equals_autograd(grid, k):
     T, Y, X = grid
     q, kk, v, do, mask = _bwd_case(grid, k=k, seed=7)
     B, L, H, D = q.shape
-    tid = attention.token_tile_ids(T, Y, X)
+    tid = geometry.token_tile_ids(T, Y, X)
     qt_, kt_, vt_ = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, kk, v))
     out = torch.zeros((B, L, H, D), dtype=torch.float64)
     outs = []
