@@ -145,9 +145,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __r
 // (Nt ints each).  Column j of head bh lists, in row order, the query tiles
 // whose CSR rows hold j; it occupies row_idx[col_start[bh*Nt + j] + [0,
 // col_cnt[bh*Nt + j])), inside the head's own CSR range.  Row ranges are
-// clamped to [0, col_len) and ids outside [0, Nt) are skipped; rows must
-// hold distinct ids (a repeated id leaves a slot of its column unwritten,
-// which the dK/dV kernel's range check then skips or reads as some row).
+// clamped to [0, col_len) and ids outside [0, Nt) are skipped.  A row that
+// repeats an id appears that many times in the id's column (the fill takes
+// its positions with an LDS atomic), so the dK/dV walk counts the repeat as
+// the forward and the dQ walk do.
 __global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ col_idx,
                                                        int64_t col_len, int32_t* __restrict__ col_start,
@@ -201,15 +202,15 @@ __global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __r
         col_start[base + j] = (int32_t)(head_off + start[j]);
         col_cnt[base + j] = cnt[j];
     }
-    // Fill in row order: one row at a time, its (distinct) ids in parallel.
+    // Fill in row order: one row at a time, its ids in parallel.  Repeats of
+    // an id within the row take distinct positions (all holding the same row).
     for (int i = 0; i < Nt; ++i) {
         const int64_t p0 = clampp(row_ptr[base + i]);
         const int64_t p1 = clampp(row_ptr[base + i + 1]);
         for (int64_t p = p0 + tid; p < p1; p += 1024) {
             const int j = col_idx[p];
             if ((unsigned)j < (unsigned)Nt) {
-                const int r = cur[j];
-                cur[j] = r + 1;
+                const int r = atomicAdd(&cur[j], 1);
                 const int64_t pos = head_off + start[j] + r;
                 if (pos < col_len) row_idx[pos] = i;
             }

@@ -290,11 +290,10 @@ int64_t attn_bwd_workspace_bytes(const bsta_geom* g, int64_t col_len);
  *   do_tiled [in] bf16 [B, Lpad, H, D], gradient of the loss w.r.t. O (pad
  *            rows are ignored)
  *   lse      [in] fp32 [B, H, Lpad], the forward's lse
- *   row_ptr, col_idx, col_len  the forward's CSR; each row must list
- *            distinct tile ids (every selection here does).  Ranges are
- *            clamped and out-of-range ids skipped as in the forward; a
- *            repeated id gives undefined gradients but no access outside
- *            the arrays.
+ *   row_ptr, col_idx, col_len  the forward's CSR.  Ranges are clamped and
+ *            out-of-range ids skipped as in the forward; an id repeated in
+ *            a row counts once per occurrence, as in the forward (every
+ *            selection here lists distinct ids).
  *   softmax_scale, causal  as the forward (1/sqrt(D), 0)
  *   dq_tiled, dk_tiled, dv_tiled [out] bf16 [B, Lpad, H, D]; pad rows and
  *            key tiles that no row selects are written as +0.0

@@ -116,20 +116,53 @@ def accept_cumulative_rows(gpu_mask: np.ndarray, oracle_scores: np.ndarray, D: i
     return same, len(cnt) - same
 
 
-def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X):
-    """Per-element error bounds for the GPU gradients (float64, tiled shapes).
+# bf16 keeps 8 significand bits, so its unit roundoff (round to nearest) is
+# 2^-8: |bf16(x) - x| <= 2^-8 |x|.
+BF16_U = 2.0 ** -8
 
-    The GPU rounds P and dS to bf16 (unit roundoff 2^-9) before the second
-    products, computes rowsum(dO*O) from the bf16 output, and rounds each
-    gradient once to bf16.  Summing the absolute values of the terms gives
-    |err dV| <= u * sum_q P |dO| + u |dV|,
-    |err dS| <= u * (|dS| + P * sum_d |dO O|),
-    |err dQ| <= scale * sum_keys |err dS| |K| + u |dQ|, and the same for dK
-    over the queries with |Q|.  The bound uses u = 2^-8 (twice bf16's unit
-    roundoff) and returns (bound_dq, bound_dk, bound_dv).
+
+def row_backward_bounds(q, keys, vals, do, scale):
+    """Gradients of one query tile over an explicit key list (float64), and
+    per-element bounds on the GPU's error in them.
+
+    The GPU recomputes P = exp(s - lse) from the forward's lse (error at
+    most LSE_TOL) and rounds it to bf16, so P carries a relative error of
+    at most e_P = (exp(LSE_TOL) - 1) + u, u = 2^-8 (bf16's unit roundoff).
+    delta = rowsum(dO * O) uses the forward's bf16 output, whose error is
+    its rounding (u |O|) plus the forward's own error, at most
+    2u * sum_k P_k |V_k| (its weights are bf16-rounded probabilities
+    normalised by their own sum).  dS = P (dP - delta) is rounded to bf16.
+    Summing absolute values of the terms:
+      |err dS| <= (e_P + u) |dS| + (1 + e_P) P |err delta|,
+      |err dV| <= e_P * sum_q P |dO|,
+      |err dQ| <= scale * sum_keys |err dS| |K|, and the same for dK over
+                  the queries with |Q|,
+    each gradient adding u times its own magnitude for its final rounding
+    (added by the caller, once per summed element).  Products of bf16
+    operands are exact in fp32 and fp32 accumulation error is far below
+    these terms.  Returns (dq, dkeys, dvals, bound_dq, bound_dkeys, bound_dvals)
+    without the final-rounding term.
     """
+    u = BF16_U
+    e_p = math.expm1(LSE_TOL) + u
+    s_ = q @ keys.T * scale
+    p = np.exp(s_ - s_.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o = p @ vals
+    ds = p * (do @ vals.T - (do * o).sum(axis=1, keepdims=True))
+    err_delta = (np.abs(do) * (u * np.abs(o) + 2.0 * u * (p @ np.abs(vals)))).sum(axis=1, keepdims=True)
+    eds = (e_p + u) * np.abs(ds) + (1.0 + e_p) * p * err_delta
+    return (scale * ds @ keys, scale * ds.T @ q, p.T @ do,
+            scale * eds @ np.abs(keys), scale * eds.T @ np.abs(q), e_p * p.T @ np.abs(do))
+
+
+def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X):
+    """Per-element error bounds for the GPU gradients (float64, tiled shapes):
+    row_backward_bounds summed over the selection, plus the final bf16
+    rounding of each gradient (u times its magnitude).  Returns
+    (bound_dq, bound_dk, bound_dv)."""
     from oracle import geometry as ogeo
-    u = 2.0 ** -8
+    u = BF16_U
     B, lpad, Hh, D = qt.shape
     E = ogeo.TILE_ELEMS
     occ = ogeo.occupancy(T, Y, X)
@@ -147,16 +180,9 @@ def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X):
                 do = dot[b, rows, h].astype(np.float64)
                 keys = np.concatenate([kt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
                 vals = np.concatenate([vt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
-                s_ = q @ keys.T * scale
-                p = np.exp(s_ - s_.max(axis=1, keepdims=True))
-                p /= p.sum(axis=1, keepdims=True)
-                o = p @ vals
-                ds = p * (do @ vals.T - (do * o).sum(axis=1, keepdims=True))
-                eds = u * (np.abs(ds) + p * np.abs(do * o).sum(axis=1, keepdims=True))
-                bq[b, rows, h] = scale * eds @ np.abs(keys)
-                gq[b, rows, h] = scale * ds @ keys
-                cbk, cbv = scale * eds.T @ np.abs(q), u * p.T @ np.abs(do)
-                cgk, cgv = scale * ds.T @ q, p.T @ do
+                cgq, cgk, cgv, cbq, cbk, cbv = row_backward_bounds(q, keys, vals, do, scale)
+                gq[b, rows, h] = cgq
+                bq[b, rows, h] = cbq
                 at = 0
                 for j in sel:
                     cols = slice(j * E, j * E + occ[j])
