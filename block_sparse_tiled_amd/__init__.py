@@ -186,6 +186,20 @@ def attn_select_alloc(g: Geometry, mode: int = SELECT_TOPK, topk: int = 0, windo
         workspace=(torch.empty(wsb // 4, dtype=torch.float32, device=device) if wsb > 0 else None))
 
 
+def _check_selection(g: Geometry, sel: Selection):
+    """Shapes and dtypes of a caller-supplied Selection against the geometry
+    (the C ABI sees only pointers and the col_idx / workspace sizes)."""
+    torch = _torch()
+    nt = attn_geometry(g)[0]
+    _expect(sel.row_ptr, (g.B * g.H * nt + 1,), torch.int32, "out.row_ptr")
+    _expect(sel.block_mask, (g.B, g.H, nt, nt), torch.uint8, "out.block_mask")
+    for name, t, dt in (("out.col_idx", sel.col_idx, torch.int32),
+                        ("out.workspace", sel.workspace, torch.float32)):
+        if t is not None and (t.dtype != dt or t.dim() != 1 or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError(f"{name}: expected a contiguous 1-D {dt} tensor on the GPU, got "
+                             f"{t.dtype} {tuple(t.shape)}")
+
+
 def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, topk: int = 0,
                        windows: Optional[Sequence[Sequence[int]]] = None, want_mask: bool = True,
                        out: Optional[Selection] = None) -> Selection:
@@ -203,6 +217,7 @@ def attn_select_blocks(g: Geometry, q_tiled, k_tiled, mode: int = SELECT_TOPK, t
     if out is None:
         dev = (q_tiled if q_tiled is not None else torch.empty(0, device="cuda")).device
         out = attn_select_alloc(g, mode, topk, windows, want_mask, dev)
+    _check_selection(g, out)
     _keep, w = _windows_arg(windows)
     ws = out.workspace
     status = _lib.load().attn_select_blocks(
@@ -231,6 +246,7 @@ def attn_select_cumulative(g: Geometry, q_tiled, k_tiled, threshold: float, min_
         raise ValueError("prepooled needs `out` holding the pooled Q and K")
     if out is None:
         out = attn_select_alloc(g, SELECT_CUMULATIVE, 0, None, want_mask, q_tiled.device)
+    _check_selection(g, out)
     ws = out.workspace
     status = _lib.load().attn_select_cumulative(
         ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), SELECT_PREPOOLED if prepooled else 0,

@@ -45,6 +45,8 @@
 //   ds_read_b64_tr_b16, per 16-lane group: if lane s addresses 4 elements
 //     C_s, lane d receives C_{d/4 + 4m}[d%4] for m = 0..3.
 //   global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l.
+#include <atomic>
+
 #include "bsta_common.hpp"
 
 namespace bsta {
@@ -678,13 +680,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 namespace {
 
 // Workgroups of the attention kernel resident per XCD on the current device
-// (computed once per device and kernel).
+// (computed once per device and kernel).  Host threads may race here: each
+// entry is an atomic, and racing threads store the same value.
 int resident_per_xcd(const void* kernel) {
-    static int cache[2][64] = {};
+    static std::atomic<int> cache[2][64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 16;
     const int which = kernel == (const void*)attn_fwd_kernel<128> ? 0 : 1;
-    if (cache[which][dev] > 0) return cache[which][dev];
+    const int known = cache[which][dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 128, 0) != hipSuccess ||
@@ -692,9 +696,9 @@ int resident_per_xcd(const void* kernel) {
         cus = 256;
         per_cu = 4;
     }
-    const int r = (cus / 8) * per_cu;
-    cache[which][dev] = r > 0 ? r : 1;
-    return cache[which][dev];
+    const int r = (cus / 8) * per_cu > 0 ? (cus / 8) * per_cu : 1;
+    cache[which][dev].store(r, std::memory_order_relaxed);
+    return r;
 }
 
 }  // namespace

@@ -282,24 +282,43 @@ def test_fwd_raster_equals_fwd_then_untile(bsta, name):
 
 
 @pytest.mark.parametrize("name", ["ragged_d128", "smooth_40"])
-def test_heads_first_layout_equals_standard(bsta, name):
+def test_heads_first_layout(bsta, name):
     """A heads-first [B, H, L, D] layout is the geometry (B*H, 1): every call
-    runs unchanged on it.  Tiles, CSR and output (CSR-order key walk) equal
-    those of the standard [B, L, H, D] layout, head by head, bit for bit."""
+    runs unchanged on it.  Its selection is the oracle's (tie band), its
+    output (default rotated key walk) matches the oracle's attention under
+    that selection, and with the CSR-order walk tiles, CSR and output equal
+    those of the standard [B, L, H, D] layout head by head, bit for bit."""
     import torch
     w = SMALL[name]
     inp = H.inputs(w)
     H.log(f"heads-first {name}")
+    gh = bsta.Geometry(w.B * w.H, 1, w.D, w.T, w.Y, w.X)
+    hf = {n: H.to_dev(inp[n]).permute(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D).contiguous()
+          for n in ("q", "k", "v")}
+
+    def run_hf():
+        qt, kt, vt = (bsta.attn_tile(gh, hf[n]) for n in ("q", "k", "v"))
+        sel = bsta.attn_select_blocks(gh, qt, kt, bsta.SELECT_TOPK, w.topk)
+        o = bsta.attn_block_sparse_fwd(gh, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+        torch.cuda.synchronize()
+        return qt, sel, o
+
+    # Against the oracle, in the library's default key walk.
+    _, sel, o = run_hf()
+    _, tf = _oracle_tiled(w, inp)
+    s = select.scores(select.pool(tf["q"], w.T, w.Y, w.X), select.pool(tf["k"], w.T, w.Y, w.X))
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    gmask = sel.block_mask.cpu().numpy().astype(bool).reshape(w.B, w.H, nt, nt)
+    H.accept_topk_rows(gmask, s, w.topk)
+    ref, _ = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X)
+    ref_hf = tiling.untile(ref, w.T, w.Y, w.X).transpose(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D)
+    H.compare_outputs(H.bf16_dev_to_f32(o), ref_hf, "heads-first output")
+
+    # Against the standard layout, bit for bit, with the CSR-order walk.
     prev = bsta.attn_set_deterministic(True)
     try:
         r = _run_gpu(bsta, w, inp, want_mask=False)
-        gh = bsta.Geometry(w.B * w.H, 1, w.D, w.T, w.Y, w.X)
-        hf = {n: H.to_dev(inp[n]).permute(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D).contiguous()
-              for n in ("q", "k", "v")}
-        qt, kt, vt = (bsta.attn_tile(gh, hf[n]) for n in ("q", "k", "v"))
-        sel = bsta.attn_select_blocks(gh, qt, kt, bsta.SELECT_TOPK, w.topk, want_mask=False)
-        o = bsta.attn_block_sparse_fwd(gh, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
-        torch.cuda.synchronize()
+        qt, sel, o = run_hf()
     finally:
         bsta.attn_set_deterministic(prev)
     # Heads-first row order (b, h, i) is the standard CSR row order.
@@ -310,6 +329,46 @@ def test_heads_first_layout_equals_standard(bsta, name):
     assert torch.equal(qt.view(torch.int16), std_tiles.contiguous().view(torch.int16))
     std_o = r["o"].permute(0, 2, 1, 3).reshape(w.B * w.H, w.L, 1, w.D)
     assert torch.equal(o.view(torch.int16), std_o.contiguous().view(torch.int16))
+
+
+def test_concurrent_calls_on_two_streams(bsta):
+    """Two attention calls in flight at once on two streams of equal
+    (default) priority, on different inputs and selections.  They share the
+    library's per-XCD key-walk counters; each output must still match the
+    oracle's attention under its own selection."""
+    import torch
+    cases = [workloads.custom("two_streams_a", 1, 12, 128, 16, 32, 32, "topk", 32, "lowrank", seed=31),
+             workloads.custom("two_streams_b", 1, 8, 128, 12, 40, 36, "topk", 40, "smooth", seed=32)]
+    prep = []
+    for w in cases:
+        inp = workloads.make_inputs(w)
+        r = _run_gpu(bsta, w, inp)
+        prep.append((w, inp, r))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        pair = []
+        for (w, inp, r), st in zip(prep, streams):
+            with torch.cuda.stream(st):
+                o = torch.full((w.B, w.L, w.H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+                bsta.attn_block_sparse_fwd(r["g"], r["qt"], r["kt"], r["vt"], r["sel"].row_ptr,
+                                           r["sel"].col_idx, out=o, raster=True)
+            pair.append(o)
+        outs.append(pair)
+    torch.cuda.synchronize()
+    for n, (w, inp, r) in enumerate(prep):
+        H.log(f"two streams: {w.name}")
+        _, tf = _oracle_tiled(w, inp)
+        gmask = r["sel"].block_mask.cpu().numpy().astype(bool)
+        nt = geometry.num_tiles(w.T, w.Y, w.X)
+        rows = [(0, h, i) for h in range(w.H) for i in (0, nt // 3, nt - 1)]
+        ref, _ = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X,
+                                             rows=rows)
+        for pair in outs:
+            o = pair[n]
+            assert not torch.isnan(o.float()).any(), "every raster row is written"
+            _compare_raster_rows(w, H.bf16_dev_to_f32(o), ref, rows)
 
 
 # ---------------------------------------------------------------- windows
@@ -627,6 +686,67 @@ def test_trainable_op_equals_direct_calls(bsta, mode):
         assert same(t.grad, bsta.attn_untile(g, gr))
 
 
+def test_backward_repeated_ids(bsta):
+    """A CSR row that lists a tile twice counts it twice, in the forward and
+    in all three gradients: against the chain rule over the row's explicit
+    key list, repeats included (the oracle's per-query-tile attention and
+    its backward, float64, dK and dV summed per tile)."""
+    import torch
+    w = SMALL["ragged_d64"]
+    inp = H.inputs(w)
+    g = _geom(bsta, w)
+    _, tf = _oracle_tiled(w, inp)
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    occ = geometry.occupancy(w.T, w.Y, w.X)
+    rng = np.random.default_rng(41)
+    lists = []
+    for r in range(w.B * w.H * nt):
+        ids = sorted(rng.choice(nt, size=4, replace=False).tolist())
+        if r % 3 == 0:
+            ids.insert(1, ids[0])            # a repeat, next to its first occurrence
+        if r % 5 == 0:
+            ids.append(ids[-1])
+        lists.append(ids)
+    rp = np.zeros(len(lists) + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([len(x) for x in lists])
+    ci = np.concatenate(lists).astype(np.int32)
+    qt, kt, vt = (H.to_dev(tiling.tile(inp[n], w.T, w.Y, w.X)) for n in ("q", "k", "v"))
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    dot = bsta.attn_tile(g, H.to_dev(do_bits))
+    rpd, cid = torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+    ot, lse = bsta.attn_block_sparse_fwd(g, qt, kt, vt, rpd, cid, want_lse=True)
+    grads = bsta.attn_block_sparse_bwd(g, qt, kt, vt, ot, dot, lse, rpd, cid)
+    torch.cuda.synchronize()
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits, w.T, w.Y, w.X)).astype(np.float64)
+    ref_o = np.zeros(tf["q"].shape)
+    ref = [np.zeros(tf["q"].shape) for _ in range(3)]
+    bnd = [np.zeros(tf["q"].shape) for _ in range(3)]
+    scale = 1.0 / math.sqrt(w.D)
+    for r, ids in enumerate(lists):
+        b, h, i = r // (w.H * nt), (r // nt) % w.H, r % nt
+        rows = slice(i * 64, i * 64 + occ[i])
+        keys = np.concatenate([tf["k"][b, j * 64:j * 64 + occ[j], h] for j in ids]).astype(np.float64)
+        vals = np.concatenate([tf["v"][b, j * 64:j * 64 + occ[j], h] for j in ids]).astype(np.float64)
+        q = tf["q"][b, rows, h].astype(np.float64)
+        ref_o[b, rows, h] = oatt.tile_attention(q, keys, vals, scale)[0]
+        gq, gk, gv, bq, bk, bv = H.row_backward_bounds(q, keys, vals, dtf[b, rows, h], scale)
+        ref[0][b, rows, h] = gq
+        bnd[0][b, rows, h] = bq
+        at = 0
+        for j in ids:
+            cols = slice(j * 64, j * 64 + occ[j])
+            ref[1][b, cols, h] += gk[at:at + occ[j]]
+            ref[2][b, cols, h] += gv[at:at + occ[j]]
+            bnd[1][b, cols, h] += bk[at:at + occ[j]]
+            bnd[2][b, cols, h] += bv[at:at + occ[j]]
+            at += occ[j]
+    H.compare_outputs(H.bf16_dev_to_f32(ot), ref_o, "forward with repeated ids")
+    for name, gr, rf, bd in zip(("dq", "dk", "dv"), grads, ref, bnd):
+        err = np.abs(H.bf16_dev_to_f32(gr).astype(np.float64) - rf)
+        bound = bd + H.BF16_U * np.abs(rf) + 1e-6
+        assert np.all(err <= bound), f"{name}: error above its bound (ratio {float((err / bound).max()):.3f})"
+
+
 def test_backward_deterministic(bsta):
     """Fixed summation orders: two calls give bitwise equal gradients."""
     import torch
@@ -887,13 +1007,35 @@ def test_rotated_walk_matches_deterministic(bsta):
 
 # ---------------------------------------------------------------- full sizes
 
-def _full_size_check(bsta, w, n_rows):
-    """Full workload in the benchmark's launch configuration; selection checked
-    for every row, attention on sampled query tiles."""
-    H.log(f"full size {w.name}: generating inputs")
-    inp = H.inputs(w)
+def _compare_raster_rows(w, got_raster, ref_tiled, rows):
+    """Raster-order GPU output of query tiles `rows` against the oracle's
+    tiled output: the tokens of tile i are the i-th run of the tile order."""
+    occ = geometry.occupancy(w.T, w.Y, w.X)
+    order = geometry.tile_order(w.T, w.Y, w.X)
+    start = np.concatenate([[0], np.cumsum(occ)])
+    gs, rs = [], []
+    for b, h, i in rows:
+        toks = order[start[i]:start[i + 1]]
+        gs.append(got_raster[b, toks, h])
+        rs.append(ref_tiled[b, i * 64:i * 64 + occ[i], h])
+    return H.compare_outputs(np.concatenate(gs), np.concatenate(rs), "raster output rows")
+
+
+def _csr_mask(row_ptr, col_idx, B, Hh, nt):
+    """Block mask of a CSR (host arrays)."""
+    mask = np.zeros((B * Hh * nt, nt), dtype=bool)
+    for r in range(B * Hh * nt):
+        mask[r, col_idx[row_ptr[r]:row_ptr[r + 1]]] = True
+    return mask.reshape(B, Hh, nt, nt)
+
+
+def _full_size_check(bsta, w, inp, n_rows):
+    """Full workload through the unfused calls (attn_tile x3, attn_select_blocks
+    pooling the tiled Q and K itself, the tiled-output attention, attn_untile);
+    selection checked for every row, attention on sampled query tiles.
+    Returns the oracle's tiled inputs and scores for the next check."""
     win = inp.get("windows")
-    H.log(f"full size {w.name}: GPU path")
+    H.log(f"full size {w.name}: GPU path (unfused calls)")
     r = _run_gpu(bsta, w, inp, windows=None if win is None else win.tolist())
     g = r["g"]
     nt = geometry.num_tiles(w.T, w.Y, w.X)
@@ -902,6 +1044,7 @@ def _full_size_check(bsta, w, n_rows):
     H.log(f"full size {w.name}: oracle selection")
     gmask = r["sel"].block_mask.cpu().numpy().astype(bool)
     tb, tf = _oracle_tiled(w, inp)
+    s = pq = pk = None
     if w.mode == "sta":
         om = select.sta_mask(w.T, w.Y, w.X, win, w.B)
         assert np.array_equal(gmask, om)
@@ -911,7 +1054,8 @@ def _full_size_check(bsta, w, n_rows):
         gpq, gpk = (t.cpu().numpy() for t in r["sel"].pooled(g))
         assert np.all(np.abs(gpq - pq) <= H.POOL_TOL * (1 + np.abs(pq)))
         assert np.all(np.abs(gpk - pk) <= H.POOL_TOL * (1 + np.abs(pk)))
-        exact, band = H.accept_topk_rows(gmask, select.scores(pq, pk), w.topk)
+        s = select.scores(pq, pk)
+        exact, band = H.accept_topk_rows(gmask, s, w.topk)
         H.log(f"  rows exact {exact}, inside tie band {band}")
     rp, ci = select.mask_to_csr(gmask)
     assert np.array_equal(r["sel"].row_ptr.cpu().numpy(), rp)
@@ -933,9 +1077,116 @@ def _full_size_check(bsta, w, n_rows):
     H.compare_outputs(np.concatenate(gs), np.concatenate(rs))
     # untile of the output is the oracle untile of the GPU's tiled output
     assert np.array_equal(H.from_dev(r["o"]), tiling.untile(H.from_dev(r["ot"]), w.T, w.Y, w.X))
+    del r
+    return tb, tf, s, pq, pk
+
+
+def _bench_route(m, w, inp):
+    """The benchmark's step, call for call: with top-k, attn_tile_pool tiles Q
+    and K and writes their pooled vectors into the selection's workspace,
+    attn_tile tiles V, and attn_select_blocks starts from the pooled vectors
+    (SELECT_PREPOOLED); with windows, attn_tile tiles all three.  The
+    attention writes raster order itself (attn_block_sparse_fwd_raster) in
+    the library's default rotated key walk, into a buffer that starts as
+    NaN, so a row left unwritten shows.  No block mask is requested."""
+    import torch
+    g = _geom(m, w)
+    nt, lpad = m.attn_geometry(g)
+    mode = m.SELECT_STA if w.mode == "sta" else m.SELECT_TOPK
+    win = inp["windows"].tolist() if w.mode == "sta" else None
+    q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
+    qt, kt, vt = (torch.empty((w.B, lpad, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+                  for _ in range(3))
+    o = torch.full((w.B, w.L, w.H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sel = m.attn_select_alloc(g, mode, w.topk, win, want_mask=False)
+    fused = mode == m.SELECT_TOPK
+    if fused:
+        pq, pk = sel.pooled(g)
+        m.attn_tile_pool(g, q, pq, out=qt)
+        m.attn_tile_pool(g, k, pk, out=kt)
+    else:
+        m.attn_tile(g, q, out=qt)
+        m.attn_tile(g, k, out=kt)
+    m.attn_tile(g, v, out=vt)
+    sel_mode = (m.SELECT_TOPK | m.SELECT_PREPOOLED) if fused else mode
+    m.attn_select_blocks(g, None if fused else qt, None if fused else kt, sel_mode, w.topk, win,
+                         out=sel)
+    m.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    return dict(g=g, qt=qt, kt=kt, vt=vt, sel=sel, o=o)
+
+
+def _bench_route_check(bsta, w, inp, tb, tf, s, pq, pk):
+    """The benchmark's route at full size against the oracle: tiles bit-exact,
+    pooled vectors to 1e-5(1+|x|), every selection row (tie band for top-k,
+    exact for windows) and the CSR, then the raster attention output of one
+    query tile of every (b, h) (plus the first and last tiles) element-wise
+    against the oracle's attention under the GPU's validated selection."""
+    import torch
+    assert bsta.attn_set_deterministic(False) is False, "default mode is the rotated walk"
+    H.log(f"full size {w.name}: benchmark route")
+    r = _bench_route(bsta, w, inp)
+    g = r["g"]
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    for n in ("q", "k", "v"):
+        assert np.array_equal(H.from_dev(r[n + "t"]), tb[n]), f"tiled {n}"
+    row_ptr = r["sel"].row_ptr.cpu().numpy().astype(np.int64)
+    col_idx = r["sel"].col_idx.cpu().numpy()[:row_ptr[-1]]
+    gmask = _csr_mask(row_ptr, col_idx, w.B, w.H, nt)
+    if w.mode == "sta":
+        assert np.array_equal(gmask, select.sta_mask(w.T, w.Y, w.X, inp["windows"], w.B))
+    else:
+        gpq, gpk = (t.cpu().numpy() for t in r["sel"].pooled(g))
+        assert np.all(np.abs(gpq - pq) <= H.POOL_TOL * (1 + np.abs(pq)))
+        assert np.all(np.abs(gpk - pk) <= H.POOL_TOL * (1 + np.abs(pk)))
+        exact, band = H.accept_topk_rows(gmask, s, w.topk)
+        H.log(f"  rows exact {exact}, inside tie band {band}")
+    rp, ci = select.mask_to_csr(gmask)
+    assert np.array_equal(row_ptr, rp) and np.array_equal(col_idx, ci), "CSR ascending, row_ptr exact"
+    assert not torch.isnan(r["o"].float()).any(), "every raster row is written"
+    rng = np.random.default_rng(100 + w.index)
+    rows = [(b, h, int(rng.integers(nt))) for b in range(w.B) for h in range(w.H)]
+    rows += [(0, 0, 0), (w.B - 1, w.H - 1, nt - 1)]
+    H.log(f"full size {w.name}: oracle attention on {len(rows)} query tiles (raster output)")
+    ref, _ = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], gmask, w.T, w.Y, w.X, rows=rows)
+    mx, mean = _compare_raster_rows(w, H.bf16_dev_to_f32(r["o"]), ref, rows)
+    H.log(f"  raster rows max-abs {mx:.3g}, mean-abs {mean:.3g}")
+    return r
+
+
+def _oracle_csr_full_head(bsta, w, r, tf, s, h0):
+    """The benchmarked attention call (raster output, rotated walk) on the
+    oracle's own top-k selection for head h0, every other row empty: all of
+    head h0's query tiles against the oracle; the other heads' rows are zero."""
+    import torch
+    nt = geometry.num_tiles(w.T, w.Y, w.X)
+    om = select.topk_mask(s, w.topk)
+    one = np.zeros_like(om)
+    one[:, h0] = om[:, h0]
+    rp, ci = select.mask_to_csr(one)
+    o = torch.full((w.B, w.L, w.H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bsta.attn_block_sparse_fwd(r["g"], r["qt"], r["kt"], r["vt"], torch.from_numpy(rp).cuda(),
+                               torch.from_numpy(ci).cuda(), out=o, raster=True)
+    torch.cuda.synchronize()
+    H.log(f"full size {w.name}: oracle attention, head {h0}, all {nt} query tiles on the oracle's CSR")
+    rows = [(b, h0, i) for b in range(w.B) for i in range(nt)]
+    ref, _ = oatt.block_sparse_attention(tf["q"], tf["k"], tf["v"], om, w.T, w.Y, w.X, rows=rows)
+    got = H.bf16_dev_to_f32(o)
+    mx, mean = _compare_raster_rows(w, got, ref, rows)
+    H.log(f"  head {h0}: max-abs {mx:.3g}, mean-abs {mean:.3g}")
+    others = np.ones(w.H, dtype=bool)
+    others[h0] = False
+    assert np.all(H.from_dev(o)[:, :, others] == 0), "empty rows are written as +0.0"
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_full_size(bsta, name):
-    _full_size_check(bsta, workloads.WORKLOADS[name], 24)
+    w = workloads.WORKLOADS[name]
+    H.log(f"full size {w.name}: generating inputs")
+    inp = H.inputs(w)
+    tb, tf, s, pq, pk = _full_size_check(bsta, w, inp, 24)
+    r = _bench_route_check(bsta, w, inp, tb, tf, s, pq, pk)
+    if name == "c3":
+        _oracle_csr_full_head(bsta, w, r, tf, s, h0=17)
