@@ -25,7 +25,8 @@ from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, 
 
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
-    "attn_select_cumulative", "attn_block_sparse_bwd", "block_sparse_attention_trainable",
+    "attn_select_cumulative", "attn_block_sparse_bwd", "attn_block_sparse_bwd_noalloc",
+    "block_sparse_attention_trainable",
     "attn_tile",
     "attn_tile_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
@@ -317,6 +318,35 @@ def attn_block_sparse_bwd(g: Geometry, q_tiled, k_tiled, v_tiled, o_tiled, do_ti
         _ptr(do_tiled), _ptr(lse), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
         float(softmax_scale), 0, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws), wsb,
         _stream()))
+    return out
+
+
+def attn_block_sparse_bwd_noalloc(g: Geometry, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse,
+                                  row_ptr, col_idx, out, softmax_scale: Optional[float] = None):
+    """attn_block_sparse_bwd with the library's static 64 MiB device scratch
+    as its workspace: allocates nothing (the caller gives ``out`` = (dq, dk,
+    dv)).  Equal to attn_block_sparse_bwd bit for bit; raises BstaError
+    (capacity) when the workspace it needs exceeds the scratch.  Calls that
+    overlap on one GPU share the scratch and race."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    for name, t in (("q_tiled", q_tiled), ("k_tiled", k_tiled), ("v_tiled", v_tiled),
+                    ("o_tiled", o_tiled), ("do_tiled", do_tiled)):
+        _expect(t, (g.B, lpad, g.H, g.D), torch.bfloat16, name)
+    _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
+    _expect(row_ptr, (g.B * g.H * nt + 1,), torch.int32, "row_ptr")
+    if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
+        raise ValueError("col_idx: expected contiguous int32")
+    if out is None or len(out) != 3:
+        raise ValueError("out: give the three output tensors (dq, dk, dv)")
+    for name, t in zip(("dq", "dk", "dv"), out):
+        _expect(t, (g.B, lpad, g.H, g.D), torch.bfloat16, name)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(g.D)
+    _lib.check(_lib.load().attn_block_sparse_bwd_noalloc(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(o_tiled),
+        _ptr(do_tiled), _ptr(lse), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+        float(softmax_scale), 0, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _stream()))
     return out
 
 

@@ -37,6 +37,8 @@
 // dS are rounded to bf16 for the second product, accumulators are fp32 and
 // each gradient is rounded once to bf16 at the end.  Pad query rows and pad
 // key rows contribute nothing and are written as +0.0.
+#include <mutex>
+
 #include "bsta_common.hpp"
 
 namespace bsta {
@@ -520,6 +522,38 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ launcher
+// Device scratch of attn_block_sparse_bwd_noalloc: the same workspace
+// (rowsum(dO*O) and the CSR's transpose) in a static array, so that callers
+// that cannot allocate (graph capture, tight serving loops) need no
+// workspace argument.  Every GPU the library runs on holds its own copy
+// until the process ends.  Each call writes every word of it that its
+// kernels read before they read it, so no clearing is needed; calls that
+// overlap on one GPU share it and race.
+static __device__ __align__(256) char scratch[kBwdScratchBytes];
+
+// Device address of `scratch` on the current device.  On the host the
+// array's name is only a host-side stand-in, so the address is looked up
+// with hipGetSymbolAddress, once per device with that device current, and
+// kept; callers pass it to the kernels like any workspace pointer.
+hipError_t bwd_scratch(void** out) {
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,

@@ -32,6 +32,7 @@ hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32
 hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, float* s,
                               uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t stream);
+hipError_t bwd_scratch(void** out);
 hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
@@ -425,6 +426,51 @@ int64_t attn_bwd_workspace_bytes(const bsta_geom* gin, int64_t col_len) {
     return bwd_layout(g, col_len).total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two backward entry points.
+int32_t check_bwd(const bsta_geom* gin, Geo* g, const void* q_tiled, const void* k_tiled,
+                  const void* v_tiled, const void* o_tiled, const void* do_tiled, const float* lse,
+                  const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                  float softmax_scale, int32_t causal, void* dq_tiled, void* dk_tiled,
+                  void* dv_tiled, const char* who) {
+    int32_t st = make_geo(gin, g);
+    if (st != BSTA_OK) return st;
+    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o_tiled == nullptr ||
+        do_tiled == nullptr || lse == nullptr || row_ptr == nullptr || col_idx == nullptr ||
+        dq_tiled == nullptr || dk_tiled == nullptr || dv_tiled == nullptr)
+        return fail(BSTA_ERR_NULL, "%s: NULL tensor, lse or index pointer", who);
+    st = check_scale(*g, softmax_scale, causal);
+    if (st != BSTA_OK) return st;
+    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
+    if (col_len > 0x7fffffffLL)
+        return fail(BSTA_ERR_SHAPE, "col_len %lld overflows int32 offsets", (long long)col_len);
+    if (g->Nt > kMaxBwdTiles)
+        return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
+                    g->Nt);
+    return BSTA_OK;
+}
+
+int32_t run_bwd(const Geo& g, const BwdLayout& l, char* ws, const void* q_tiled,
+                const void* k_tiled, const void* v_tiled, const void* o_tiled, const void* do_tiled,
+                const float* lse, const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                float softmax_scale, void* dq_tiled, void* dk_tiled, void* dv_tiled, void* stream,
+                const char* who) {
+    return hip_status(
+            bsta::launch_attn_bwd(g, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                                  col_idx, col_len, softmax_scale, dq_tiled, dk_tiled, dv_tiled,
+                                  (float*)(ws + l.delta), (int32_t*)(ws + l.col_start),
+                                  (int32_t*)(ws + l.col_cnt), (int32_t*)(ws + l.row_idx),
+                                  (hipStream_t)stream),
+            who);
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t attn_block_sparse_bwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const void* o_tiled, const void* do_tiled,
                               const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
@@ -432,33 +478,44 @@ int32_t attn_block_sparse_bwd(const bsta_geom* gin, const void* q_tiled, const v
                               void* dq_tiled, void* dk_tiled, void* dv_tiled, void* workspace,
                               int64_t workspace_bytes, void* stream) {
     Geo g;
-    int32_t st = make_geo(gin, &g);
+    int32_t st = check_bwd(gin, &g, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                           col_idx, col_len, softmax_scale, causal, dq_tiled, dk_tiled, dv_tiled,
+                           "attn_block_sparse_bwd");
     if (st != BSTA_OK) return st;
-    if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || o_tiled == nullptr ||
-        do_tiled == nullptr || lse == nullptr || row_ptr == nullptr || col_idx == nullptr ||
-        dq_tiled == nullptr || dk_tiled == nullptr || dv_tiled == nullptr)
-        return fail(BSTA_ERR_NULL, "attn_block_sparse_bwd: NULL tensor, lse or index pointer");
-    st = check_scale(g, softmax_scale, causal);
-    if (st != BSTA_OK) return st;
-    if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
-    if (col_len > 0x7fffffffLL)
-        return fail(BSTA_ERR_SHAPE, "col_len %lld overflows int32 offsets", (long long)col_len);
-    if (g.Nt > kMaxBwdTiles)
-        return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
-                    g.Nt);
     const BwdLayout l = bwd_layout(g, col_len);
     if (workspace == nullptr) return fail(BSTA_ERR_NULL, "attn_block_sparse_bwd: NULL workspace");
     if (workspace_bytes < l.total)
         return fail(BSTA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
                     (long long)workspace_bytes, (long long)l.total);
-    char* ws = (char*)workspace;
-    return hip_status(
-            bsta::launch_attn_bwd(g, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
-                                  col_idx, col_len, softmax_scale, dq_tiled, dk_tiled, dv_tiled,
-                                  (float*)(ws + l.delta), (int32_t*)(ws + l.col_start),
-                                  (int32_t*)(ws + l.col_cnt), (int32_t*)(ws + l.row_idx),
-                                  (hipStream_t)stream),
-            "attn_block_sparse_bwd");
+    return run_bwd(g, l, (char*)workspace, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse,
+                   row_ptr, col_idx, col_len, softmax_scale, dq_tiled, dk_tiled, dv_tiled, stream,
+                   "attn_block_sparse_bwd");
+}
+
+int32_t attn_block_sparse_bwd_noalloc(const bsta_geom* gin, const void* q_tiled,
+                                      const void* k_tiled, const void* v_tiled,
+                                      const void* o_tiled, const void* do_tiled, const float* lse,
+                                      const int32_t* row_ptr, const int32_t* col_idx,
+                                      int64_t col_len, float softmax_scale, int32_t causal,
+                                      void* dq_tiled, void* dk_tiled, void* dv_tiled,
+                                      void* stream) {
+    Geo g;
+    int32_t st = check_bwd(gin, &g, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                           col_idx, col_len, softmax_scale, causal, dq_tiled, dk_tiled, dv_tiled,
+                           "attn_block_sparse_bwd_noalloc");
+    if (st != BSTA_OK) return st;
+    const BwdLayout l = bwd_layout(g, col_len);
+    if (l.total > bsta::kBwdScratchBytes)
+        return fail(BSTA_ERR_CAPACITY,
+                    "attn_block_sparse_bwd_noalloc: needs %lld bytes of scratch, the static "
+                    "scratch holds %lld (use attn_block_sparse_bwd with a workspace)",
+                    (long long)l.total, (long long)bsta::kBwdScratchBytes);
+    void* ws = nullptr;
+    st = hip_status(bsta::bwd_scratch(&ws), "attn_block_sparse_bwd_noalloc: scratch address");
+    if (st != BSTA_OK) return st;
+    return run_bwd(g, l, (char*)ws, q_tiled, k_tiled, v_tiled, o_tiled, do_tiled, lse, row_ptr,
+                   col_idx, col_len, softmax_scale, dq_tiled, dk_tiled, dv_tiled, stream,
+                   "attn_block_sparse_bwd_noalloc");
 }
 
 int32_t attn_set_deterministic(int32_t enable) {

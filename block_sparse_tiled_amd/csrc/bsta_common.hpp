@@ -17,6 +17,10 @@
 namespace bsta {
 
 constexpr int kTileElems = 64;  // 4 x 4 x 4 tokens
+// Size of the static device scratch behind attn_block_sparse_bwd_noalloc,
+// and the device ordinals whose scratch address is cached.
+constexpr int64_t kBwdScratchBytes = int64_t(64) << 20;
+constexpr int kMaxDevices = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

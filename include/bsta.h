@@ -311,6 +311,35 @@ int32_t attn_block_sparse_bwd(const bsta_geom* g, const void* q_tiled, const voi
                               int64_t workspace_bytes, void* stream);
 
 /*
+ * attn_block_sparse_bwd_noalloc: attn_block_sparse_bwd without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc).  It validates its arguments exactly as attn_block_sparse_bwd,
+ * runs the same kernels in the same order (so its gradients equal that
+ * call's bit for bit), and calls no hipMalloc, hipFree or other allocating
+ * routine.  Its workspace is a static device array of the library, 64 MiB
+ * (67108864 bytes) per GPU, held on every GPU the library runs on until
+ * the process ends; its address is looked up once per device on the first
+ * call made with that device current.
+ *   Arguments: as attn_block_sparse_bwd, without workspace and
+ *            workspace_bytes.
+ *   Errors: as attn_block_sparse_bwd; BSTA_ERR_CAPACITY (nothing enqueued)
+ *            when attn_bwd_workspace_bytes(g, col_len) exceeds 64 MiB;
+ *            BSTA_ERR_HIP when the scratch address cannot be obtained.
+ * Every call on a GPU uses that GPU's one array, which keeps the last
+ * call's contents (each call writes every word its kernels read, so
+ * nothing needs clearing).  Calls that overlap on one GPU race: serialise
+ * them, for instance on one stream.
+ */
+int32_t attn_block_sparse_bwd_noalloc(const bsta_geom* g, const void* q_tiled,
+                                      const void* k_tiled, const void* v_tiled,
+                                      const void* o_tiled, const void* do_tiled, const float* lse,
+                                      const int32_t* row_ptr, const int32_t* col_idx,
+                                      int64_t col_len, float softmax_scale, int32_t causal,
+                                      void* dq_tiled, void* dk_tiled, void* dv_tiled,
+                                      void* stream);
+
+/*
  * attn_set_deterministic (host only, no HIP call): process-wide key order of
  * attn_block_sparse_fwd for calls made after it returns.  enable != 0: every
  * row is walked in CSR order, so equal inputs give bitwise equal outputs;

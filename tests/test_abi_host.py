@@ -219,6 +219,39 @@ def test_bwd_workspace_and_errors(lib):
     assert "4096" in _err(lib)
 
 
+def _bwd_noalloc(lib, g, scale=None, causal=0, ptrs=None, col_len=16):
+    if scale is None:
+        scale = 1.0 / math.sqrt(g.D)
+    p = [FAKE] * 11 if ptrs is None else ptrs
+    return lib.attn_block_sparse_bwd_noalloc(ctypes.byref(g), p[0], p[1], p[2], p[3], p[4], p[5],
+                                             p[6], p[7], col_len, scale, causal, p[8], p[9], p[10],
+                                             None)
+
+
+def test_bwd_noalloc_errors(lib):
+    """The no-allocation backward checks its arguments as the workspace call
+    does, and refuses a problem whose workspace exceeds its 64 MiB scratch
+    on the host (every case here fails before any HIP call)."""
+    s = _g()
+    for n in range(11):
+        ptrs = [FAKE] * 11
+        ptrs[n] = None
+        assert _bwd_noalloc(lib, s, ptrs=ptrs) == _lib.BSTA_ERR_NULL, n
+    assert _bwd_noalloc(lib, s, causal=1) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(lib, s, scale=0.5) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(lib, s, col_len=-1) == _lib.BSTA_ERR_SHAPE
+    big = _g(T=64, Y=64, X=68)
+    assert _bwd_noalloc(lib, big) == _lib.BSTA_ERR_SHAPE
+    # 64 MiB: the largest col_len whose workspace fits, and one entry more.
+    limit = 64 << 20
+    fixed = lib.attn_bwd_workspace_bytes(ctypes.byref(s), 0)
+    fits = (limit - fixed) // 4
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), fits) <= limit
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(s), fits + 64) > limit
+    assert _bwd_noalloc(lib, s, col_len=fits + 64) == _lib.BSTA_ERR_CAPACITY
+    assert "64" in _err(lib) or "67108864" in _err(lib)
+
+
 def _fwd(lib, g, scale=None, causal=0, q=FAKE, o=FAKE, rp=FAKE, col_len=16, fn="attn_block_sparse_fwd"):
     if scale is None:
         scale = 1.0 / math.sqrt(g.D)
