@@ -8,6 +8,8 @@ computes, written from the FastVideo attention-backend pages:
                     mask -> CSR index map
   * attention.py -- masked softmax attention over the selected tiles, and a
                     brute-force dense attention with an explicit token mask
+  * prune.py     -- query pruning: kept tokens per tile, the kept queries'
+                    means for the selection, attention of the kept rows
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It shares no code with the HIP path and imports nothing
