@@ -32,6 +32,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the synthetic 40-head 1200-tile workload it keeps about 10% of the key
 # tiles, the density of its top-120 selection.
 CUM_THRESHOLD = 0.15
+# Keep ratio of the query-pruning leg timed beside the step.
+PRUNE_RATIO = 0.5
 METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI355X"
 
 # Counter readings of the attention kernel on the default workload, from the
@@ -290,6 +292,44 @@ def main():
         print(f"[bench] cumulative selection {cum}", file=sys.stderr, flush=True)
         del sel_c
 
+    # Query pruning (attn_prune_queries) at keep ratio 0.5 on the tiled Q,
+    # the cumulative-threshold selection from the kept queries' means, and
+    # the pruned attention (attn_block_sparse_fwd_pruned); not part of the
+    # step.  Pruned rows are masked in the attention, not skipped.
+    pruned = None
+    if fused and nt <= 2048:
+        sel_p = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, want_mask=False, device=dev)
+        ppq, ppk = sel_p.pooled(g)
+        ppk.copy_(pk)
+        keep = torch.empty((w.B, w.H, nt), dtype=torch.int64, device=dev)
+        kcount = torch.empty((w.B, w.H, nt), dtype=torch.int32, device=dev)
+        per_p = {"prune": [], "select": [], "attn": []}
+        for _ in range(n_calls):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            bsta.attn_prune_queries(g, qt, PRUNE_RATIO, pooled=ppq, keep_mask=keep, keep_count=kcount)
+            e[1].record()
+            bsta.attn_select_cumulative(g, None, None, CUM_THRESHOLD, 0, prepooled=True, out=sel_p)
+            e[2].record()
+            bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel_p.row_ptr, sel_p.col_idx, out=o,
+                                       raster=True, keep=keep)
+            e[3].record()
+            torch.cuda.synchronize()
+            for idx, n in enumerate(per_p):
+                per_p[n].append(e[idx].elapsed_time(e[idx + 1]))
+        nnz_p = int(sel_p.row_ptr[-1].item())
+        pms = {n: float(np.median(v)) for n, v in per_p.items()}
+        q_bytes = w.B * w.H * w.D * 2 * lpad + w.B * w.H * nt * (w.D * 4 + 12)
+        pruned = {"keep_ratio": PRUNE_RATIO, "threshold": CUM_THRESHOLD,
+                  "prune_ms": pms["prune"], "prune_gbps": q_bytes / (pms["prune"] * 1e-3) / 1e9,
+                  "select_ms": pms["select"], "attn_ms": pms["attn"],
+                  "selected_tile_pairs": nnz_p,
+                  "attn_tflops_kept_rows": PRUNE_RATIO * attention_flop(w, nnz_p) / (pms["attn"] * 1e-3) / 1e12,
+                  "note": "prune (scores, ranks, kept means) + cumulative selection from the kept means + "
+                          "attention writing kept rows (pruned rows masked, not skipped); not in the step"}
+        print(f"[bench] pruned queries {pruned}", file=sys.stderr, flush=True)
+        del sel_p, keep, kcount
+
     # The backward (attn_block_sparse_bwd) on the step's selection, with a
     # seeded synthetic output gradient; not part of the step.  Its
     # algorithmic work is five products per selected pair (S, dP, dV, dQ,
@@ -387,6 +427,7 @@ def main():
             "untile": {"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
                        "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
             "select_cumulative": cum,
+            "pruned_queries": pruned,
             "attn_bwd": bwd,
         },
     }

@@ -26,6 +26,7 @@ from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, 
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
     "attn_select_cumulative", "attn_block_sparse_bwd", "attn_block_sparse_bwd_noalloc",
+    "attn_prune_queries",
     "block_sparse_attention_trainable",
     "attn_tile",
     "attn_tile_pool", "attn_untile", "attn_select_alloc",
@@ -258,12 +259,43 @@ def attn_select_cumulative(g: Geometry, q_tiled, k_tiled, threshold: float, min_
     return out
 
 
+def attn_prune_queries(g: Geometry, q_tiled, keep_ratio: float, pooled=None, keep_mask=None,
+                       keep_count=None):
+    """Query pruning: each tile keeps min(n, max(1, floor(keep_ratio * n))) of
+    its n valid query tokens, those least aligned with the tile's mean query.
+    Returns (keep_mask, keep_count, pooled): keep_mask int64 [B, H, Nt] holding
+    the 64-bit kept-slot mask of each tile (bit r = slot r), keep_count int32
+    [B, H, Nt], pooled fp32 [B, H, Nt, D] the kept queries' means.  Give
+    ``pooled`` = Selection.pooled(g)[0] to select key tiles from them."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
+    dev = q_tiled.device
+    if keep_mask is None:
+        keep_mask = torch.empty((g.B, g.H, nt), dtype=torch.int64, device=dev)
+    if keep_count is None:
+        keep_count = torch.empty((g.B, g.H, nt), dtype=torch.int32, device=dev)
+    if pooled is None:
+        pooled = torch.empty((g.B, g.H, nt, g.D), dtype=torch.float32, device=dev)
+    _expect(keep_mask, (g.B, g.H, nt), torch.int64, "keep_mask")
+    _expect(keep_count, (g.B, g.H, nt), torch.int32, "keep_count")
+    _expect(pooled, (g.B, g.H, nt, g.D), torch.float32, "pooled")
+    _lib.check(_lib.load().attn_prune_queries(ctypes.byref(g.c), _ptr(q_tiled), float(keep_ratio),
+                                              _ptr(keep_mask), _ptr(keep_count), _ptr(pooled),
+                                              _stream()))
+    return keep_mask, keep_count, pooled
+
+
 def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                           softmax_scale: Optional[float] = None, causal: bool = False,
-                          out=None, lse=None, want_lse: bool = False, raster: bool = False):
+                          out=None, lse=None, want_lse: bool = False, raster: bool = False,
+                          keep=None):
     """Block-sparse attention over the tiled tensors.  The output is tiled
     [B, Lpad, H, D], or with ``raster=True`` written straight to raster order
-    [B, L, H, D] (attn_block_sparse_fwd_raster: no separate untile pass)."""
+    [B, L, H, D] (attn_block_sparse_fwd_raster: no separate untile pass).
+    ``keep`` (the keep_mask of attn_prune_queries) restricts the output rows
+    to the kept query slots (attn_block_sparse_fwd_pruned); the others are
+    written as zeros."""
     torch = _torch()
     nt, lpad = attn_geometry(g)
     for name, t in (("q_tiled", q_tiled), ("k_tiled", k_tiled), ("v_tiled", v_tiled)):
@@ -281,6 +313,13 @@ def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_i
         lse = torch.empty((g.B, g.H, lpad), dtype=torch.float32, device=q_tiled.device)
     _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
     lib = _lib.load()
+    if keep is not None:
+        _expect(keep, (g.B, g.H, nt), torch.int64, "keep")
+        _lib.check(lib.attn_block_sparse_fwd_pruned(
+            ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(row_ptr),
+            _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(keep),
+            int(bool(raster)), _ptr(out), _ptr(lse), _stream()))
+        return (out, lse) if want_lse or lse is not None else out
     fn = lib.attn_block_sparse_fwd_raster if raster else lib.attn_block_sparse_fwd
     _lib.check(fn(
         ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(row_ptr),
@@ -358,16 +397,26 @@ def attn_set_deterministic(enable: bool) -> bool:
 
 
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,
-                           windows=None, threshold: Optional[float] = None, min_blocks: int = 0):
+                           windows=None, threshold: Optional[float] = None, min_blocks: int = 0,
+                           query_keep_ratio: Optional[float] = None):
     """The whole path on raster [B, L, H, D] tensors: tile, select, attend, untile.
     ``mode`` is SELECT_TOPK (``topk``), SELECT_STA (``windows``) or
     SELECT_CUMULATIVE (``threshold``, ``min_blocks``).  With top-k and the
     cumulative threshold Q and K are pooled while they are tiled; the
-    attention writes its output in raster order directly."""
+    attention writes its output in raster order directly.  With
+    ``query_keep_ratio`` (top-k or cumulative) the queries are pruned first
+    (attn_prune_queries): key tiles are selected from the kept queries'
+    means and pruned query rows come out as zeros."""
+    keep = None
     if mode in (SELECT_TOPK, SELECT_CUMULATIVE):
         sel = attn_select_alloc(g, mode, topk, want_mask=False, device=q.device)
         pq, pk = sel.pooled(g)
-        qt, kt = attn_tile_pool(g, q, pq), attn_tile_pool(g, k, pk)
+        if query_keep_ratio is None:
+            qt = attn_tile_pool(g, q, pq)
+        else:
+            qt = attn_tile(g, q)
+            keep, _, _ = attn_prune_queries(g, qt, query_keep_ratio, pooled=pq)
+        kt = attn_tile_pool(g, k, pk)
         vt = attn_tile(g, v)
         if mode == SELECT_TOPK:
             sel = attn_select_blocks(g, None, None, SELECT_TOPK | SELECT_PREPOOLED, topk, out=sel)
@@ -377,9 +426,12 @@ def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: 
             sel = attn_select_cumulative(g, None, None, threshold, min_blocks, prepooled=True,
                                          out=sel)
     else:
+        if query_keep_ratio is not None:
+            raise ValueError("query pruning selects from the kept queries: use SELECT_TOPK or "
+                             "SELECT_CUMULATIVE")
         qt, kt, vt = attn_tile(g, q), attn_tile(g, k), attn_tile(g, v)
         sel = attn_select_blocks(g, qt, kt, mode, topk, windows, want_mask=False)
-    return attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True)
+    return attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, raster=True, keep=keep)
 
 
 def _select_for(g: Geometry, qt, kt, mode, topk, windows, threshold, min_blocks):

@@ -31,7 +31,7 @@ EXPORTS = (
     "attn_workspace_bytes", "attn_select_blocks", "attn_select_cumulative",
     "attn_block_sparse_fwd",
     "attn_block_sparse_fwd_raster", "attn_bwd_workspace_bytes", "attn_block_sparse_bwd",
-    "attn_block_sparse_bwd_noalloc",
+    "attn_block_sparse_bwd_noalloc", "attn_prune_queries", "attn_block_sparse_fwd_pruned",
     "attn_status_string", "attn_last_error", "attn_set_deterministic",
 )
 
@@ -79,6 +79,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         P, i64, P]),
         "attn_block_sparse_bwd_noalloc": (i32, [G, P, P, P, P, P, P, P, P, i64, ctypes.c_float, i32,
                                                 P, P, P, P]),
+        "attn_prune_queries": (i32, [G, P, ctypes.c_double, P, P, P, P]),
+        "attn_block_sparse_fwd_pruned": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, i32, P,
+                                               P, P]),
         "attn_status_string": (ctypes.c_char_p, [i32]),
         "attn_last_error": (ctypes.c_char_p, []),
         "attn_set_deterministic": (i32, [i32]),

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbsta.so")
-SOURCES = ["bsta_api.hip", "tile_kernels.hip", "select_kernels.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["bsta_api.hip", "tile_kernels.hip", "select_kernels.hip", "prune_kernels.hip",
+           "attn_fwd.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

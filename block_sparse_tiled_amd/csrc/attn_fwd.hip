@@ -190,8 +190,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
         const int32_t* __restrict__ col_idx, int64_t col_len, float scale_log2,
-        __bf16* __restrict__ o, float* __restrict__ lse, int64_t items_per_xcd, int rotate,
-        int raster) {
+        __bf16* __restrict__ o, float* __restrict__ lse, const uint64_t* __restrict__ keep,
+        int64_t items_per_xcd, int rotate, int raster) {
     constexpr int NDC = D / 16;                    // MFMA k-steps for S (16 d each)
     constexpr int NDB = D / 32;                    // 32-row d blocks of O^T
     constexpr int HALF_ELEMS = 32 * D;             // one half-tile slot
@@ -643,10 +643,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
 
-        // Finalise: l is split over lanes l and l^32.
+        // Finalise: l is split over lanes l and l^32.  With a keep mask (query
+        // pruning) a row outside it is written like a pad row.
         const int ni = tile_occupancy(g, i);
         const float l_tot = l_run + wave_xor32(l_run);
-        const bool valid = qi < ni && l_tot > 0.f;
+        const bool kept = keep == nullptr || ((keep[item] >> qi) & 1) != 0;
+        const bool valid = qi < ni && l_tot > 0.f && kept;
         const float inv = valid ? 1.0f / l_tot : 0.f;
         // Output row: slot i*64 + qi of the tiled tensor, or with `raster`
         // the token that slot holds in [B, L, H, D] (a pad slot has none).
@@ -705,8 +707,8 @@ int resident_per_xcd(const void* kernel) {
 
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, bool rotate, bool raster,
-                           hipStream_t stream) {
+                           float scale, void* o, float* lse, const uint64_t* keep, bool rotate,
+                           bool raster, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     const void* kernel =
         g.D == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
@@ -718,13 +720,13 @@ hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const voi
     if (g.D == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0,
-                           raster ? 1 : 0);
+                           col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd,
+                           rotate ? 1 : 0, raster ? 1 : 0);
     else
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(128), 0, stream, g,
                            (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, items_per_xcd, rotate ? 1 : 0,
-                           raster ? 1 : 0);
+                           col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd,
+                           rotate ? 1 : 0, raster ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -41,8 +41,10 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
                            hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, bool rotate, bool raster,
-                           hipStream_t stream);
+                           float scale, void* o, float* lse, const uint64_t* keep, bool rotate,
+                           bool raster, hipStream_t stream);
+hipError_t launch_prune(const Geo& g, const void* q_tiled, double ratio, uint64_t* keep_mask,
+                        int32_t* keep_count, float* pooled_q, hipStream_t stream);
 }  // namespace bsta
 
 using bsta::Geo;
@@ -221,7 +223,8 @@ int32_t check_scale(const Geo& g, float softmax_scale, int32_t causal) {
 int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_tiled,
                          const void* k_tiled, const void* v_tiled, const int32_t* row_ptr,
                          const int32_t* col_idx, int64_t col_len, float softmax_scale,
-                         int32_t causal, void* o, float* lse, bool raster, void* stream) {
+                         int32_t causal, const uint64_t* keep, void* o, float* lse, bool raster,
+                         void* stream) {
     Geo g;
     int32_t st = make_geo(gin, &g);
     if (st != BSTA_OK) return st;
@@ -232,7 +235,7 @@ int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_t
     if (st != BSTA_OK) return st;
     if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
     return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
-                                            col_len, softmax_scale, o, lse,
+                                            col_len, softmax_scale, o, lse, keep,
                                             g_deterministic.load(std::memory_order_relaxed) == 0,
                                             raster, (hipStream_t)stream),
                       name);
@@ -405,7 +408,8 @@ int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const v
                               int64_t col_len, float softmax_scale, int32_t causal,
                               void* o_tiled, float* lse, void* stream) {
     return block_sparse_fwd("attn_block_sparse_fwd", gin, q_tiled, k_tiled, v_tiled, row_ptr,
-                            col_idx, col_len, softmax_scale, causal, o_tiled, lse, false, stream);
+                            col_idx, col_len, softmax_scale, causal, nullptr, o_tiled, lse, false,
+                            stream);
 }
 
 int32_t attn_block_sparse_fwd_raster(const bsta_geom* gin, const void* q_tiled,
@@ -414,7 +418,36 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* gin, const void* q_tiled,
                                      int64_t col_len, float softmax_scale, int32_t causal, void* o,
                                      float* lse, void* stream) {
     return block_sparse_fwd("attn_block_sparse_fwd_raster", gin, q_tiled, k_tiled, v_tiled,
-                            row_ptr, col_idx, col_len, softmax_scale, causal, o, lse, true, stream);
+                            row_ptr, col_idx, col_len, softmax_scale, causal, nullptr, o, lse, true,
+                            stream);
+}
+
+int32_t attn_prune_queries(const bsta_geom* gin, const void* q_tiled, double keep_ratio,
+                           uint64_t* keep_mask, int32_t* keep_count, float* pooled_q,
+                           void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (q_tiled == nullptr || keep_mask == nullptr || pooled_q == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_prune_queries: NULL q_tiled, keep_mask or pooled_q");
+    if (!(keep_ratio > 0.0 && keep_ratio <= 1.0))
+        return fail(BSTA_ERR_SHAPE, "keep_ratio %g outside (0, 1]", keep_ratio);
+    return hip_status(bsta::launch_prune(g, q_tiled, keep_ratio, keep_mask, keep_count, pooled_q,
+                                         (hipStream_t)stream),
+                      "attn_prune_queries");
+}
+
+int32_t attn_block_sparse_fwd_pruned(const bsta_geom* gin, const void* q_tiled,
+                                     const void* k_tiled, const void* v_tiled,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_len, float softmax_scale, int32_t causal,
+                                     const uint64_t* keep_mask, int32_t raster, void* o,
+                                     float* lse, void* stream) {
+    if (keep_mask == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd_pruned: NULL keep_mask");
+    return block_sparse_fwd("attn_block_sparse_fwd_pruned", gin, q_tiled, k_tiled, v_tiled,
+                            row_ptr, col_idx, col_len, softmax_scale, causal, keep_mask, o, lse,
+                            raster != 0, stream);
 }
 
 int64_t attn_bwd_workspace_bytes(const bsta_geom* gin, int64_t col_len) {

@@ -269,6 +269,53 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
                                      float* lse, void* stream);
 
 /*
+ * attn_prune_queries: the query half of bidirectional sparse attention
+ * ("bsa_attn" page: the introduction prunes redundant query tokens in each
+ * block; forward prunes the query blocks at a keep ratio, selects key-value
+ * blocks from the kept queries and attends with them only).  The page shows
+ * the calls, not the rule; the rule here: a tile with n valid tokens keeps
+ * c = min(n, max(1, floor(keep_ratio * n))) of them, those with the lowest
+ * cos(q_r, m), m the mean of the tile's valid queries of that head (0 when
+ * either vector is zero), ties to the lower slot.
+ *   q_tiled    [in]  bf16 [B, Lpad, H, D] tiled queries
+ *   keep_ratio [in]  in (0, 1] (host double; floor(keep_ratio * n) is taken
+ *              in double precision)
+ *   keep_mask  [out] uint64 [B, H, Nt]: bit r set iff slot r of the tile is
+ *              kept (pad slots never are)
+ *   keep_count [out] int32 [B, H, Nt] kept tokens per tile, or NULL
+ *   pooled_q   [out] fp32 [B, H, Nt, D]: the mean of each tile's kept
+ *              queries (fp32 sum in slot order, one division).  Pass the
+ *              pooled-Q part of a selection workspace (the first
+ *              B*H*Nt*D floats) and pool K with attn_tile_pool into the
+ *              second part; attn_select_blocks (BSTA_SELECT_TOPK |
+ *              BSTA_SELECT_PREPOOLED) or attn_select_cumulative (prepooled)
+ *              then select key tiles from the kept queries.
+ * Errors: ERR_NULL (q_tiled, keep_mask or pooled_q NULL), ERR_SHAPE (ratio
+ * outside (0, 1]), ERR_UNSUPPORTED (geometry), ERR_HIP.  One wave per
+ * (batch, head, tile); computed in fp32.
+ */
+int32_t attn_prune_queries(const bsta_geom* g, const void* q_tiled, double keep_ratio,
+                           uint64_t* keep_mask, int32_t* keep_count, float* pooled_q,
+                           void* stream);
+
+/*
+ * attn_block_sparse_fwd_pruned: attn_block_sparse_fwd (raster = 0) or
+ * attn_block_sparse_fwd_raster (raster != 0) for pruned queries: only slots
+ * in keep_mask (from attn_prune_queries) are output rows; every other slot
+ * is written as +0.0 with lse = -inf, as the "bsa_attn" page's forward
+ * restores full length from the kept positions (reading: pruned positions
+ * hold zero).  Arguments otherwise as attn_block_sparse_fwd; keep_mask is
+ * uint64 [B, H, Nt] on the device (ERR_NULL if NULL).  Pruned rows are
+ * masked, not skipped: the call costs what the unpruned one does.
+ */
+int32_t attn_block_sparse_fwd_pruned(const bsta_geom* g, const void* q_tiled,
+                                     const void* k_tiled, const void* v_tiled,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_len, float softmax_scale, int32_t causal,
+                                     const uint64_t* keep_mask, int32_t raster, void* o,
+                                     float* lse, void* stream);
+
+/*
  * attn_bwd_workspace_bytes (host only): bytes of device workspace
  * attn_block_sparse_bwd needs for a CSR of col_len entries (per-query
  * rowsum(dO*O) and the CSR's transpose); a negative status on bad arguments.

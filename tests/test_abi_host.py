@@ -187,6 +187,28 @@ def test_cumulative_errors(lib):
     assert "attn_select_cumulative" in _err(lib)
 
 
+def test_prune_errors(lib):
+    """Query pruning and the pruned forward check their arguments on the host."""
+    g = _g()
+    prune = lambda q=FAKE, ratio=0.5, km=FAKE, pq=FAKE, gg=g: lib.attn_prune_queries(  # noqa: E731
+        ctypes.byref(gg), q, ratio, km, None, pq, None)
+    for bad in (0.0, -0.5, 1.0000001, float("nan"), float("inf")):
+        assert prune(ratio=bad) == _lib.BSTA_ERR_SHAPE, bad
+        assert "keep_ratio" in _err(lib)
+    assert prune(q=None) == _lib.BSTA_ERR_NULL
+    assert prune(km=None) == _lib.BSTA_ERR_NULL
+    assert prune(pq=None) == _lib.BSTA_ERR_NULL
+    assert prune(gg=_g(D=96)) == _lib.BSTA_ERR_UNSUPPORTED
+    scale = 1.0 / math.sqrt(g.D)
+    fwd = lambda keep=FAKE, causal=0, sc=scale, q=FAKE: lib.attn_block_sparse_fwd_pruned(  # noqa: E731
+        ctypes.byref(g), q, FAKE, FAKE, FAKE, FAKE, 16, sc, causal, keep, 1, FAKE, None, None)
+    assert fwd(keep=None) == _lib.BSTA_ERR_NULL
+    assert "keep_mask" in _err(lib)
+    assert fwd(causal=1) == _lib.BSTA_ERR_UNSUPPORTED
+    assert fwd(sc=0.5) == _lib.BSTA_ERR_UNSUPPORTED
+    assert fwd(q=None) == _lib.BSTA_ERR_NULL
+
+
 def _bwd(lib, g, scale=None, causal=0, ptrs=None, col_len=16, ws=FAKE, wsb=10 ** 12):
     if scale is None:
         scale = 1.0 / math.sqrt(g.D)
