@@ -36,7 +36,7 @@ def tile_attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: flo
     return o, lse
 
 
-def block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale=None, rows=None):
+def block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale=None, rows=None, tile=geometry.TILE):
     """Attention of tile-ordered [B, Lpad, H, D] tensors under a block mask.
 
     mask: bool [B, H, Nt, Nt].  rows: optional list of (b, h, i) query tiles
@@ -44,8 +44,8 @@ def block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale=None, rows=None):
     float64 [B, Lpad, H, D] and lse float64 [B, H, Lpad].
     """
     B, lpad, H, D = qt.shape
-    E = geometry.TILE_ELEMS
-    occ = geometry.occupancy(T, Y, X)
+    E = geometry.tile_elems(tile)
+    occ = geometry.occupancy(T, Y, X, tile)
     nt = len(occ)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -125,7 +125,7 @@ def block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X, scale=None):
     return dq, dk, dv
 
 
-def dense_masked_attention(q, k, v, mask, T, Y, X, scale=None):
+def dense_masked_attention(q, k, v, mask, T, Y, X, scale=None, tile=geometry.TILE):
     """Brute force in raster order with an explicit L x L 0/-inf token mask.
 
     q, k, v: [B, L, H, D]; mask: bool block mask [B, H, Nt, Nt].  The token
@@ -135,7 +135,7 @@ def dense_masked_attention(q, k, v, mask, T, Y, X, scale=None):
     B, L, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    tid = geometry.token_tile_ids(T, Y, X)
+    tid = geometry.token_tile_ids(T, Y, X, tile)
     out = np.empty((B, L, H, D), dtype=np.float64)
     lse = np.empty((B, H, L), dtype=np.float64)
     for b in range(B):

@@ -30,6 +30,15 @@ import numpy as np
 
 TILE = (4, 4, 4)
 TILE_ELEMS = TILE[0] * TILE[1] * TILE[2]
+# Tile shapes by token count.  The "video_sparse_attn_h3" page keys its tile
+# registry by 64 and 128 tokens without printing the shapes; reading: the
+# 64-token tile is 4x4x4 (the configurations') and the 128-token tile doubles
+# the innermost (width) axis, 4x4x8.
+TILE_SHAPES = {64: (4, 4, 4), 128: (4, 4, 8)}
+
+
+def tile_elems(tile=TILE) -> int:
+    return tile[0] * tile[1] * tile[2]
 
 
 def tile_counts(T: int, Y: int, X: int, tile=TILE):

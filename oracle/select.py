@@ -38,11 +38,11 @@ import numpy as np
 from . import geometry
 
 
-def pool(xt: np.ndarray, T: int, Y: int, X: int) -> np.ndarray:
+def pool(xt: np.ndarray, T: int, Y: int, X: int, tile=geometry.TILE) -> np.ndarray:
     """Mean of the valid rows of every tile: [B, Lpad, H, D] -> f32 [B, H, Nt, D]."""
     B, lpad, H, D = xt.shape
-    E = geometry.TILE_ELEMS
-    occ = geometry.occupancy(T, Y, X)
+    E = geometry.tile_elems(tile)
+    occ = geometry.occupancy(T, Y, X, tile)
     out = np.empty((B, H, len(occ), D), dtype=np.float32)
     for j, n in enumerate(occ):
         rows = xt[:, j * E:j * E + n].astype(np.float64)     # [B, n, H, D]
@@ -139,10 +139,10 @@ def sta_window_start(a: int, w: int, n: int) -> int:
     return min(max(a - w // 2, 0), n - w)
 
 
-def sta_mask(T: int, Y: int, X: int, windows: np.ndarray, B: int) -> np.ndarray:
+def sta_mask(T: int, Y: int, X: int, windows: np.ndarray, B: int, tile=geometry.TILE) -> np.ndarray:
     """Block mask of per-head sliding tile windows: bool [B, H, Nt, Nt]."""
-    n = geometry.tile_counts(T, Y, X)
-    coords = geometry.tile_coords(T, Y, X)
+    n = geometry.tile_counts(T, Y, X, tile)
+    coords = geometry.tile_coords(T, Y, X, tile)
     nt = len(coords)
     H = len(windows)
     mask = np.zeros((H, nt, nt), dtype=bool)

@@ -13,19 +13,19 @@ import numpy as np
 from . import geometry
 
 
-def tile(x: np.ndarray, T: int, Y: int, X: int) -> np.ndarray:
+def tile(x: np.ndarray, T: int, Y: int, X: int, tile=geometry.TILE) -> np.ndarray:
     """[B, L, H, D] raster -> [B, Lpad, H, D] tile order, pad slots zero."""
     B, L, H, D = x.shape
     if L != T * Y * X:
         raise ValueError(f"sequence length {L} does not match grid {T}x{Y}x{X}")
-    lpad = geometry.padded_len(T, Y, X)
+    lpad = geometry.padded_len(T, Y, X, tile)
     out = np.zeros((B, lpad, H, D), dtype=x.dtype)
-    out[:, geometry.token_slots(T, Y, X)] = x
+    out[:, geometry.token_slots(T, Y, X, tile)] = x
     return out
 
 
-def untile(xt: np.ndarray, T: int, Y: int, X: int) -> np.ndarray:
+def untile(xt: np.ndarray, T: int, Y: int, X: int, tile=geometry.TILE) -> np.ndarray:
     """[B, Lpad, H, D] tile order -> [B, L, H, D] raster; pad slots dropped."""
-    if xt.shape[1] != geometry.padded_len(T, Y, X):
+    if xt.shape[1] != geometry.padded_len(T, Y, X, tile):
         raise ValueError("padded length does not match the grid")
-    return xt[:, geometry.token_slots(T, Y, X)]
+    return xt[:, geometry.token_slots(T, Y, X, tile)]

@@ -642,3 +642,93 @@ def test_sta_full_window_equals_dense():
     ref = torch.nn.functional.scaled_dot_product_attention(
         *(torch.from_numpy(a).permute(0, 2, 1, 3) for a in (qf, kf, vf))).permute(0, 2, 1, 3).numpy()
     assert np.allclose(res["out"], ref, rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------- 128-token tiles
+
+T448 = geometry.TILE_SHAPES[128]
+
+
+def test_tile128_partition_golden():
+    g = _golden("geometry_examples.json")["partition_2x3x10_tile448"]
+    assert tuple(g["tile"]) == T448
+    T, Y, X = g["grid"]
+    assert list(geometry.tile_order(T, Y, X, T448)) == g["tile_order"]
+    assert list(geometry.occupancy(T, Y, X, T448)) == g["occupancy"]
+    assert geometry.padded_len(T, Y, X, T448) == 2 * 128
+
+
+def test_tile128_occupancy_histogram_golden():
+    g = _golden("geometry_examples.json")["occupancy_21x30x52_tile448"]
+    T, Y, X = g["grid"]
+    assert geometry.tile_counts(T, Y, X, T448) == tuple(g["tile_counts"])
+    vals, counts = np.unique(geometry.occupancy(T, Y, X, T448), return_counts=True)
+    assert {str(v): int(c) for v, c in zip(vals, counts)} == g["histogram"]
+
+
+@pytest.mark.parametrize("grid", [(8, 8, 16), (4, 12, 24)])
+def test_tile128_divisible_equals_rearrange(grid):
+    """Divisible grid: "(nt 4)(ny 4)(nx 8) -> (nt ny nx)(4 4 8)"."""
+    T, Y, X = grid
+    ids = np.arange(T * Y * X).reshape(T // 4, 4, Y // 4, 4, X // 8, 8)
+    expected = ids.transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+    assert np.array_equal(geometry.tile_order(T, Y, X, T448), expected)
+    assert np.array_equal(geometry.token_slots(T, Y, X, T448), np.argsort(expected))
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (3, 9, 19), (1, 1, 1), (6, 5, 17)])
+def test_tile128_brute_force_and_closed_forms(grid):
+    """Tile id and rank by counting in raster order; occupancy and slot from
+    the per-axis extents min(4, .), min(4, .), min(8, .)."""
+    T, Y, X = grid
+    ny, nx = math.ceil(Y / 4), math.ceil(X / 8)
+    slots = geometry.token_slots(T, Y, X, T448)
+    occ = geometry.occupancy(T, Y, X, T448)
+    counts = np.zeros(len(occ), dtype=np.int64)
+    for l in range(T * Y * X):
+        t, rem = divmod(l, Y * X)
+        y, x = divmod(rem, X)
+        a, b, c = t // 4, y // 4, x // 8
+        j = (a * ny + b) * nx + c
+        sy, sx = min(4, Y - 4 * b), min(8, X - 8 * c)
+        assert slots[l] == 128 * j + counts[j]
+        assert slots[l] == 128 * j + ((t % 4) * sy + y % 4) * sx + x % 8
+        counts[j] += 1
+    assert np.array_equal(counts, occ)
+    for j in range(len(occ)):
+        a, rest = divmod(j, ny * nx)
+        b, c = divmod(rest, nx)
+        assert occ[j] == min(4, T - 4 * a) * min(4, Y - 4 * b) * min(8, X - 8 * c)
+
+
+def test_tile128_pool_and_attention_brute_force():
+    """128-token tiles through pooling (grouped float64 sums), top-k and the
+    attention, against a dense float64 brute force with the explicit token
+    mask; all tiles selected equals plain softmax attention."""
+    rng = np.random.default_rng(81)
+    T, Y, X = 5, 6, 19
+    B, Hh, D = 1, 2, 16
+    L = T * Y * X
+    q, k, v = (rng.standard_normal((B, L, Hh, D)) for _ in range(3))
+    qt, kt, vt = (tiling.tile(x, T, Y, X, T448) for x in (q, k, v))
+    assert np.array_equal(tiling.untile(qt, T, Y, X, T448), q)
+    tid = geometry.token_tile_ids(T, Y, X, T448)
+    nt = geometry.num_tiles(T, Y, X, T448)
+    sums = np.zeros((nt, Hh, D))
+    np.add.at(sums, tid, q[0])
+    want = (sums / np.bincount(tid)[:, None, None]).astype(np.float32).transpose(1, 0, 2)
+    pq = select.pool(qt, T, Y, X, T448)
+    assert np.array_equal(pq[0], want)
+    s = select.scores(pq, select.pool(kt, T, Y, X, T448))
+    mask = select.topk_mask(s, 2)
+    out_t, lse_t = attention.block_sparse_attention(qt, kt, vt, mask, T, Y, X, tile=T448)
+    dense, dlse = attention.dense_masked_attention(q, k, v, mask, T, Y, X, tile=T448)
+    slots = geometry.token_slots(T, Y, X, T448)
+    assert np.allclose(out_t[:, slots], dense, rtol=0, atol=1e-12)
+    assert np.allclose(lse_t[:, :, slots], dlse, rtol=0, atol=1e-12)
+    full = np.ones((B, Hh, nt, nt), dtype=bool)
+    out_f, _ = attention.block_sparse_attention(qt, kt, vt, full, T, Y, X, tile=T448)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.transpose(0, 2, 1, 3)), torch.from_numpy(k.transpose(0, 2, 1, 3)),
+        torch.from_numpy(v.transpose(0, 2, 1, 3))).numpy().transpose(0, 2, 1, 3)
+    assert np.allclose(tiling.untile(out_f, T, Y, X, T448), ref, rtol=0, atol=1e-10)
