@@ -330,6 +330,49 @@ def main():
         print(f"[bench] pruned queries {pruned}", file=sys.stderr, flush=True)
         del sel_p, keep, kcount
 
+    # 128-token tiles (4x4x8) on the same raster inputs: the step's calls with
+    # a geometry of half as many tiles and top-k halved (same density); not
+    # part of the step.
+    t128 = None
+    if w.mode == "topk":
+        g8 = bsta.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X, tile_x=8)
+        nt8, lpad8 = bsta.attn_geometry(g8)
+        k8 = max(1, min(nt8, w.topk * nt8 // nt))
+        qt8, kt8, vt8 = (torch.empty((w.B, lpad8, w.H, w.D), dtype=torch.bfloat16, device=dev)
+                         for _ in range(3))
+        sel8 = bsta.attn_select_alloc(g8, bsta.SELECT_TOPK, k8, want_mask=False, device=dev)
+        pq8, pk8 = sel8.pooled(g8)
+        per8 = {"tile_qkv": [], "select": [], "attn_fwd": []}
+        for it in range(n_calls + 2):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            bsta.attn_tile_pool(g8, q, pq8, out=qt8)
+            bsta.attn_tile_pool(g8, k, pk8, out=kt8)
+            bsta.attn_tile(g8, v, out=vt8)
+            e[1].record()
+            bsta.attn_select_blocks(g8, None, None, bsta.SELECT_TOPK | bsta.SELECT_PREPOOLED, k8,
+                                    out=sel8)
+            e[2].record()
+            bsta.attn_block_sparse_fwd(g8, qt8, kt8, vt8, sel8.row_ptr, sel8.col_idx, out=o,
+                                       raster=True)
+            e[3].record()
+            torch.cuda.synchronize()
+            if it >= 2:
+                for idx, n in enumerate(per8):
+                    per8[n].append(e[idx].elapsed_time(e[idx + 1]))
+        nnz8 = int(sel8.row_ptr[-1].item())
+        ms8 = {n: float(np.median(v_)) for n, v_ in per8.items()}
+        flop8 = 4.0 * w.D * 128 * 128 * nnz8
+        t128 = {"tile": [4, 4, 8], "tiles": nt8, "topk": k8, "selected_tile_pairs": nnz8,
+                "tile_qkv_ms": ms8["tile_qkv"], "select_ms": ms8["select"],
+                "attn_ms": ms8["attn_fwd"],
+                "attn_tflops": flop8 / (ms8["attn_fwd"] * 1e-3) / 1e12,
+                "attn_frac_mfma_peak": flop8 / (ms8["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "note": "128-token tiles: tile_pool/tile, top-k from pooled, raster attention "
+                        "(each 128-key tile = two 64-key units); not in the step"}
+        print(f"[bench] 128-token tiles {t128}", file=sys.stderr, flush=True)
+        del qt8, kt8, vt8, sel8
+
     # The backward (attn_block_sparse_bwd) on the step's selection, with a
     # seeded synthetic output gradient; not part of the step.  Its
     # algorithmic work is five products per selected pair (S, dP, dV, dQ,
@@ -428,6 +471,7 @@ def main():
                        "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
             "select_cumulative": cum,
             "pruned_queries": pruned,
+            "tile128": t128,
             "attn_bwd": bwd,
         },
     }

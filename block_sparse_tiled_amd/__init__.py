@@ -37,16 +37,20 @@ __all__ = [
 
 @dataclasses.dataclass(frozen=True)
 class Geometry:
+    """Batch, heads, head dim and the (T, Y, X) latent grid.  ``tile_x`` is
+    the tile's extent along X: 4 (4x4x4 = 64-token tiles, the default) or 8
+    (4x4x8 = 128-token tiles)."""
     B: int
     H: int
     D: int
     T: int
     Y: int
     X: int
+    tile_x: int = 4
 
     @property
     def c(self) -> _lib.Geom:
-        return _lib.geom(self.B, self.H, self.D, self.T, self.Y, self.X)
+        return _lib.geom(self.B, self.H, self.D, self.T, self.Y, self.X, self.tile_x)
 
     @property
     def L(self) -> int:

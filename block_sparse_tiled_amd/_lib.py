@@ -101,5 +101,5 @@ def check(status: int) -> int:
     return status
 
 
-def geom(B, H, D, T, Y, X) -> Geom:
-    return Geom(int(B), int(H), int(D), int(T), int(Y), int(X), 4, 4, 4)
+def geom(B, H, D, T, Y, X, tile_x=4) -> Geom:
+    return Geom(int(B), int(H), int(D), int(T), int(Y), int(X), 4, 4, int(tile_x))

@@ -185,7 +185,11 @@ __device__ inline uint32_t read_sweep(const unsigned int* ctr) {
 
 }  // namespace
 
-template <int D>
+// SUB = 64-slot units per tile: 1 for 64-token tiles, 2 for 128-token tiles.
+// With 128-token tiles a work item is one 64-row unit of a query tile (the
+// two units of a tile share its CSR row), and each CSR entry j stands for the
+// key units 2j and 2j+1, walked as consecutive key steps.
+template <int D, int SUB>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
@@ -211,7 +215,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t rs = (int64_t)g.H * D;  // elements between consecutive tokens
     const int64_t rs2 = rs * 2;           // bytes
-    const bool all_full = (g.T & 3) == 0 && (g.Y & 3) == 0 && (g.X & 3) == 0;
+    const bool all_full = (g.T & 3) == 0 && (g.Y & 3) == 0 && (g.X & (g.tx - 1)) == 0;
+    const int NU = g.Nt * SUB;  // 64-slot units per (batch, head)
 
     // Per-lane DMA source offsets (bytes, relative to the half-tile's first
     // row) of blocks 0..3: block u covers slot bytes [1024u, 1024u+1024),
@@ -259,7 +264,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int S = gridDim.x >> 3;
-    const int64_t n_items = (int64_t)g.B * g.H * g.Nt;
+    const int64_t n_rows = (int64_t)g.B * g.H * g.Nt;  // CSR rows
+    const int64_t n_items = n_rows * SUB;
     const int64_t first = (int64_t)xcd * items_per_xcd;
     const int64_t last = first + items_per_xcd < n_items ? first + items_per_xcd : n_items;
 
@@ -274,9 +280,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // then touch neighbouring key ids whatever their start times.  Any
     // rotation visits the same set of keys, so only rounding depends on it.
     unsigned int* const sweep = &g_sweep[xcd * 32];
-    int64_t nnz = rp_s[n_items];
+    int64_t nnz = rp_s[n_rows];
     nnz = nnz < 0 ? 0 : (nnz > col_len ? col_len : nnz);
-    const uint64_t per_raw = (uint64_t)S * (uint64_t)nnz / (uint64_t)(n_items > 0 ? n_items : 1);
+    const uint64_t per_raw = (uint64_t)S * SUB * (uint64_t)nnz / (uint64_t)(n_rows > 0 ? n_rows : 1);
     const uint32_t period = per_raw == 0 ? 1u : (per_raw > 0x7fffffffu ? 0x7fffffffu : (uint32_t)per_raw);
     // Wave 0 hands each item's rotation start to wave 1 through the first
     // word of the last ring slot: between an item's final barrier and the
@@ -286,18 +292,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int* const handoff = (int*)&ring[(kRing - 1) * HALF_ELEMS];
 
     for (int64_t item = first + slot; item < last; item += S) {
-        const int bh = (int)(item / g.Nt);
-        const int i = (int)(item - (int64_t)bh * g.Nt);
+        const int bh = (int)(item / NU);
+        const int i = (int)(item - (int64_t)bh * NU);  // query unit
         const int b = bh / g.H, h = bh - b * g.H;
         const int64_t head_off = (int64_t)h * D;
         const int64_t batch_row0 = (int64_t)b * g.Lpad;
         const uint64_t kbase = (uint64_t)(uintptr_t)(k + batch_row0 * rs + head_off);
         const uint64_t vbase = (uint64_t)(uintptr_t)(v + batch_row0 * rs + head_off);
 
-        int64_t p0 = rp_s[item], p1 = rp_s[item + 1];
+        const int64_t row = (int64_t)bh * g.Nt + i / SUB;
+        int64_t p0 = rp_s[row], p1 = rp_s[row + 1];
         p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
         p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
-        const int n = (int)(p1 - p0);
+        const int ne = (int)(p1 - p0);  // CSR entries
+        const int n = ne * SUB;         // key steps
 
         // Rotation start k0: the number of the row's entries below the sweep
         // target, i.e. for a sorted row the first entry at or above it (any
@@ -309,21 +317,25 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // Both waves read the same ids and reach the same verdict.
         bool clean = all_full;
         if (all_full) {
-            for (int base = 0; base < n; base += 64) {
+            for (int base = 0; base < ne; base += 64) {
                 const int idx = base + lane;
-                const int j = idx < n ? col_idx[p0 + idx] : 0;
+                const int j = idx < ne ? col_idx[p0 + idx] : 0;
                 clean = clean && __builtin_amdgcn_ballot_w64((unsigned)j >= (unsigned)g.Nt) == 0;
             }
         }
         if (rotate && n > 1) {  // workgroup-uniform
             if (wave == 0) {
                 const uint32_t c = read_sweep(sweep);
-                const int target = sweep_target(c, period, g.Nt);
+                const int target = sweep_target(c, period, NU);
+                // Key units below the target (entry j stands for units
+                // SUB*j .. SUB*j + SUB-1).
                 int cnt = 0;
-                for (int base = 0; base < n; base += 64) {
+                for (int base = 0; base < ne; base += 64) {
                     const int idx = base + lane;
-                    const int j = idx < n ? col_idx[p0 + idx] : 0x7fffffff;
-                    cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(j < target));
+                    const int j = idx < ne ? col_idx[p0 + idx] : 0x3fffffff;
+#pragma unroll
+                    for (int u = 0; u < SUB; ++u)
+                        cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(SUB * j + u < target));
                 }
                 if (lane == 0) *handoff = cnt < n ? cnt : 0;
             }
@@ -339,8 +351,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         auto tile_id = [&](int t) -> int {
             if (t >= n) return -1;
             const int r = t + k0 < n ? t + k0 : t + k0 - n;
-            const int j = ci_s[p0 + r];
-            return (unsigned)j < (unsigned)g.Nt ? j : -1;
+            const int j = ci_s[p0 + r / SUB];
+            return (unsigned)j < (unsigned)g.Nt ? j * SUB + r % SUB : -1;
         };
         // Byte offset of a tile's first row from the head's base.
         auto tile_bytes = [&](int j) -> uint64_t { return (uint64_t)((int64_t)(j < 0 ? 0 : j) * 64 * rs2); };
@@ -432,7 +444,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint32_t slot_ = ring0 + (uint32_t)my_slot * SLOT_BYTES;                     \
         if (do_k) {                                                                        \
             off_km1 = off_k;                                                               \
-            off_k = (unsigned)jraw2 < (unsigned)g.Nt ? (uint64_t)jraw2 * tile_stride : 0;   \
+            off_k = (unsigned)jraw2 < (unsigned)g.Nt                                       \
+                        ? (uint64_t)(jraw2 * SUB + (r2 % SUB)) * tile_stride : 0;            \
             dma_half<D>(kbase + off_k + hi_off, rows16, koff, slot_);                      \
         } else {                                                                           \
             dma_half<D>(vbase + off_km1 + hi_off, rows16, voff, slot_);                    \
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // (kb, r): 32kb + 8(r/4) + 4half + r%4, compared as
         // 4half >= n_j - (32kb + 8(r/4) + r%4) with a scalar right side.
         auto mask = [&](f32x16 (&sc)[2], int j) {
-            const int nj = j < 0 ? 0 : (all_full ? 64 : tile_occupancy(g, j));
+            const int nj = j < 0 ? 0 : (all_full ? 64 : unit_occupancy(g, j));
             if (nj < 64) {  // tile-uniform
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bool steady = t + 2 < n;
             // Raw id of tile t+2 (checked after the barrier, so that the
             // scalar load's latency hides behind the waits).
-            const int jraw2 = steady ? rowp[r2] : -1;
+            const int jraw2 = steady ? rowp[r2 / SUB] : -1;
             // Probabilities of tile t, overlapped with the scores of tile t+1.
             bf16x8 pf[4];
             float ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // Finalise: l is split over lanes l and l^32.  With a keep mask (query
         // pruning) a row outside it is written like a pad row.
-        const int ni = tile_occupancy(g, i);
+        const int ni = unit_occupancy(g, i);
         const float l_tot = l_run + wave_xor32(l_run);
         const bool kept = keep == nullptr || ((keep[item] >> qi) & 1) != 0;
         const bool valid = qi < ni && l_tot > 0.f && kept;
@@ -682,13 +695,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 namespace {
 
 // Workgroups of the attention kernel resident per XCD on the current device
-// (computed once per device and kernel).  Host threads may race here: each
-// entry is an atomic, and racing threads store the same value.
-int resident_per_xcd(const void* kernel) {
-    static std::atomic<int> cache[2][64] = {};
+// (computed once per device and kernel variant).  Host threads may race here:
+// each entry is an atomic, and racing threads store the same value.
+int resident_per_xcd(const void* kernel, int which) {
+    static std::atomic<int> cache[4][64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 16;
-    const int which = kernel == (const void*)attn_fwd_kernel<128> ? 0 : 1;
     const int known = cache[which][dev].load(std::memory_order_relaxed);
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
@@ -703,31 +715,42 @@ int resident_per_xcd(const void* kernel) {
     return r;
 }
 
+template <int D, int SUB>
+hipError_t launch_variant(const Geo& g, const void* q, const void* k, const void* v,
+                          const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
+                          float scale_log2, void* o, float* lse, const uint64_t* keep, bool rotate,
+                          bool raster, hipStream_t stream) {
+    const void* kernel = (const void*)attn_fwd_kernel<D, SUB>;
+    const int64_t n_items = (int64_t)g.B * g.H * g.Nt * SUB;
+    const int64_t items_per_xcd = (n_items + 7) / 8;
+    int64_t per_xcd = resident_per_xcd(kernel, (D == 128 ? 0 : 1) + (SUB == 2 ? 2 : 0));
+    if (per_xcd > items_per_xcd) per_xcd = items_per_xcd;
+    const unsigned blocks = (unsigned)(8 * per_xcd);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, SUB>), dim3(blocks), dim3(128), 0, stream, g,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                       col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd, rotate ? 1 : 0,
+                       raster ? 1 : 0);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
                            float scale, void* o, float* lse, const uint64_t* keep, bool rotate,
                            bool raster, hipStream_t stream) {
-    const float scale_log2 = scale * 1.4426950408889634f;
-    const void* kernel =
-        g.D == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
-    const int64_t n_items = (int64_t)g.B * g.H * g.Nt;
-    const int64_t items_per_xcd = (n_items + 7) / 8;
-    int64_t per_xcd = resident_per_xcd(kernel);
-    if (per_xcd > items_per_xcd) per_xcd = items_per_xcd;
-    const unsigned blocks = (unsigned)(8 * per_xcd);
+    const float sl2 = scale * 1.4426950408889634f;
+    if (g.D == 128 && g.sub == 1)
+        return launch_variant<128, 1>(g, q, k, v, row_ptr, col_idx, col_len, sl2, o, lse, keep,
+                                      rotate, raster, stream);
+    if (g.D == 64 && g.sub == 1)
+        return launch_variant<64, 1>(g, q, k, v, row_ptr, col_idx, col_len, sl2, o, lse, keep,
+                                     rotate, raster, stream);
     if (g.D == 128)
-        hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(blocks), dim3(128), 0, stream, g,
-                           (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd,
-                           rotate ? 1 : 0, raster ? 1 : 0);
-    else
-        hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(blocks), dim3(128), 0, stream, g,
-                           (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                           col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd,
-                           rotate ? 1 : 0, raster ? 1 : 0);
-    return hipGetLastError();
+        return launch_variant<128, 2>(g, q, k, v, row_ptr, col_idx, col_len, sl2, o, lse, keep,
+                                      rotate, raster, stream);
+    return launch_variant<64, 2>(g, q, k, v, row_ptr, col_idx, col_len, sl2, o, lse, keep, rotate,
+                                 raster, stream);
 }
 
 }  // namespace bsta

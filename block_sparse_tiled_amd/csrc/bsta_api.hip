@@ -89,8 +89,9 @@ int32_t hip_status(hipError_t e, const char* what) {
 // Validate a geometry and fill the derived fields.
 int32_t make_geo(const bsta_geom* in, Geo* g) {
     if (in == nullptr) return fail(BSTA_ERR_NULL, "geometry pointer is NULL");
-    if (in->tile_t != 4 || in->tile_y != 4 || in->tile_x != 4)
-        return fail(BSTA_ERR_UNSUPPORTED, "tile %dx%dx%d unsupported: only 4x4x4 (64 tokens)",
+    if (in->tile_t != 4 || in->tile_y != 4 || (in->tile_x != 4 && in->tile_x != 8))
+        return fail(BSTA_ERR_UNSUPPORTED,
+                    "tile %dx%dx%d unsupported: 4x4x4 (64 tokens) or 4x4x8 (128 tokens)",
                     in->tile_t, in->tile_y, in->tile_x);
     if (in->D != 64 && in->D != 128)
         return fail(BSTA_ERR_UNSUPPORTED, "head dim D=%d unsupported: must be 64 or 128", in->D);
@@ -105,14 +106,19 @@ int32_t make_geo(const bsta_geom* in, Geo* g) {
     g->T = in->T;
     g->Y = in->Y;
     g->X = in->X;
+    g->tx = in->tile_x;
+    g->lx = in->tile_x == 8 ? 3 : 2;
+    g->E = 16 * in->tile_x;
+    g->le = in->tile_x == 8 ? 7 : 6;
+    g->sub = g->E / 64;
     g->nT = (in->T + 3) / 4;
     g->nY = (in->Y + 3) / 4;
-    g->nX = (in->X + 3) / 4;
+    g->nX = (in->X + g->tx - 1) / g->tx;
     const int64_t nt = (int64_t)g->nT * g->nY * g->nX;
     if (nt > (1 << 26)) return fail(BSTA_ERR_SHAPE, "tile count %lld too large", (long long)nt);
     g->Nt = (int32_t)nt;
     g->L = (int64_t)in->T * in->Y * in->X;
-    g->Lpad = nt * 64;
+    g->Lpad = nt * g->E;
     // Offsets are 64-bit in the kernels; keep every element count well
     // inside int64 and grid sizes inside 32 bits.
     const double elems = (double)g->B * (double)g->Lpad * (double)g->H * (double)g->D;
@@ -430,6 +436,8 @@ int32_t attn_prune_queries(const bsta_geom* gin, const void* q_tiled, double kee
     if (st != BSTA_OK) return st;
     if (q_tiled == nullptr || keep_mask == nullptr || pooled_q == nullptr)
         return fail(BSTA_ERR_NULL, "attn_prune_queries: NULL q_tiled, keep_mask or pooled_q");
+    if (g.tx != 4)
+        return fail(BSTA_ERR_UNSUPPORTED, "attn_prune_queries: 64-token tiles only (4x4x4)");
     if (!(keep_ratio > 0.0 && keep_ratio <= 1.0))
         return fail(BSTA_ERR_SHAPE, "keep_ratio %g outside (0, 1]", keep_ratio);
     return hip_status(bsta::launch_prune(g, q_tiled, keep_ratio, keep_mask, keep_count, pooled_q,
@@ -445,6 +453,8 @@ int32_t attn_block_sparse_fwd_pruned(const bsta_geom* gin, const void* q_tiled,
                                      float* lse, void* stream) {
     if (keep_mask == nullptr)
         return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd_pruned: NULL keep_mask");
+    if (gin != nullptr && gin->tile_x != 4)
+        return fail(BSTA_ERR_UNSUPPORTED, "attn_block_sparse_fwd_pruned: 64-token tiles only");
     return block_sparse_fwd("attn_block_sparse_fwd_pruned", gin, q_tiled, k_tiled, v_tiled,
                             row_ptr, col_idx, col_len, softmax_scale, causal, keep_mask, o, lse,
                             raster != 0, stream);
@@ -483,6 +493,8 @@ int32_t check_bwd(const bsta_geom* gin, Geo* g, const void* q_tiled, const void*
     if (g->Nt > kMaxBwdTiles)
         return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
                     g->Nt);
+    if (g->tx != 4)
+        return fail(BSTA_ERR_UNSUPPORTED, "%s: 64-token tiles only (4x4x4)", who);
     return BSTA_OK;
 }
 

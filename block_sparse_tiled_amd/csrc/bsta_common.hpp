@@ -28,18 +28,26 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Plain-old-data geometry passed by value to every kernel.
+// Plain-old-data geometry passed by value to every kernel.  Tiles are
+// 4 x 4 x tx tokens with tx = 4 (64 tokens) or 8 (128 tokens, reading of the
+// "video_sparse_attn_h3" page's tile registry: the width axis doubled).  A
+// tile owns E = 16*tx consecutive slots; kernels that work on 64-slot units
+// see a 128-token tile as two units (sub = E / 64).
 struct Geo {
     int32_t B, H, D;
     int32_t T, Y, X;
     int32_t nT, nY, nX, Nt;
     int64_t L, Lpad;
+    int32_t tx, lx;   // tile extent along X and its log2
+    int32_t E, le;    // slots per tile and its log2
+    int32_t sub;      // 64-slot units per tile
 };
 
-// Extent of tile `idx` along an axis of `dim` tokens (4, or the remainder).
-__host__ __device__ inline int axis_extent(int dim, int idx) {
-    int r = dim - 4 * idx;
-    return r < 4 ? r : 4;
+// Extent of tile `idx` along an axis of `dim` tokens cut into `size`s
+// (size, or the remainder).
+__host__ __device__ inline int axis_extent(int dim, int idx, int size = 4) {
+    int r = dim - size * idx;
+    return r < size ? r : size;
 }
 
 struct TileInfo {
@@ -56,7 +64,7 @@ __host__ __device__ inline TileInfo tile_info(const Geo& g, int j) {
     t.a = r / g.nY;
     t.st = axis_extent(g.T, t.a);
     t.sy = axis_extent(g.Y, t.b);
-    t.sx = axis_extent(g.X, t.c);
+    t.sx = axis_extent(g.X, t.c, g.tx);
     t.n = t.st * t.sy * t.sx;
     return t;
 }
@@ -66,10 +74,18 @@ __host__ __device__ inline int tile_occupancy(const Geo& g, int j) {
     return tile_info(g, j).n;
 }
 
+// Valid slots of 64-slot unit u (slots [64u, 64u + 64)): the tile's valid
+// tokens come first, so a tile's second unit holds what exceeds 64.
+__host__ __device__ inline int unit_occupancy(const Geo& g, int u) {
+    const int part = u & (g.sub - 1);
+    const int n = tile_occupancy(g, u >> (g.le - 6)) - 64 * part;
+    return n < 0 ? 0 : (n > 64 ? 64 : n);
+}
+
 // Raster token of slot s (s in [0, Lpad)), or -1 for a pad slot.
 __device__ inline int64_t slot_to_token(const Geo& g, int64_t s) {
-    int j = (int)(s >> 6);
-    int r = (int)(s & 63);
+    int j = (int)(s >> g.le);
+    int r = (int)(s & (g.E - 1));
     TileInfo t = tile_info(g, j);
     if (r >= t.n) return -1;
     int plane = t.sy * t.sx;
@@ -77,7 +93,7 @@ __device__ inline int64_t slot_to_token(const Geo& g, int64_t s) {
     int rem = r - dt * plane;
     int dy = rem / t.sx;
     int dx = rem - dy * t.sx;
-    int tt = 4 * t.a + dt, yy = 4 * t.b + dy, xx = 4 * t.c + dx;
+    int tt = 4 * t.a + dt, yy = 4 * t.b + dy, xx = g.tx * t.c + dx;
     return ((int64_t)tt * g.Y + yy) * g.X + xx;
 }
 
@@ -88,11 +104,11 @@ __device__ inline int64_t token_to_slot(const Geo& g, int64_t l) {
     int rem = (int)(l - (int64_t)tt * plane);
     int yy = rem / g.X;
     int xx = rem - yy * g.X;
-    int a = tt >> 2, b = yy >> 2, c = xx >> 2;
-    int sy = axis_extent(g.Y, b), sx = axis_extent(g.X, c);
+    int a = tt >> 2, b = yy >> 2, c = xx >> g.lx;
+    int sy = axis_extent(g.Y, b), sx = axis_extent(g.X, c, g.tx);
     int j = (a * g.nY + b) * g.nX + c;
-    int r = ((tt & 3) * sy + (yy & 3)) * sx + (xx & 3);
-    return (int64_t)j * kTileElems + r;
+    int r = ((tt & 3) * sy + (yy & 3)) * sx + (xx & (g.tx - 1));
+    return ((int64_t)j << g.le) + r;
 }
 
 }  // namespace bsta

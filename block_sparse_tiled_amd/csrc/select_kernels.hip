@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void pool_kernel(
     float* dst = blockIdx.y ? pk : pq;
     const int n = tile_occupancy(g, j);
     const int nvec = g.H * g.D / 8;
-    const u32x4* base = src + ((int64_t)b * g.Lpad + (int64_t)j * kTileElems) * nvec;
+    const u32x4* base = src + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec;
     for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         auto add = [&](const u32x4& w) {

@@ -86,7 +86,7 @@ constexpr int kTilePoolUnroll = 16;
 
 __global__ __launch_bounds__(64) void tile_pool_kernel(
         Geo g, const u32x4* __restrict__ src, u32x4* __restrict__ dst, float* __restrict__ pooled) {
-    __shared__ int64_t tok[kTileElems];
+    __shared__ int64_t tok[128];
     const int nvec = g.H * g.D / 8;
     const int nstripe = (nvec + 63) / 64;
     const int64_t bj = blockIdx.x / nstripe;
@@ -94,12 +94,12 @@ __global__ __launch_bounds__(64) void tile_pool_kernel(
     const int b = (int)(bj / g.Nt);
     const int j = (int)(bj - (int64_t)b * g.Nt);
     const int n = tile_occupancy(g, j);
-    tok[threadIdx.x] = slot_to_token(g, (int64_t)j * kTileElems + threadIdx.x);
+    for (int sl = threadIdx.x; sl < g.E; sl += 64) tok[sl] = slot_to_token(g, ((int64_t)j << g.le) + sl);
     __syncthreads();
     const int v = stripe * 64 + threadIdx.x;
     if (v >= nvec) return;
     const u32x4* sb = src + (int64_t)b * g.L * nvec + v;
-    u32x4* db = dst + ((int64_t)b * g.Lpad + (int64_t)j * kTileElems) * nvec + v;
+    u32x4* db = dst + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec + v;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     auto add = [&](const u32x4& w) {
 #pragma unroll
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(64) void tile_pool_kernel(
         __builtin_nontemporal_store(w, &db[(int64_t)r * nvec]);
         add(w);
     }
-    for (; r < kTileElems; ++r) __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, &db[(int64_t)r * nvec]);
+    for (; r < g.E; ++r) __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, &db[(int64_t)r * nvec]);
     const int col = v * 8;
     const int h = col / g.D;
     const int d0 = col - h * g.D;

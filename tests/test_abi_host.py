@@ -187,6 +187,35 @@ def test_cumulative_errors(lib):
     assert "attn_select_cumulative" in _err(lib)
 
 
+@pytest.mark.parametrize("grid", [(8, 8, 16), (21, 30, 52), (20, 48, 80), (5, 6, 7), (1, 1, 1)])
+def test_geometry_tile128_matches_oracle(lib, grid):
+    """4x4x8 (128-token) tiles: tile count, padded length and occupancy."""
+    T, Y, X = grid
+    t448 = geometry.TILE_SHAPES[128]
+    g = _g(T=T, Y=Y, X=X, tile=t448)
+    nt, lpad = ctypes.c_int32(), ctypes.c_int64()
+    assert lib.attn_geometry(ctypes.byref(g), ctypes.byref(nt), ctypes.byref(lpad), None) == 0
+    assert nt.value == geometry.num_tiles(T, Y, X, t448)
+    assert lpad.value == geometry.padded_len(T, Y, X, t448)
+    occ = (ctypes.c_int32 * nt.value)()
+    assert lib.attn_geometry(ctypes.byref(g), None, None, occ) == 0
+    assert np.array_equal(np.array(occ), geometry.occupancy(T, Y, X, t448))
+
+
+def test_tile128_unsupported_calls(lib):
+    """Query pruning and the backward are built for 64-token tiles only."""
+    g = _g(tile=(4, 4, 8))
+    assert lib.attn_prune_queries(ctypes.byref(g), FAKE, 0.5, FAKE, None, FAKE, None) == \
+        _lib.BSTA_ERR_UNSUPPORTED
+    scale = 1.0 / math.sqrt(g.D)
+    assert lib.attn_block_sparse_fwd_pruned(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, 16, scale, 0,
+                                            FAKE, 1, FAKE, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd(lib, g) == _lib.BSTA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(lib, g) == _lib.BSTA_ERR_UNSUPPORTED
+    for bad in ((4, 4, 16), (4, 8, 4), (8, 4, 4), (2, 4, 8)):
+        assert lib.attn_geometry(ctypes.byref(_g(tile=bad)), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+
+
 def test_prune_errors(lib):
     """Query pruning and the pruned forward check their arguments on the host."""
     g = _g()
