@@ -156,6 +156,8 @@ def main():
     # Preallocated outputs: the timed region allocates nothing.
     qt, kt, vt, ot = (torch.empty((w.B, lpad, w.H, w.D), dtype=torch.bfloat16, device=dev)
                       for _ in range(4))
+    pool_q, pool_k = (torch.empty((w.B, w.H, nt, w.D), dtype=torch.float32, device=dev)
+                      for _ in range(2))
     o = torch.empty_like(q)
     sel = bsta.attn_select_alloc(g, mode, w.topk, win, want_mask=False, device=dev)
     # Top-k: Q and K are pooled in the tiling pass (attn_tile_pool writes the
@@ -166,7 +168,7 @@ def main():
     sel_mode = (bsta.SELECT_TOPK | bsta.SELECT_PREPOOLED) if fused else mode
     # The attention call writes its output in raster order itself
     # (attn_block_sparse_fwd_raster), so the step has no untile pass.
-    names = ["tile_qkv", "select", "attn_fwd"]
+    names = ["tile_qk", "tile_v", "select", "attn_fwd"]
 
     def step(ev=None):
         if ev:
@@ -177,16 +179,18 @@ def main():
         else:
             bsta.attn_tile(g, q, out=qt)
             bsta.attn_tile(g, k, out=kt)
-        bsta.attn_tile(g, v, out=vt)
         if ev:
             ev[1].record()
+        bsta.attn_tile(g, v, out=vt)
+        if ev:
+            ev[2].record()
         bsta.attn_select_blocks(g, None if fused else qt, None if fused else kt, sel_mode, w.topk,
                                 win, out=sel)
         if ev:
-            ev[2].record()
+            ev[3].record()
         bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
         if ev:
-            ev[3].record()
+            ev[4].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -213,7 +217,32 @@ def main():
         for idx, n in enumerate(names):
             per[n].append(ev[idx].elapsed_time(ev[idx + 1]))
     ms = {n: float(np.median(per[n])) for n in names}
+    ms["tile_qkv"] = float(np.median([a + b for a, b in zip(per["tile_qk"], per["tile_v"])]))
     print(f"[bench] per-call median ms {ms}", file=sys.stderr, flush=True)
+
+    # The pooling step on its own (attn_pool on the tiled Q and K), for its
+    # HBM rate; not part of the step (the step pools while tiling).
+    per_pool = []
+    for _ in range(n_calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bsta.attn_pool(g, qt, out=pool_q)
+        bsta.attn_pool(g, kt, out=pool_k)
+        e1.record()
+        torch.cuda.synchronize()
+        per_pool.append(e0.elapsed_time(e1))
+    pool_ms = float(np.median(per_pool))
+
+    # Valid-token work of the step's selection: 4*D*n_i*n_j per selected
+    # pair (n = valid tokens per tile), against the tile-level 4*D*64*64.
+    occ_t = torch.tensor(bsta.attn_geometry(g, with_occupancy=True)[2], dtype=torch.float64,
+                         device=dev)
+    rp64 = sel.row_ptr.to(torch.int64)
+    row_len = rp64[1:] - rp64[:-1]
+    row_tile = torch.arange(w.B * w.H * nt, device=dev) % nt
+    n_i = torch.repeat_interleave(occ_t[row_tile], row_len)
+    n_j = occ_t[sel.col_idx[:int(rp64[-1].item())].to(torch.int64)]
+    valid_flop = float(4.0 * w.D * (n_i * n_j).sum().item())
 
     # The unfused selection (its own pooling pass over the tiled Q and K), for
     # the pooling kernel's standalone rate; not part of the step.
@@ -412,6 +441,8 @@ def main():
     elem = w.B * w.H * w.D * 2
     pooled_bytes = 2 * w.B * w.H * nt * w.D * 4 if fused else 0
     tile_bytes = 3 * elem * (w.L + lpad) + pooled_bytes
+    tile_qk_bytes = 2 * elem * (w.L + lpad) + pooled_bytes
+    tile_v_bytes = elem * (w.L + lpad)
     untile_bytes = elem * (w.L + lpad)
     pool_bytes = 2 * elem * w.L + 2 * w.B * w.H * nt * w.D * 4
     out = {
@@ -452,6 +483,8 @@ def main():
         "kernels": {
             "attn_fwd": {"ms": ms["attn_fwd"], "tflops": attn_tflops,
                          "dense_equiv_tflops": dense_flop / (ms["attn_fwd"] * 1e-3) / 1e12,
+                         "valid_token_flop": valid_flop,
+                         "valid_token_tflops": valid_flop / (ms["attn_fwd"] * 1e-3) / 1e12,
                          "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
                          "calls": n_calls, "stat": "median",
                          "note": "attn_block_sparse_fwd_raster (output in raster order)"},
@@ -462,6 +495,19 @@ def main():
                          "frac_hbm_peak": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                          "note": ("attn_tile_pool for Q and K (pooling fused), attn_tile for V"
                                   if fused else "attn_tile for Q, K and V")},
+            "tile_pool": {"ms": ms["tile_qk"], "bytes": tile_qk_bytes,
+                          "gbps": tile_qk_bytes / (ms["tile_qk"] * 1e-3) / 1e9,
+                          "frac_hbm_peak": tile_qk_bytes / (ms["tile_qk"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "note": ("attn_tile_pool for Q and K: read L rows, write Lpad rows and the "
+                                   "pooled vectors, per tensor" if fused else "attn_tile for Q and K")},
+            "tile_v": {"ms": ms["tile_v"], "gbps": tile_v_bytes / (ms["tile_v"] * 1e-3) / 1e9,
+                       "frac_hbm_peak": tile_v_bytes / (ms["tile_v"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                       "note": "attn_tile for V"},
+            "pool": {"ms": pool_ms, "bytes": pool_bytes,
+                     "gbps": pool_bytes / (pool_ms * 1e-3) / 1e9,
+                     "frac_hbm_peak": pool_bytes / (pool_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "note": "attn_pool on the tiled Q and K (the pooling step alone: read the valid "
+                             "rows, write the pooled vectors); not in the step"},
             "select": {"ms": ms["select"],
                        "note": "scores + top-k (prepooled)" if fused else "window CSR"},
             "select_unfused": ({"ms": unfused_ms, "pool_bytes": pool_bytes,

@@ -29,7 +29,7 @@ __all__ = [
     "attn_prune_queries",
     "block_sparse_attention_trainable",
     "attn_tile",
-    "attn_tile_pool", "attn_untile", "attn_select_alloc",
+    "attn_tile_pool", "attn_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
     "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
 ]
@@ -142,6 +142,19 @@ def attn_tile_pool(g: Geometry, x, pooled, out=None):
     _expect(pooled, (g.B, g.H, nt, g.D), torch.float32, "pooled")
     _lib.check(_lib.load().attn_tile_pool(ctypes.byref(g.c), _ptr(x), _ptr(out), _ptr(pooled),
                                           _stream()))
+    return out
+
+
+def attn_pool(g: Geometry, x_tiled, out=None):
+    """Per-tile mean of the valid rows of a tiled tensor: fp32 [B, H, Nt, D]
+    (the same vectors attn_tile_pool writes, bit for bit)."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    _expect(x_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "x_tiled")
+    if out is None:
+        out = torch.empty((g.B, g.H, nt, g.D), dtype=torch.float32, device=x_tiled.device)
+    _expect(out, (g.B, g.H, nt, g.D), torch.float32, "pooled")
+    _lib.check(_lib.load().attn_pool(ctypes.byref(g.c), _ptr(x_tiled), _ptr(out), _stream()))
     return out
 
 

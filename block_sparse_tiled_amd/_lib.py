@@ -27,7 +27,7 @@ SELECT_PREPOOLED = 0x100
 MAX_STA_HEADS = 256
 
 EXPORTS = (
-    "attn_geometry", "attn_tile", "attn_tile_pool", "attn_untile", "attn_select_capacity",
+    "attn_geometry", "attn_tile", "attn_tile_pool", "attn_pool", "attn_untile", "attn_select_capacity",
     "attn_workspace_bytes", "attn_select_blocks", "attn_select_cumulative",
     "attn_block_sparse_fwd",
     "attn_block_sparse_fwd_raster", "attn_bwd_workspace_bytes", "attn_block_sparse_bwd",
@@ -68,6 +68,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "attn_tile": (i32, [G, P, P, P]),
         "attn_tile_pool": (i32, [G, P, P, P, P]),
         "attn_untile": (i32, [G, P, P, P]),
+        "attn_pool": (i32, [G, P, P, P]),
         "attn_select_capacity": (i64, [G, i32, i32, P]),
         "attn_workspace_bytes": (i64, [G, i32]),
         "attn_select_blocks": (i32, [G, P, P, i32, i32, P, P, P, P, i64, P, i64, P]),

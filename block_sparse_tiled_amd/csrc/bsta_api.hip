@@ -21,6 +21,7 @@ hipError_t launch_permute(const Geo& g, const void* src, void* dst, bool to_tile
                           hipStream_t stream);
 hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, float* pooled,
                             hipStream_t stream);
+hipError_t launch_pool1(const Geo& g, const void* x, float* px, hipStream_t stream);
 hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
                        hipStream_t stream);
 hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,
@@ -312,6 +313,14 @@ int32_t attn_tile_pool(const bsta_geom* gin, const void* x, void* x_tiled, float
         return fail(BSTA_ERR_NULL, "attn_tile_pool: NULL tensor");
     return hip_status(bsta::launch_tile_pool(g, x, x_tiled, pooled, (hipStream_t)stream),
                       "attn_tile_pool");
+}
+
+int32_t attn_pool(const bsta_geom* gin, const void* x_tiled, float* pooled, void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (x_tiled == nullptr || pooled == nullptr) return fail(BSTA_ERR_NULL, "attn_pool: NULL tensor");
+    return hip_status(bsta::launch_pool1(g, x_tiled, pooled, (hipStream_t)stream), "attn_pool");
 }
 
 int32_t attn_untile(const bsta_geom* gin, const void* y_tiled, void* y, void* stream) {

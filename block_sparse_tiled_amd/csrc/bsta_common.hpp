@@ -82,6 +82,22 @@ __host__ __device__ inline int unit_occupancy(const Geo& g, int u) {
     return n < 0 ? 0 : (n > 64 ? 64 : n);
 }
 
+// Pooling order shared by the fused tile+pool kernel and the standalone
+// pooling kernel, so that both give the same fp32 vectors bit for bit: a
+// tile's slots are cut into runs of kPoolGroupRows; each run's valid rows
+// are summed in slot order from +0.0, and the run sums are added in run order
+// from +0.0 (runs with no valid row add +0.0), then divided by n_j.
+constexpr int kPoolGroupRows = 8;
+
+// acc[0..7] += the eight bf16 values of w (low half of each word first).
+__device__ inline void add_bf16x8(float (&acc)[8], const u32x4& w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        acc[2 * c] += __uint_as_float(w[c] << 16);
+        acc[2 * c + 1] += __uint_as_float(w[c] & 0xffff0000u);
+    }
+}
+
 // Raster token of slot s (s in [0, Lpad)), or -1 for a pad slot.
 __device__ inline int64_t slot_to_token(const Geo& g, int64_t s) {
     int j = (int)(s >> g.le);

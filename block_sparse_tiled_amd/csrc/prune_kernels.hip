@@ -13,9 +13,9 @@
 // One wave per (batch, head, tile): the tile's 64 rows of one head (D bf16
 // each) are staged in LDS with coalesced 16-byte loads, 64 / (D/8) rows per
 // instruction; the mean, the per-row scores, the ranks and the kept mean are
-// then lane-parallel over rows or over d.  Every sum runs in slot order in
-// fp32, so with ratio 1 the kept mean is the same sum and quotient as the
-// pooling kernels' (bit for bit).
+// then lane-parallel over rows or over d.  The kept mean is summed in fp32
+// in the pooling kernels' order, so with ratio 1 it equals their pooled
+// vector bit for bit.
 #include "bsta_common.hpp"
 
 namespace bsta {
@@ -88,12 +88,18 @@ __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restri
         if (keep_count != nullptr) keep_count[item] = c;
     }
 
-    // Mean of the kept rows (slot order), the tile's pooled query.
+    // Mean of the kept rows, the tile's pooled query, in the pooling kernels'
+    // order (runs of kPoolGroupRows slots, each summed from +0.0, the run
+    // sums added in order from +0.0).
     for (int d = lane; d < D; d += 64) {
-        float acc = 0.f;
-        for (int r = 0; r < n; ++r)
-            if ((kept >> r) & 1) acc += at(r, d);
-        pooled[item * D + d] = acc / (float)c;
+        float tot = 0.f;
+        for (int r0 = 0; r0 < 64; r0 += kPoolGroupRows) {
+            float acc = 0.f;
+            for (int r = r0; r < r0 + kPoolGroupRows && r < n; ++r)
+                if ((kept >> r) & 1) acc += at(r, d);
+            tot += acc;
+        }
+        pooled[item * D + d] = tot / (float)c;
     }
 }
 

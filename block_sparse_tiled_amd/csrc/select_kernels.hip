@@ -19,52 +19,68 @@
 namespace bsta {
 
 // ------------------------------------------------------------------ pooling
-// grid (B*Nt, 2): one workgroup per (batch, tile, tensor), one thread per
-// eight consecutive (head, d) columns (blockDim covers the H*D row, looping
-// past 1024 columns of 8).  Each thread sums the tile's valid rows in row
-// order with 16 row loads in flight; the tile's rows are contiguous.
-constexpr int kPoolUnroll = 16;
-
-__global__ __launch_bounds__(1024) void pool_kernel(
+// grid (B*Nt*stripes, tensors): one workgroup per (batch, tile, stripe of 64
+// vectors of 8 (head, d) columns, tensor), one wave per run of
+// kPoolGroupRows slots (bsta_common.hpp).  Each wave sums its run's valid
+// rows (all loads in flight) and wave 0 adds the run sums in order: the
+// fused tile+pool kernel's structure and order, without the copy.  Many
+// short waves: a wave walking all 64 rows of a tile left a long tail (70%
+// of HBM peak against 76%).
+template <int PARTS>
+__global__ __launch_bounds__(64 * PARTS) void pool_kernel(
         Geo g, const u32x4* __restrict__ q, const u32x4* __restrict__ k,
         float* __restrict__ pq, float* __restrict__ pk) {
-    const int b = blockIdx.x / g.Nt;
-    const int j = blockIdx.x - b * g.Nt;
+    __shared__ f32x4 part[PARTS][64][2];
     const u32x4* src = blockIdx.y ? k : q;
     float* dst = blockIdx.y ? pk : pq;
-    const int n = tile_occupancy(g, j);
     const int nvec = g.H * g.D / 8;
-    const u32x4* base = src + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec;
-    for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    const int nstripe = (nvec + 63) / 64;
+    const int64_t bj = blockIdx.x / nstripe;
+    const int stripe = (int)(blockIdx.x - bj * nstripe);
+    const int b = (int)(bj / g.Nt);
+    const int j = (int)(bj - (int64_t)b * g.Nt);
+    const int n = tile_occupancy(g, j);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int v = stripe * 64 + lane;
+    const int r0 = wave * kPoolGroupRows;
+    const int re = n < r0 + kPoolGroupRows ? n : r0 + kPoolGroupRows;
+    if (v < nvec) {
+        const u32x4* base = src + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec + v;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        auto add = [&](const u32x4& w) {
+        if (re - r0 == kPoolGroupRows) {
+            u32x4 w[kPoolGroupRows];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc[2 * c] += __uint_as_float(w[c] << 16);
-                acc[2 * c + 1] += __uint_as_float(w[c] & 0xffff0000u);
-            }
-        };
-        int r = 0;
-        for (; r + kPoolUnroll <= n; r += kPoolUnroll) {
-            u32x4 w[kPoolUnroll];
+            for (int u = 0; u < kPoolGroupRows; ++u)
+                w[u] = __builtin_nontemporal_load(&base[(int64_t)(r0 + u) * nvec]);
 #pragma unroll
-            for (int u = 0; u < kPoolUnroll; ++u)
-                w[u] = __builtin_nontemporal_load(&base[(int64_t)(r + u) * nvec + v]);
-#pragma unroll
-            for (int u = 0; u < kPoolUnroll; ++u) add(w[u]);
+            for (int u = 0; u < kPoolGroupRows; ++u) add_bf16x8(acc, w[u]);
+        } else {
+            for (int r = r0; r < re; ++r) add_bf16x8(acc, __builtin_nontemporal_load(&base[(int64_t)r * nvec]));
         }
-        for (; r < n; ++r) add(__builtin_nontemporal_load(&base[(int64_t)r * nvec + v]));
-        const int col = v * 8;
-        const int h = col / g.D;
-        const int d0 = col - h * g.D;
-        float* out = dst + (((int64_t)b * g.H + h) * g.Nt + j) * g.D + d0;
-        // Divide (not multiply by 1/n) for the correctly rounded quotient.
-        const float fn = (float)n;
-        f32x4 lo = {acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn};
-        f32x4 hi = {acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn};
-        *(f32x4*)out = lo;
-        *(f32x4*)(out + 4) = hi;
+        part[wave][lane][0] = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+        part[wave][lane][1] = (f32x4){acc[4], acc[5], acc[6], acc[7]};
     }
+    __syncthreads();
+    if (wave != 0 || v >= nvec) return;
+    float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < PARTS; ++p) {
+        const f32x4 lo = part[p][lane][0], hi = part[p][lane][1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            tot[c] += lo[c];
+            tot[4 + c] += hi[c];
+        }
+    }
+    const int col = v * 8;
+    const int h = col / g.D;
+    const int d0 = col - h * g.D;
+    float* out = dst + (((int64_t)b * g.H + h) * g.Nt + j) * g.D + d0;
+    // Divide (not multiply by 1/n) for the correctly rounded quotient.
+    const float fn = (float)n;
+    f32x4 lo = {tot[0] / fn, tot[1] / fn, tot[2] / fn, tot[3] / fn};
+    f32x4 hi = {tot[4] / fn, tot[5] / fn, tot[6] / fn, tot[7] / fn};
+    *(f32x4*)out = lo;
+    *(f32x4*)(out + 4) = hi;
 }
 
 // ------------------------------------------------------------------ scores
@@ -547,14 +563,31 @@ __global__ __launch_bounds__(256) void sta_kernel(
 }
 
 // ------------------------------------------------------------------ launchers
+namespace {
+hipError_t launch_pool_tensors(const Geo& g, const void* q, const void* k, float* pq, float* pk,
+                               unsigned tensors, hipStream_t stream) {
+    const int nvec = g.H * g.D / 8;
+    const unsigned groups = (unsigned)((int64_t)g.B * g.Nt * ((nvec + 63) / 64));
+    if (g.E == 64)
+        hipLaunchKernelGGL(pool_kernel<64 / kPoolGroupRows>, dim3(groups, tensors),
+                           dim3(64 * (64 / kPoolGroupRows)), 0, stream, g, (const u32x4*)q,
+                           (const u32x4*)k, pq, pk);
+    else
+        hipLaunchKernelGGL(pool_kernel<128 / kPoolGroupRows>, dim3(groups, tensors),
+                           dim3(64 * (128 / kPoolGroupRows)), 0, stream, g, (const u32x4*)q,
+                           (const u32x4*)k, pq, pk);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_pool(const Geo& g, const void* q, const void* k, float* pq, float* pk,
                        hipStream_t stream) {
-    const int nvec = g.H * g.D / 8;
-    int threads = (nvec + 63) / 64 * 64;
-    if (threads > 1024) threads = 1024;
-    hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(g.B * g.Nt), 2), dim3(threads), 0, stream, g,
-                       (const u32x4*)q, (const u32x4*)k, pq, pk);
-    return hipGetLastError();
+    return launch_pool_tensors(g, q, k, pq, pk, 2, stream);
+}
+
+// One tensor: the same kernel with a grid of one tensor.
+hipError_t launch_pool1(const Geo& g, const void* x, float* px, hipStream_t stream) {
+    return launch_pool_tensors(g, x, x, px, px, 1, stream);
 }
 
 hipError_t launch_scores(const Geo& g, const float* pq, const float* pk, float* s,

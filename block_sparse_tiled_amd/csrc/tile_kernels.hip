@@ -72,21 +72,25 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(
 }
 
 // Tiling with the per-tile mean pooling of the top-k coarse stage ("sla"
-// page, get_block_map / mean_pool) in the same pass.  One wave per (batch,
-// tile, stripe of 64 vectors): lane l copies vector 64*stripe + l (eight
-// consecutive (head, d) values) of every valid row of tile j to its slot (16
-// rows in flight), writes +0.0 to the pad rows, and sums the valid rows in
-// slot order in fp32, then divides by n_j: the same additions in the same
-// order as pool_kernel on the tiled tensor, so the pooled vectors are bit
-// for bit those attn_select_blocks would compute.  The stripe index varies
-// fastest over the grid, so the stripes of a tile's rows are read close
-// together in time (0.32 -> 0.30 ms per tensor at 40 heads x 128 against
-// stripe-major order; one wave measured as fast as 2 or 4).
-constexpr int kTilePoolUnroll = 16;
-
-__global__ __launch_bounds__(64) void tile_pool_kernel(
+// page, get_block_map / mean_pool) in the same pass.  One workgroup per
+// (batch, tile, stripe of 64 vectors) with one wave per run of
+// kPoolGroupRows rows: lane l copies vector 64*stripe + l (eight consecutive
+// (head, d) values) of each valid row of its run to the row's slot (all the
+// run's loads in flight), writes +0.0 to its pad rows, and sums its valid
+// rows in slot order in fp32.  Wave 0 then adds the runs' sums in run order,
+// starting from +0.0, and divides by n_j: the order pool_kernel uses on the
+// tiled tensor, so the pooled vectors are bit for bit those
+// attn_select_blocks would compute.  Short runs per wave matter: with 8
+// rows per wave the kernel moves 6.1 TB/s at 40 heads x 128, against 5.4
+// TB/s with one wave walking all 64 rows (same box), since the many short
+// waves leave no long tail.  The stripe index varies fastest over the grid,
+// so the stripes of a tile's rows are read close together in time.
+template <int PARTS>
+__global__ __launch_bounds__(64 * PARTS) void tile_pool_kernel(
         Geo g, const u32x4* __restrict__ src, u32x4* __restrict__ dst, float* __restrict__ pooled) {
-    __shared__ int64_t tok[128];
+    static_assert(PARTS * kPoolGroupRows <= 128, "a tile holds at most 128 slots");
+    __shared__ int64_t tok[PARTS * kPoolGroupRows];
+    __shared__ f32x4 part[PARTS][64][2];
     const int nvec = g.H * g.D / 8;
     const int nstripe = (nvec + 63) / 64;
     const int64_t bj = blockIdx.x / nstripe;
@@ -94,44 +98,55 @@ __global__ __launch_bounds__(64) void tile_pool_kernel(
     const int b = (int)(bj / g.Nt);
     const int j = (int)(bj - (int64_t)b * g.Nt);
     const int n = tile_occupancy(g, j);
-    for (int sl = threadIdx.x; sl < g.E; sl += 64) tok[sl] = slot_to_token(g, ((int64_t)j << g.le) + sl);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((int)threadIdx.x < g.E) tok[threadIdx.x] = slot_to_token(g, ((int64_t)j << g.le) + threadIdx.x);
     __syncthreads();
-    const int v = stripe * 64 + threadIdx.x;
-    if (v >= nvec) return;
-    const u32x4* sb = src + (int64_t)b * g.L * nvec + v;
-    u32x4* db = dst + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec + v;
+    const int v = stripe * 64 + lane;
+    const int r0 = wave * kPoolGroupRows;
+    const int re = n < r0 + kPoolGroupRows ? n : r0 + kPoolGroupRows;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const u32x4& w) {
+    if (v < nvec) {
+        const u32x4* sb = src + (int64_t)b * g.L * nvec + v;
+        u32x4* db = dst + ((int64_t)b * g.Lpad + ((int64_t)j << g.le)) * nvec + v;
+        if (re - r0 == kPoolGroupRows) {
+            u32x4 w[kPoolGroupRows];
+#pragma unroll
+            for (int u = 0; u < kPoolGroupRows; ++u) w[u] = __builtin_nontemporal_load(&sb[tok[r0 + u] * nvec]);
+#pragma unroll
+            for (int u = 0; u < kPoolGroupRows; ++u) {
+                __builtin_nontemporal_store(w[u], &db[(int64_t)(r0 + u) * nvec]);
+                add_bf16x8(acc, w[u]);
+            }
+        } else {
+            for (int r = r0; r < re; ++r) {
+                const u32x4 w = __builtin_nontemporal_load(&sb[tok[r] * nvec]);
+                __builtin_nontemporal_store(w, &db[(int64_t)r * nvec]);
+                add_bf16x8(acc, w);
+            }
+            for (int r = (re > r0 ? re : r0); r < r0 + kPoolGroupRows; ++r)
+                __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, &db[(int64_t)r * nvec]);
+        }
+        part[wave][lane][0] = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+        part[wave][lane][1] = (f32x4){acc[4], acc[5], acc[6], acc[7]};
+    }
+    __syncthreads();
+    if (wave != 0 || v >= nvec) return;
+    float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < PARTS; ++p) {
+        const f32x4 lo = part[p][lane][0], hi = part[p][lane][1];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            acc[2 * c] += __uint_as_float(w[c] << 16);
-            acc[2 * c + 1] += __uint_as_float(w[c] & 0xffff0000u);
-        }
-    };
-    int r = 0;
-    for (; r + kTilePoolUnroll <= n; r += kTilePoolUnroll) {
-        u32x4 w[kTilePoolUnroll];
-#pragma unroll
-        for (int u = 0; u < kTilePoolUnroll; ++u) w[u] = __builtin_nontemporal_load(&sb[tok[r + u] * nvec]);
-#pragma unroll
-        for (int u = 0; u < kTilePoolUnroll; ++u) {
-            __builtin_nontemporal_store(w[u], &db[(int64_t)(r + u) * nvec]);
-            add(w[u]);
+            tot[c] += lo[c];
+            tot[4 + c] += hi[c];
         }
     }
-    for (; r < n; ++r) {
-        const u32x4 w = __builtin_nontemporal_load(&sb[tok[r] * nvec]);
-        __builtin_nontemporal_store(w, &db[(int64_t)r * nvec]);
-        add(w);
-    }
-    for (; r < g.E; ++r) __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, &db[(int64_t)r * nvec]);
     const int col = v * 8;
     const int h = col / g.D;
     const int d0 = col - h * g.D;
     float* out = pooled + (((int64_t)b * g.H + h) * g.Nt + j) * g.D + d0;
     const float fn = (float)n;
-    f32x4 lo = {acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn};
-    f32x4 hi = {acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn};
+    f32x4 lo = {tot[0] / fn, tot[1] / fn, tot[2] / fn, tot[3] / fn};
+    f32x4 hi = {tot[4] / fn, tot[5] / fn, tot[6] / fn, tot[7] / fn};
     *(f32x4*)out = lo;
     *(f32x4*)(out + 4) = hi;
 }
@@ -139,10 +154,16 @@ __global__ __launch_bounds__(64) void tile_pool_kernel(
 hipError_t launch_tile_pool(const Geo& g, const void* x, void* x_tiled, float* pooled,
                             hipStream_t stream) {
     const int nvec = g.H * g.D / 8;
-    const int64_t waves = (int64_t)g.B * g.Nt * ((nvec + 63) / 64);
-    if (waves <= 0) return hipSuccess;
-    hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)waves), dim3(64), 0, stream, g,
-                       (const u32x4*)x, (u32x4*)x_tiled, pooled);
+    const int64_t groups = (int64_t)g.B * g.Nt * ((nvec + 63) / 64);
+    if (groups <= 0) return hipSuccess;
+    if (g.E == 64)
+        hipLaunchKernelGGL(tile_pool_kernel<64 / kPoolGroupRows>, dim3((unsigned)groups),
+                           dim3(64 * (64 / kPoolGroupRows)), 0, stream, g, (const u32x4*)x,
+                           (u32x4*)x_tiled, pooled);
+    else
+        hipLaunchKernelGGL(tile_pool_kernel<128 / kPoolGroupRows>, dim3((unsigned)groups),
+                           dim3(64 * (128 / kPoolGroupRows)), 0, stream, g, (const u32x4*)x,
+                           (u32x4*)x_tiled, pooled);
     return hipGetLastError();
 }
 

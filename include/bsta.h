@@ -120,6 +120,20 @@ int32_t attn_tile_pool(const bsta_geom* g, const void* x, void* x_tiled, float* 
                        void* stream);
 
 /*
+ * attn_pool: the per-tile mean of the valid rows of one tiled tensor
+ * ("sla" section of the backends page, mean_pool inside get_block_map; the
+ * pooling step attn_select_blocks runs on Q and K before scoring).
+ *   x_tiled [in]  bf16 [B, Lpad, H, D]
+ *   pooled  [out] fp32 [B, H, Nt, D]: the sum of tile j's n_j valid rows
+ *           divided by n_j, summed in fp32 in the order the fused
+ *           attn_tile_pool uses (runs of 8 slots summed from +0.0 in slot
+ *           order, run sums added in order), so the two give the same
+ *           vectors bit for bit.
+ * Errors: ERR_NULL, ERR_UNSUPPORTED (geometry), ERR_HIP.
+ */
+int32_t attn_pool(const bsta_geom* g, const void* x_tiled, float* pooled, void* stream);
+
+/*
  * attn_untile: tile -> raster order ("bsa_attn" page, postprocess_output and
  * get_reverse_tile_partition_indices).  Pad slots are dropped.
  *   y_tiled  [in]  bf16 [B, Lpad, H, D]

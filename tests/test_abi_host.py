@@ -216,6 +216,13 @@ def test_tile128_unsupported_calls(lib):
         assert lib.attn_geometry(ctypes.byref(_g(tile=bad)), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
 
 
+def test_pool_errors(lib):
+    g = _g()
+    assert lib.attn_pool(ctypes.byref(g), None, FAKE, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_pool(ctypes.byref(g), FAKE, None, None) == _lib.BSTA_ERR_NULL
+    assert lib.attn_pool(ctypes.byref(_g(D=32)), FAKE, FAKE, None) == _lib.BSTA_ERR_UNSUPPORTED
+
+
 def test_prune_errors(lib):
     """Query pruning and the pruned forward check their arguments on the host."""
     g = _g()

@@ -227,6 +227,15 @@ def test_tile_pool_fused(bsta, name):
     rpq, rpk = ref.pooled(g)
     for a, b in ((pq, rpq), (pk, rpk)):
         assert torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+    # attn_pool (the pooling step on its own) gives the same vectors, and
+    # they are the oracle's means
+    for x_t, want in ((qt, pq), (kt, pk)):
+        got = bsta.attn_pool(g, x_t)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), want.contiguous().view(torch.int32))
+    _, tf = _oracle_tiled(w, inp)
+    opq = select.pool(tf["q"], w.T, w.Y, w.X)
+    assert np.all(np.abs(pq.cpu().numpy() - opq) <= H.POOL_TOL * (1 + np.abs(opq)))
     assert torch.equal(sel.row_ptr, ref.row_ptr)
     nnz = int(ref.row_ptr[-1])
     assert torch.equal(sel.col_idx[:nnz], ref.col_idx[:nnz])
