@@ -8,6 +8,8 @@ computes, written from the FastVideo attention-backend pages:
                     mask -> CSR index map
   * attention.py -- masked softmax attention over the selected tiles, and a
                     brute-force dense attention with an explicit token mask
+  * packed.py    -- packed sequences of dense segments and video regions:
+                    layout, selection with per-region keep rates, attention
   * prune.py     -- query pruning: kept tokens per tile, the kept queries'
                     means for the selection, attention of the kept rows
 
