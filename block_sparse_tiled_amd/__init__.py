@@ -26,7 +26,7 @@ from ._lib import SELECT_CUMULATIVE, SELECT_PREPOOLED, SELECT_STA, SELECT_TOPK, 
 __all__ = [
     "Geometry", "BstaError", "SELECT_TOPK", "SELECT_STA", "SELECT_CUMULATIVE", "SELECT_PREPOOLED",
     "attn_select_cumulative", "attn_block_sparse_bwd", "attn_block_sparse_bwd_noalloc",
-    "attn_prune_queries",
+    "attn_prune_queries", "attn_packed_info", "attn_packed_capacity", "attn_select_packed",
     "block_sparse_attention_trainable",
     "attn_tile",
     "attn_tile_pool", "attn_pool", "attn_untile", "attn_select_alloc",
@@ -39,7 +39,9 @@ __all__ = [
 class Geometry:
     """Batch, heads, head dim and the (T, Y, X) latent grid.  ``tile_x`` is
     the tile's extent along X: 4 (4x4x4 = 64-token tiles, the default) or 8
-    (4x4x8 = 128-token tiles)."""
+    (4x4x8 = 128-token tiles).  A packed sequence (``Geometry.packed``) holds
+    ``segments`` instead of a grid: ints are dense segments (rows), 3-tuples
+    video regions (latent t, h, w, divided by ``patch``)."""
     B: int
     H: int
     D: int
@@ -47,13 +49,24 @@ class Geometry:
     Y: int
     X: int
     tile_x: int = 4
+    segments: Optional[tuple] = None
+    patch: tuple = (1, 1, 1)
+
+    @classmethod
+    def packed(cls, B, H, D, segments, patch=(1, 1, 1)) -> "Geometry":
+        segs = tuple(tuple(int(v) for v in s) if isinstance(s, (tuple, list)) else int(s)
+                     for s in segments)
+        return cls(B, H, D, 0, 0, 0, 4, segs, tuple(int(p) for p in patch))
 
     @property
     def c(self) -> _lib.Geom:
-        return _lib.geom(self.B, self.H, self.D, self.T, self.Y, self.X, self.tile_x)
+        return _lib.geom(self.B, self.H, self.D, self.T, self.Y, self.X, self.tile_x,
+                         self.segments, self.patch)
 
     @property
     def L(self) -> int:
+        if self.segments is not None:
+            return attn_packed_info(self)["L"]
         return self.T * self.Y * self.X
 
     @property
@@ -270,6 +283,67 @@ def attn_select_cumulative(g: Geometry, q_tiled, k_tiled, threshold: float, min_
     status = _lib.load().attn_select_cumulative(
         ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), SELECT_PREPOOLED if prepooled else 0,
         float(threshold), int(min_blocks), _ptr(out.block_mask), _ptr(out.row_ptr),
+        _ptr(out.col_idx), out.col_idx.numel(), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream())
+    _lib.check(status)
+    return out
+
+
+def attn_packed_info(g: Geometry) -> dict:
+    """Layout of a packed geometry, from the library: ``num_prefix`` (tiles
+    of the dense segments), ``spans`` (tile range of each video region) and
+    ``L`` (packed length)."""
+    lib = _lib.load()
+    c = g.c
+    npre, nreg, plen = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _lib.check(lib.attn_packed_info(ctypes.byref(c), ctypes.byref(npre), ctypes.byref(nreg), None,
+                                    ctypes.byref(plen)))
+    spans = (ctypes.c_int32 * (2 * nreg.value))()
+    _lib.check(lib.attn_packed_info(ctypes.byref(c), None, None, spans, None))
+    return {"num_prefix": npre.value, "L": plen.value,
+            "spans": [(spans[2 * r], spans[2 * r + 1]) for r in range(nreg.value)]}
+
+
+def attn_packed_capacity(g: Geometry, sparsity: float, ref_keep_rate: Optional[float] = None,
+                         exempt: bool = True) -> int:
+    rk = float("nan") if ref_keep_rate is None else float(ref_keep_rate)
+    return _lib.check(_lib.load().attn_packed_capacity(ctypes.byref(g.c), float(sparsity), rk,
+                                                       int(bool(exempt))))
+
+
+def attn_select_packed(g: Geometry, q_tiled, k_tiled, sparsity: float,
+                       ref_keep_rate: Optional[float] = None, exempt: bool = True,
+                       prepooled: bool = False, want_mask: bool = True,
+                       out: Optional[Selection] = None) -> Selection:
+    """Coarse stage of a packed sequence.  Exempt mode: prefix query tiles
+    keep every tile; video query tiles keep the prefix and, per video region,
+    its k best tiles (reference regions at ``ref_keep_rate``, the last region
+    at 1 - ``sparsity``).  Compete mode (one region): the k best tiles of the
+    whole sequence.  ``prepooled``: ``out`` (from attn_select_alloc with
+    SELECT_TOPK) already holds the pooled Q and K from attn_tile_pool."""
+    torch = _torch()
+    nt, lpad = attn_geometry(g)
+    if not prepooled:
+        _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
+        _expect(k_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "k_tiled")
+    elif out is None or out.workspace is None:
+        raise ValueError("prepooled needs `out` holding the pooled Q and K")
+    cap = attn_packed_capacity(g, sparsity, ref_keep_rate, exempt)
+    if out is None:
+        wsb = attn_workspace_bytes(g, SELECT_TOPK)
+        dev = q_tiled.device
+        out = Selection(
+            row_ptr=torch.empty(g.B * g.H * nt + 1, dtype=torch.int32, device=dev),
+            col_idx=torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+            block_mask=(torch.empty((g.B, g.H, nt, nt), dtype=torch.uint8, device=dev)
+                        if want_mask else None),
+            workspace=torch.empty(wsb // 4, dtype=torch.float32, device=dev))
+    _check_selection(g, out)
+    ws = out.workspace
+    rk = float("nan") if ref_keep_rate is None else float(ref_keep_rate)
+    status = _lib.load().attn_select_packed(
+        ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), SELECT_PREPOOLED if prepooled else 0,
+        float(sparsity), rk, int(bool(exempt)), _ptr(out.block_mask), _ptr(out.row_ptr),
         _ptr(out.col_idx), out.col_idx.numel(), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream())
     _lib.check(status)

@@ -32,6 +32,7 @@ EXPORTS = (
     "attn_block_sparse_fwd",
     "attn_block_sparse_fwd_raster", "attn_bwd_workspace_bytes", "attn_block_sparse_bwd",
     "attn_block_sparse_bwd_noalloc", "attn_prune_queries", "attn_block_sparse_fwd_pruned",
+    "attn_packed_info", "attn_packed_capacity", "attn_select_packed",
     "attn_status_string", "attn_last_error", "attn_set_deterministic",
 )
 
@@ -44,9 +45,20 @@ class BstaError(ValueError):
         self.status = status
 
 
+MAX_SEGMENTS = 16
+
+
+class Segments(ctypes.Structure):
+    """bsta_segments: a packed sequence of dense segments and video regions."""
+    _fields_ = [("count", ctypes.c_int32), ("patch", ctypes.c_int32 * 3),
+                ("kind", ctypes.c_int32 * MAX_SEGMENTS), ("rows", ctypes.c_int32 * MAX_SEGMENTS),
+                ("shape", (ctypes.c_int32 * 3) * MAX_SEGMENTS)]
+
+
 class Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "H", "D", "T", "Y", "X", "tile_t", "tile_y", "tile_x")]
+                ("B", "H", "D", "T", "Y", "X", "tile_t", "tile_y", "tile_x")] + [
+                    ("segments", ctypes.POINTER(Segments))]
 
 
 _lib = None
@@ -83,6 +95,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "attn_prune_queries": (i32, [G, P, ctypes.c_double, P, P, P, P]),
         "attn_block_sparse_fwd_pruned": (i32, [G, P, P, P, P, P, i64, ctypes.c_float, i32, P, i32, P,
                                                P, P]),
+        "attn_packed_info": (i32, [G, ctypes.POINTER(i32), ctypes.POINTER(i32), P,
+                                   ctypes.POINTER(i64)]),
+        "attn_packed_capacity": (i64, [G, ctypes.c_double, ctypes.c_double, i32]),
+        "attn_select_packed": (i32, [G, P, P, i32, ctypes.c_double, ctypes.c_double, i32, P, P, P,
+                                     i64, P, i64, P]),
         "attn_status_string": (ctypes.c_char_p, [i32]),
         "attn_last_error": (ctypes.c_char_p, []),
         "attn_set_deterministic": (i32, [i32]),
@@ -102,5 +119,27 @@ def check(status: int) -> int:
     return status
 
 
-def geom(B, H, D, T, Y, X, tile_x=4) -> Geom:
-    return Geom(int(B), int(H), int(D), int(T), int(Y), int(X), 4, 4, int(tile_x))
+def segments(packed, patch=(1, 1, 1)) -> Segments:
+    """bsta_segments of a packed list: ints are dense segments (rows),
+    3-tuples video regions (latent t, h, w)."""
+    if len(packed) > MAX_SEGMENTS:
+        raise ValueError(f"at most {MAX_SEGMENTS} segments, got {len(packed)}")
+    sg = Segments()
+    sg.count = len(packed)
+    for ax in range(3):
+        sg.patch[ax] = int(patch[ax])
+    for i, seg in enumerate(packed):
+        if isinstance(seg, (tuple, list)):
+            sg.kind[i] = 1
+            for ax in range(3):
+                sg.shape[i][ax] = int(seg[ax])
+        else:
+            sg.rows[i] = int(seg)
+    return sg
+
+
+def geom(B, H, D, T, Y, X, tile_x=4, packed=None, patch=(1, 1, 1)) -> Geom:
+    g = Geom(int(B), int(H), int(D), int(T), int(Y), int(X), 4, 4, int(tile_x))
+    if packed is not None:
+        g.segments = ctypes.pointer(segments(packed, patch))  # kept alive by g
+    return g

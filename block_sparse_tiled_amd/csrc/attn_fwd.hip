@@ -215,7 +215,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int l32 = lane & 31, half = lane >> 5;
     const int64_t rs = (int64_t)g.H * D;  // elements between consecutive tokens
     const int64_t rs2 = rs * 2;           // bytes
-    const bool all_full = (g.T & 3) == 0 && (g.Y & 3) == 0 && (g.X & (g.tx - 1)) == 0;
+    const bool all_full = g.full != 0;
     const int NU = g.Nt * SUB;  // 64-slot units per (batch, head)
 
     // Per-lane DMA source offsets (bytes, relative to the half-tile's first

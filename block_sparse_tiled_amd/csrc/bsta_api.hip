@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "bsta_common.hpp"
 
@@ -33,6 +34,9 @@ hipError_t launch_sta(const Geo& g, const int32_t* windows, uint8_t* mask, int32
 hipError_t launch_cumulative(const Geo& g, float threshold, int min_blocks, float* s,
                               uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
                               hipStream_t stream);
+hipError_t launch_packed_select(const Geo& g, const PackedSpans& sp, const float* s,
+                                uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
+                                hipStream_t stream);
 hipError_t bwd_scratch(void** out);
 hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
@@ -49,6 +53,7 @@ hipError_t launch_prune(const Geo& g, const void* q_tiled, double ratio, uint64_
 }  // namespace bsta
 
 using bsta::Geo;
+using bsta::Seg;
 
 namespace {
 
@@ -87,6 +92,87 @@ int32_t hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Sizes every launch must stay within (offsets are 64-bit in the kernels;
+// grid sizes 32-bit).
+int32_t check_sizes(const Geo* g) {
+    const double elems = (double)g->B * (double)g->Lpad * (double)g->H * (double)g->D;
+    if (elems > 9.0e15) return fail(BSTA_ERR_SHAPE, "tensor too large");
+    if ((double)g->B * g->H * g->Nt * 8.0 > 4.0e9)
+        return fail(BSTA_ERR_SHAPE, "B*H*Nt too large for one launch");
+    return BSTA_OK;
+}
+
+// The packed-sequence part of make_geo: token segments (empty dense ones
+// dropped, regions divided by the patch), dense tiles first, then regions.
+int32_t make_packed(const bsta_segments* sg, Geo* g) {
+    if (g->tx != 4)
+        return fail(BSTA_ERR_UNSUPPORTED, "packed sequences use 64-token (4x4x4) tiles");
+    if (sg->count < 1 || sg->count > BSTA_MAX_SEGMENTS)
+        return fail(BSTA_ERR_SHAPE, "segment count %d outside 1..%d", sg->count, BSTA_MAX_SEGMENTS);
+    for (int ax = 0; ax < 3; ++ax)
+        if (sg->patch[ax] < 1) return fail(BSTA_ERR_SHAPE, "patch size must be >= 1");
+    int n = 0, regions = 0;
+    int64_t tok = 0;
+    for (int i = 0; i < sg->count; ++i) {
+        Seg s = {};
+        s.tok0 = tok;
+        if (sg->kind[i] == 0) {
+            if (sg->rows[i] < 0) return fail(BSTA_ERR_SHAPE, "segment %d: %d rows", i, sg->rows[i]);
+            if (sg->rows[i] > (1 << 28)) return fail(BSTA_ERR_SHAPE, "segment %d too long", i);
+            if (sg->rows[i] == 0) continue;  // dropped
+            s.rows = sg->rows[i];
+            s.ntile = (s.rows + 63) / 64;
+            tok += s.rows;
+        } else if (sg->kind[i] == 1) {
+            int d[3];
+            for (int ax = 0; ax < 3; ++ax) {
+                const int v = sg->shape[i][ax];
+                if (v <= 0 || v % sg->patch[ax] != 0)
+                    return fail(BSTA_ERR_SHAPE,
+                                "segment %d: latent shape %dx%dx%d is not a positive multiple of "
+                                "patch %dx%dx%d", i, sg->shape[i][0], sg->shape[i][1],
+                                sg->shape[i][2], sg->patch[0], sg->patch[1], sg->patch[2]);
+                d[ax] = v / sg->patch[ax];
+                if (d[ax] > kMaxDim) return fail(BSTA_ERR_SHAPE, "segment %d: side above %d", i, kMaxDim);
+            }
+            s.T = d[0];
+            s.Y = d[1];
+            s.X = d[2];
+            s.nY = (d[1] + 3) / 4;
+            s.nX = (d[2] + 3) / 4;
+            s.ntile = ((d[0] + 3) / 4) * s.nY * s.nX;
+            tok += (int64_t)d[0] * d[1] * d[2];
+            ++regions;
+        } else {
+            return fail(BSTA_ERR_SHAPE, "segment %d: kind %d (0 dense, 1 video region)", i,
+                        sg->kind[i]);
+        }
+        g->seg[n++] = s;
+    }
+    if (regions == 0) return fail(BSTA_ERR_SHAPE, "a packed sequence needs a video region");
+    g->nseg = n;
+    int64_t tiles = 0;
+    bool full = true;
+    for (int pass = 0; pass < 2; ++pass)  // dense segments first, then regions
+        for (int i = 0; i < n; ++i) {
+            Seg& s = g->seg[i];
+            if ((s.rows > 0) != (pass == 0)) continue;
+            s.tile0 = (int32_t)tiles;
+            tiles += s.ntile;
+            if (tiles > (1 << 26)) return fail(BSTA_ERR_SHAPE, "tile count too large");
+            full = full && (s.rows > 0 ? s.rows % 64 == 0
+                                       : (s.T % 4 == 0 && s.Y % 4 == 0 && s.X % 4 == 0));
+            if (pass == 0) g->nprefix = (int32_t)tiles;
+        }
+    g->Nt = (int32_t)tiles;
+    g->L = tok;
+    g->Lpad = tiles * 64;
+    g->full = full ? 1 : 0;
+    g->T = g->Y = g->X = 0;
+    g->nT = g->nY = g->nX = 0;
+    return check_sizes(g);
+}
+
 // Validate a geometry and fill the derived fields.
 int32_t make_geo(const bsta_geom* in, Geo* g) {
     if (in == nullptr) return fail(BSTA_ERR_NULL, "geometry pointer is NULL");
@@ -96,22 +182,26 @@ int32_t make_geo(const bsta_geom* in, Geo* g) {
                     in->tile_t, in->tile_y, in->tile_x);
     if (in->D != 64 && in->D != 128)
         return fail(BSTA_ERR_UNSUPPORTED, "head dim D=%d unsupported: must be 64 or 128", in->D);
-    if (in->B < 1 || in->H < 1 || in->T < 1 || in->Y < 1 || in->X < 1)
-        return fail(BSTA_ERR_SHAPE, "B=%d H=%d T=%d Y=%d X=%d: all must be >= 1", in->B, in->H,
-                    in->T, in->Y, in->X);
-    if (in->T > kMaxDim || in->Y > kMaxDim || in->X > kMaxDim)
-        return fail(BSTA_ERR_SHAPE, "grid side above %d", kMaxDim);
+    if (in->B < 1 || in->H < 1)
+        return fail(BSTA_ERR_SHAPE, "B=%d H=%d: both must be >= 1", in->B, in->H);
+    *g = Geo{};
     g->B = in->B;
     g->H = in->H;
     g->D = in->D;
-    g->T = in->T;
-    g->Y = in->Y;
-    g->X = in->X;
     g->tx = in->tile_x;
     g->lx = in->tile_x == 8 ? 3 : 2;
     g->E = 16 * in->tile_x;
     g->le = in->tile_x == 8 ? 7 : 6;
     g->sub = g->E / 64;
+    if (in->segments != nullptr) return make_packed(in->segments, g);
+    if (in->T < 1 || in->Y < 1 || in->X < 1)
+        return fail(BSTA_ERR_SHAPE, "B=%d H=%d T=%d Y=%d X=%d: all must be >= 1", in->B, in->H,
+                    in->T, in->Y, in->X);
+    if (in->T > kMaxDim || in->Y > kMaxDim || in->X > kMaxDim)
+        return fail(BSTA_ERR_SHAPE, "grid side above %d", kMaxDim);
+    g->T = in->T;
+    g->Y = in->Y;
+    g->X = in->X;
     g->nT = (in->T + 3) / 4;
     g->nY = (in->Y + 3) / 4;
     g->nX = (in->X + g->tx - 1) / g->tx;
@@ -120,16 +210,13 @@ int32_t make_geo(const bsta_geom* in, Geo* g) {
     g->Nt = (int32_t)nt;
     g->L = (int64_t)in->T * in->Y * in->X;
     g->Lpad = nt * g->E;
-    // Offsets are 64-bit in the kernels; keep every element count well
-    // inside int64 and grid sizes inside 32 bits.
-    const double elems = (double)g->B * (double)g->Lpad * (double)g->H * (double)g->D;
-    if (elems > 9.0e15) return fail(BSTA_ERR_SHAPE, "tensor too large");
-    if ((double)g->B * g->H * g->Nt * 8.0 > 4.0e9)
-        return fail(BSTA_ERR_SHAPE, "B*H*Nt too large for one launch");
-    return BSTA_OK;
+    g->full = (in->T % 4 == 0 && in->Y % 4 == 0 && in->X % g->tx == 0) ? 1 : 0;
+    return check_sizes(g);
 }
 
 int32_t check_windows(const Geo& g, const int32_t* w, int64_t* per_batch) {
+    if (g.nseg > 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "window mode needs a single grid, not a packed sequence");
     if (w == nullptr) return fail(BSTA_ERR_NULL, "sta_windows_host is NULL in window mode");
     if (g.H > BSTA_MAX_STA_HEADS)
         return fail(BSTA_ERR_SHAPE, "H=%d above %d heads in window mode", g.H, BSTA_MAX_STA_HEADS);
@@ -178,6 +265,59 @@ int64_t capacity_of(const Geo& g, int32_t mode_in, int32_t topk, const int32_t* 
         nnz = (int64_t)g.B * g.H * g.Nt * g.Nt;
     } else {
         return fail(BSTA_ERR_UNSUPPORTED, "selection mode %d unknown", mode_in);
+    }
+    if (nnz > 0x7fffffffLL)
+        return fail(BSTA_ERR_SHAPE, "%lld CSR entries overflow int32 row_ptr", (long long)nnz);
+    return nnz;
+}
+
+// Tiles a span of n keeps at keep fraction `keep`: floor(keep * n) in
+// double precision, clamped to [1, n].
+int32_t span_keep(int32_t n, double keep) {
+    const double f = std::floor(keep * (double)n);
+    return f < 1.0 ? 1 : (f > (double)n ? n : (int32_t)f);
+}
+
+// The selection of a packed sequence: spans and their keep counts (exempt
+// mode) or the single k of compete mode, and the CSR entry count.
+int64_t packed_plan(const Geo& g, double sparsity, double ref_keep_rate, int32_t exempt,
+                    bsta::PackedSpans* sp, int32_t* compete_k) {
+    if (g.nseg == 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "a packed selection needs a packed geometry");
+    if (!std::isfinite(sparsity) || sparsity > 1.0)
+        return fail(BSTA_ERR_SHAPE, "sparsity %g must be finite and <= 1", sparsity);
+    *sp = bsta::PackedSpans{};
+    sp->nprefix = g.nprefix;
+    for (int t = 0; t < g.nseg; ++t)
+        if (g.seg[t].rows == 0) {
+            sp->a[sp->n] = g.seg[t].tile0;
+            sp->b[sp->n] = g.seg[t].tile0 + g.seg[t].ntile;
+            ++sp->n;
+        }
+    int64_t nnz;
+    if (!exempt) {
+        if (sp->n != 1)
+            return fail(BSTA_ERR_UNSUPPORTED,
+                        "compete mode supports one video region, the sequence has %d", sp->n);
+        *compete_k = sparsity <= 0.0 ? g.Nt : span_keep(g.Nt, 1.0 - sparsity);
+        nnz = (int64_t)g.B * g.H * g.Nt * *compete_k;
+    } else {
+        const bool dense = sparsity <= 0.0;
+        if (sp->n > 1 && !(ref_keep_rate >= 0.0 && ref_keep_rate <= 1.0))
+            return fail(BSTA_ERR_SHAPE, "ref_keep_rate %g outside [0, 1] with %d regions",
+                        ref_keep_rate, sp->n);
+        if (g.Nt > kMaxCumulativeTiles)
+            return fail(BSTA_ERR_SHAPE, "packed selection supports at most %d tiles, got %d",
+                        kMaxCumulativeTiles, g.Nt);
+        sp->vlen = sp->nprefix;
+        for (int r = 0; r < sp->n; ++r) {
+            const int32_t n = sp->b[r] - sp->a[r];
+            const double keep = dense ? 1.0 : (r + 1 < sp->n ? ref_keep_rate : 1.0 - sparsity);
+            sp->k[r] = span_keep(n, keep);
+            sp->vlen += sp->k[r];
+        }
+        nnz = (int64_t)g.B * g.H *
+              ((int64_t)sp->nprefix * g.Nt + (int64_t)(g.Nt - sp->nprefix) * sp->vlen);
     }
     if (nnz > 0x7fffffffLL)
         return fail(BSTA_ERR_SHAPE, "%lld CSR entries overflow int32 row_ptr", (long long)nnz);
@@ -418,6 +558,81 @@ int32_t attn_select_cumulative(const bsta_geom* gin, const void* q_tiled, const 
     return hip_status(e, "attn_select_cumulative");
 }
 
+int32_t attn_packed_info(const bsta_geom* gin, int32_t* num_prefix, int32_t* num_regions,
+                         int32_t* spans, int64_t* packed_len) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (g.nseg == 0) return fail(BSTA_ERR_UNSUPPORTED, "attn_packed_info: not a packed geometry");
+    int r = 0;
+    for (int t = 0; t < g.nseg; ++t)
+        if (g.seg[t].rows == 0) {
+            if (spans) {
+                spans[2 * r] = g.seg[t].tile0;
+                spans[2 * r + 1] = g.seg[t].tile0 + g.seg[t].ntile;
+            }
+            ++r;
+        }
+    if (num_prefix) *num_prefix = g.nprefix;
+    if (num_regions) *num_regions = r;
+    if (packed_len) *packed_len = g.L;
+    return ok();
+}
+
+int64_t attn_packed_capacity(const bsta_geom* gin, double sparsity, double ref_keep_rate,
+                             int32_t exempt) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    bsta::PackedSpans sp;
+    int32_t k = 0;
+    const int64_t n = packed_plan(g, sparsity, ref_keep_rate, exempt, &sp, &k);
+    if (n >= 0) ok();
+    return n;
+}
+
+int32_t attn_select_packed(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
+                           int32_t flags, double sparsity, double ref_keep_rate, int32_t exempt,
+                           uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+    Geo g;
+    int32_t st = make_geo(gin, &g);
+    if (st != BSTA_OK) return st;
+    if (flags != 0 && flags != BSTA_SELECT_PREPOOLED)
+        return fail(BSTA_ERR_UNSUPPORTED, "attn_select_packed: flags %d unknown", flags);
+    const bool prepooled = flags == BSTA_SELECT_PREPOOLED;
+    if (row_ptr == nullptr || col_idx == nullptr)
+        return fail(BSTA_ERR_NULL, "attn_select_packed: NULL row_ptr or col_idx");
+    if (!prepooled && (q_tiled == nullptr || k_tiled == nullptr))
+        return fail(BSTA_ERR_NULL, "attn_select_packed: NULL q_tiled or k_tiled");
+    bsta::PackedSpans sp;
+    int32_t k = 0;
+    const int64_t need = packed_plan(g, sparsity, ref_keep_rate, exempt, &sp, &k);
+    if (need < 0) return (int32_t)need;
+    if (col_capacity < need)
+        return fail(BSTA_ERR_CAPACITY, "col_capacity %lld < %lld entries needed",
+                    (long long)col_capacity, (long long)need);
+    if (g.Nt > kMaxTopkTiles)
+        return fail(BSTA_ERR_SHAPE, "packed selection supports at most %d tiles, got %d",
+                    kMaxTopkTiles, g.Nt);
+    const int64_t ws = workspace_of(g, BSTA_SELECT_TOPK);
+    if (workspace == nullptr) return fail(BSTA_ERR_NULL, "attn_select_packed: NULL workspace");
+    if (workspace_bytes < ws)
+        return fail(BSTA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                    (long long)workspace_bytes, (long long)ws);
+    hipStream_t s = (hipStream_t)stream;
+    float* pq = (float*)workspace;
+    float* pk = pq + (int64_t)g.B * g.H * g.Nt * g.D;
+    float* sc = pk + (int64_t)g.B * g.H * g.Nt * g.D;
+    hipError_t e = prepooled ? hipSuccess : bsta::launch_pool(g, q_tiled, k_tiled, pq, pk, s);
+    if (e == hipSuccess) e = bsta::launch_scores(g, pq, pk, sc, s);
+    if (e == hipSuccess)
+        e = exempt ? bsta::launch_packed_select(g, sp, sc, block_mask, row_ptr, col_idx, s)
+                   : bsta::launch_topk(g, k, sc, block_mask, row_ptr, col_idx, s);
+    return hip_status(e, "attn_select_packed");
+}
+
 int32_t attn_block_sparse_fwd(const bsta_geom* gin, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
                               int64_t col_len, float softmax_scale, int32_t causal,
@@ -445,8 +660,9 @@ int32_t attn_prune_queries(const bsta_geom* gin, const void* q_tiled, double kee
     if (st != BSTA_OK) return st;
     if (q_tiled == nullptr || keep_mask == nullptr || pooled_q == nullptr)
         return fail(BSTA_ERR_NULL, "attn_prune_queries: NULL q_tiled, keep_mask or pooled_q");
-    if (g.tx != 4)
-        return fail(BSTA_ERR_UNSUPPORTED, "attn_prune_queries: 64-token tiles only (4x4x4)");
+    if (g.tx != 4 || g.nseg > 0)
+        return fail(BSTA_ERR_UNSUPPORTED,
+                    "attn_prune_queries: 64-token tiles (4x4x4) of a single grid only");
     if (!(keep_ratio > 0.0 && keep_ratio <= 1.0))
         return fail(BSTA_ERR_SHAPE, "keep_ratio %g outside (0, 1]", keep_ratio);
     return hip_status(bsta::launch_prune(g, q_tiled, keep_ratio, keep_mask, keep_count, pooled_q,
@@ -462,8 +678,9 @@ int32_t attn_block_sparse_fwd_pruned(const bsta_geom* gin, const void* q_tiled,
                                      float* lse, void* stream) {
     if (keep_mask == nullptr)
         return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd_pruned: NULL keep_mask");
-    if (gin != nullptr && gin->tile_x != 4)
-        return fail(BSTA_ERR_UNSUPPORTED, "attn_block_sparse_fwd_pruned: 64-token tiles only");
+    if (gin != nullptr && (gin->tile_x != 4 || gin->segments != nullptr))
+        return fail(BSTA_ERR_UNSUPPORTED,
+                    "attn_block_sparse_fwd_pruned: 64-token tiles of a single grid only");
     return block_sparse_fwd("attn_block_sparse_fwd_pruned", gin, q_tiled, k_tiled, v_tiled,
                             row_ptr, col_idx, col_len, softmax_scale, causal, keep_mask, o, lse,
                             raster != 0, stream);

@@ -253,20 +253,14 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 }
 
-// One wave per CSR row, for rows of at most 64*C scores: lane l holds
-// scores j = 64c + l, c < C, in registers (coalesced loads, no LDS, no
-// barriers).  The k-th largest key is found bit by bit from the top: a bit
-// is kept when at least k keys are at or above the candidate (one ballot and
-// popcount per register).  Then keys above it are kept, and of the keys
-// equal to it the first k - (count above) in j order; with j = 64c + l,
-// walking c upward and ranking lanes by mbcnt visits j in increasing order,
-// so the same ballots give the tie ranks and the ascending CSR positions.
-// Writes the k kept ids to out[0, k) and the row's mask (if any).
 // The k-th largest key of a row held as key[c] = lane's score j = 64c + l
 // (0 for padding): returns it, and in *take_eq how many keys equal to it
 // are kept (the lowest-index ones) so that exactly k are kept.
+// Only columns j in [lo, hi) take part; the caller holds key 0 everywhere
+// else (the whole row: lo = 0, hi = Nt).
 template <int C>
-__device__ inline uint32_t kth_key(const uint32_t (&key)[C], int Nt, int k, int lane, int* take_eq) {
+__device__ inline uint32_t kth_key(const uint32_t (&key)[C], int lo, int hi, int k, int lane,
+                                   int* take_eq) {
     // Padding slots hold key 0 and every candidate below is >= 1, so they
     // never count; a real key 0 is handled by the explicit validity test in
     // the final pass.
@@ -281,7 +275,8 @@ __device__ inline uint32_t kth_key(const uint32_t (&key)[C], int Nt, int k, int 
     int above = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const bool valid = c * 64 + lane < Nt;
+        const int j = c * 64 + lane;
+        const bool valid = j >= lo && j < hi;
         above += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid && key[c] > thr));
     }
     *take_eq = k - above;
@@ -294,14 +289,14 @@ __device__ inline uint32_t kth_key(const uint32_t (&key)[C], int Nt, int k, int 
 // visits j in increasing order, so the same ballots give the tie ranks and
 // the output positions.  Returns the number written.
 template <int C>
-__device__ inline int write_kept(const uint32_t (&key)[C], int Nt, uint32_t thr, int take_eq,
-                                 int limit, uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
-                                 int lane) {
+__device__ inline int write_kept(const uint32_t (&key)[C], int lo, int hi, uint32_t thr,
+                                 int take_eq, int limit, uint8_t* __restrict__ mrow,
+                                 int32_t* __restrict__ out, int lane) {
     int base = 0, eq_base = 0;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int j = c * 64 + lane;
-        const bool valid = j < Nt;
+        const bool valid = j >= lo && j < hi;
         const bool eq = valid && key[c] == thr;
         const uint64_t eqm = __builtin_amdgcn_ballot_w64(eq);
         const int eq_rank = eq_base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
@@ -335,8 +330,8 @@ __device__ inline void select_row_wave(int Nt, int k, const float* __restrict__ 
         key[c] = j < Nt ? score_key(srow[j]) : 0u;
     }
     int take_eq;
-    const uint32_t thr = kth_key<C>(key, Nt, k, lane, &take_eq);
-    write_kept<C>(key, Nt, thr, take_eq, k, mrow, out, lane);
+    const uint32_t thr = kth_key<C>(key, 0, Nt, k, lane, &take_eq);
+    write_kept<C>(key, 0, Nt, thr, take_eq, k, mrow, out, lane);
 }
 
 // Top-k: every row keeps k tiles; CSR row r starts at r*k.
@@ -353,6 +348,61 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(
     if (lane == 0) {
         row_ptr[row] = (int32_t)(row * k);
         if (row == rows - 1) row_ptr[rows] = (int32_t)(rows * k);
+    }
+}
+
+// Packed sequence, exempt mode (one wave per CSR row): a prefix query tile
+// keeps every tile; a video query tile keeps the prefix and, in each span
+// [a, b), the k best tiles of that span, found by the top-k routines on the
+// row's keys with every key outside the span held at 0.  Row lengths are
+// fixed (Nt for prefix rows, vlen for video rows), so every row knows its
+// CSR start without a scan.
+template <int C>
+__global__ __launch_bounds__(256) void packed_select_kernel(
+        int Nt, int64_t rows, PackedSpans sp, const float* __restrict__ s,
+        uint8_t* __restrict__ mask, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const int64_t bh = row / Nt;
+    const int i = (int)(row - bh * Nt);
+    const int P = sp.nprefix;
+    const int64_t head_nnz = (int64_t)P * Nt + (int64_t)(Nt - P) * sp.vlen;
+    const int64_t start = bh * head_nnz + (i < P ? (int64_t)i * Nt
+                                                 : (int64_t)P * Nt + (int64_t)(i - P) * sp.vlen);
+    int32_t* out = col_idx + start;
+    uint8_t* mrow = mask ? mask + row * Nt : nullptr;
+    const int whole = i < P ? Nt : P;  // leading tiles kept outright
+    for (int j = lane; j < whole; j += 64) {
+        out[j] = j;
+        if (mrow) mrow[j] = 1;
+    }
+    if (i >= P) {
+        const float* srow = s + row * Nt;
+        uint32_t key[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int j = c * 64 + lane;
+            key[c] = j < Nt ? score_key(srow[j]) : 0u;
+        }
+        int pos = P;
+        for (int r = 0; r < sp.n; ++r) {
+            const int a = sp.a[r], b = sp.b[r], k = sp.k[r];
+            uint32_t kr[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int j = c * 64 + lane;
+                kr[c] = (j >= a && j < b) ? key[c] : 0u;
+            }
+            int take;
+            const uint32_t thr = kth_key<C>(kr, a, b, k, lane, &take);
+            write_kept<C>(kr, a, b, thr, take, k, mrow, out + pos, lane);
+            pos += k;
+        }
+    }
+    if (lane == 0) {
+        row_ptr[row] = (int32_t)start;
+        if (row == rows - 1) row_ptr[rows] = (int32_t)(start + (i < P ? Nt : sp.vlen));
     }
 }
 
@@ -450,9 +500,9 @@ __global__ __launch_bounds__(256) void cumulative_count_kernel(
     int cnt = above + take;
     if (cnt < kmin) {  // wave-uniform
         cnt = kmin < Nt ? kmin : Nt;
-        thr = kth_key<C>(key, Nt, cnt, lane, &take);
+        thr = kth_key<C>(key, 0, Nt, cnt, lane, &take);
     }
-    write_kept<C>(key, Nt, thr, take, Nt, mask ? mask + row * Nt : nullptr, (int32_t*)(s + row * Nt),
+    write_kept<C>(key, 0, Nt, thr, take, Nt, mask ? mask + row * Nt : nullptr, (int32_t*)(s + row * Nt),
                   lane);
     if (lane == 0) counts[row] = cnt;
 }
@@ -622,6 +672,24 @@ hipError_t launch_topk(const Geo& g, int k, const float* s, uint8_t* mask, int32
                            rows, s, mask, row_ptr, col_idx);
     }
 #undef BSTA_TOPK_WAVE
+    return hipGetLastError();
+}
+
+hipError_t launch_packed_select(const Geo& g, const PackedSpans& sp, const float* s,
+                                uint8_t* mask, int32_t* row_ptr, int32_t* col_idx,
+                                hipStream_t stream) {
+    const int64_t rows = (int64_t)g.B * g.H * g.Nt;
+    const int chunks = (g.Nt + 63) / 64;
+    const unsigned wave_blocks = (unsigned)((rows + 3) / 4);
+#define BSTA_PACKED(CC)                                                                        \
+    hipLaunchKernelGGL(packed_select_kernel<CC>, dim3(wave_blocks), dim3(256), 0, stream, g.Nt, \
+                       rows, sp, s, mask, row_ptr, col_idx)
+    if (chunks <= 8) BSTA_PACKED(8);
+    else if (chunks <= 16) BSTA_PACKED(16);
+    else if (chunks <= 24) BSTA_PACKED(24);
+    else if (chunks <= 32) BSTA_PACKED(32);
+    else return hipErrorInvalidValue;  // the caller bounds Nt by 2048
+#undef BSTA_PACKED
     return hipGetLastError();
 }
 

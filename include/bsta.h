@@ -49,11 +49,40 @@
 extern "C" {
 #endif
 
-/* Problem geometry.  D must be 64 or 128; tile_t = tile_y = tile_x = 4. */
+/* Largest number of segments of a packed sequence. */
+#define BSTA_MAX_SEGMENTS 16
+
+/*
+ * A packed sequence ("video_sparse_attn_h3" page, build()): dense segments
+ * and video regions packed in one sequence, in this order.  kind[s] = 0: a
+ * dense segment of rows[s] rows (0 rows: the segment is dropped); kind[s] =
+ * 1: a video region whose latent shape shape[s] = (t, h, w) must be a
+ * positive multiple of patch and becomes a token grid of shape / patch.  At
+ * least one region is required.  Tiles (64 tokens): each dense segment is
+ * cut into tiles of 64 consecutive rows, the last one partial, and these
+ * tiles come first in tile order (the prefix, in packed order); then each
+ * region is cut into 4x4x4 tiles as a single grid, region by region in
+ * packed order, each region's tiles forming its span.  (The page gives the
+ * arguments and checks of build(), not the layout; this is the reading.)
+ */
+typedef struct bsta_segments {
+    int32_t count;                        /* 1 .. BSTA_MAX_SEGMENTS       */
+    int32_t patch[3];                     /* patch size (t, h, w), >= 1   */
+    int32_t kind[BSTA_MAX_SEGMENTS];      /* 0 dense, 1 video region      */
+    int32_t rows[BSTA_MAX_SEGMENTS];      /* dense rows (kind 0)          */
+    int32_t shape[BSTA_MAX_SEGMENTS][3];  /* latent t, h, w (kind 1)      */
+} bsta_segments;
+
+/* Problem geometry.  D must be 64 or 128; tile_t = tile_y = 4 and tile_x =
+ * 4 (64-token tiles) or 8 (128-token tiles).  segments = NULL: one latent
+ * grid T x Y x X.  segments != NULL (host memory, read during the call):
+ * a packed sequence, 64-token tiles only; T, Y and X are then ignored and
+ * L is the packed length (attn_packed_info). */
 typedef struct bsta_geom {
     int32_t B, H, D;            /* batch, heads, head dim                  */
     int32_t T, Y, X;            /* latent token grid                       */
     int32_t tile_t, tile_y, tile_x;
+    const bsta_segments* segments;
 } bsta_geom;
 
 enum {
@@ -235,6 +264,67 @@ int32_t attn_select_cumulative(const bsta_geom* g, const void* q_tiled, const vo
                                void* stream);
 
 /*
+ * attn_packed_info (host only, no HIP call): the layout of a packed
+ * sequence (g->segments != NULL; see bsta_segments).
+ *   num_prefix  [out, host, may be NULL]  tiles of the dense segments
+ *   num_regions [out, host, may be NULL]  video regions R
+ *   spans       [out, host int32 [2*R], may be NULL]  tile range
+ *               [spans[2r], spans[2r+1]) of region r, in packed order
+ *   packed_len  [out, host, may be NULL]  L, tokens of the packed sequence
+ * BSTA_ERR_UNSUPPORTED for a single-grid geometry.
+ */
+int32_t attn_packed_info(const bsta_geom* g, int32_t* num_prefix, int32_t* num_regions,
+                         int32_t* spans, int64_t* packed_len);
+
+/*
+ * attn_packed_capacity (host only): CSR entries attn_select_packed writes
+ * for these arguments, or a negative status.
+ */
+int64_t attn_packed_capacity(const bsta_geom* g, double sparsity, double ref_keep_rate,
+                             int32_t exempt);
+
+/*
+ * attn_select_packed: the coarse stage of a packed sequence
+ * ("video_sparse_attn_h3" page, build() and its sparsity, ref_keep_rate and
+ * compete/exempt arguments; the page shows the call, not the rule; the
+ * reading implemented here).  Pooling and pooled scores S as in top-k mode,
+ * over the packed tiles (a tile's mean is over its valid rows).  With
+ * P prefix tiles and the video spans [a_r, b_r) of n_r tiles:
+ *   exempt != 0 (the default on the page): a prefix query tile keeps every
+ *     tile; a video query tile keeps every prefix tile and, in each span r,
+ *     the k_r tiles of highest S (ties to the lower index), with
+ *     k_r = min(n_r, max(1, floor(keep_r * n_r))), keep_r = ref_keep_rate
+ *     for a reference region (every region but the last) and
+ *     1 - sparsity for the last (generated) region; sparsity <= 0 keeps
+ *     every tile.  Prefix rows hold Nt entries, video rows P + sum_r k_r.
+ *   exempt == 0 (compete): one region only; every query tile keeps the
+ *     min(Nt, max(1, floor((1 - sparsity) * Nt))) tiles of highest S over
+ *     the whole sequence (every tile if sparsity <= 0).
+ *   q_tiled, k_tiled  [in]  bf16 [B, Lpad, H, D] from attn_tile; unused (may
+ *                           be NULL) with BSTA_SELECT_PREPOOLED
+ *   flags             0 or BSTA_SELECT_PREPOOLED
+ *   sparsity          finite, <= 1
+ *   ref_keep_rate     in [0, 1] when there is more than one region (the
+ *                     page requires it then); otherwise unused
+ *   block_mask        [out, uint8 [B, H, Nt, Nt], may be NULL] 1 = kept
+ *   row_ptr           [out, int32 [B*H*Nt + 1]]
+ *   col_idx           [out, int32 [col_capacity]], ascending per row
+ *   col_capacity      >= attn_packed_capacity(g, sparsity, ref_keep_rate,
+ *                     exempt)
+ *   workspace         [scratch, >= attn_workspace_bytes(g,
+ *                     BSTA_SELECT_TOPK)]; afterwards it holds the pooled
+ *                     Q and K and the scores
+ * Needs a packed geometry with Nt <= 2048 in exempt mode (a score row lives
+ * in one wave's registers); BSTA_ERR_SHAPE otherwise.  keep_r * n_r is
+ * evaluated in double precision.
+ */
+int32_t attn_select_packed(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
+                           int32_t flags, double sparsity, double ref_keep_rate, int32_t exempt,
+                           uint8_t* block_mask, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
+/*
  * attn_block_sparse_fwd: fused block-sparse flash attention forward
  * ("bsa_attn" page, forward and _compute_sparse_attention; __init__ fixes
  * the scale to 1/sqrt(d) and rejects causal attention).
@@ -305,8 +395,8 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
  *              BSTA_SELECT_PREPOOLED) or attn_select_cumulative (prepooled)
  *              then select key tiles from the kept queries.
  * Errors: ERR_NULL (q_tiled, keep_mask or pooled_q NULL), ERR_SHAPE (ratio
- * outside (0, 1]), ERR_UNSUPPORTED (geometry), ERR_HIP.  One wave per
- * (batch, head, tile); computed in fp32.
+ * outside (0, 1]), ERR_UNSUPPORTED (128-token tiles or a packed
+ * sequence), ERR_HIP.  One wave per (batch, head, tile); computed in fp32.
  */
 int32_t attn_prune_queries(const bsta_geom* g, const void* q_tiled, double keep_ratio,
                            uint64_t* keep_mask, int32_t* keep_count, float* pooled_q,
@@ -321,6 +411,7 @@ int32_t attn_prune_queries(const bsta_geom* g, const void* q_tiled, double keep_
  * hold zero).  Arguments otherwise as attn_block_sparse_fwd; keep_mask is
  * uint64 [B, H, Nt] on the device (ERR_NULL if NULL).  Pruned rows are
  * masked, not skipped: the call costs what the unpruned one does.
+ * ERR_UNSUPPORTED for 128-token tiles and packed sequences.
  */
 int32_t attn_block_sparse_fwd_pruned(const bsta_geom* g, const void* q_tiled,
                                      const void* k_tiled, const void* v_tiled,

@@ -198,6 +198,72 @@ void thread_checks() {
     CHECK(attn_set_deterministic(0) == 1);
 }
 
+// Packed sequences: layout, capacity, argument checks, and that an accepted
+// selection reaches its launches (pool, scores, select).
+void packed_checks() {
+    bsta_segments sg = {};
+    sg.count = 4;
+    sg.patch[0] = sg.patch[1] = sg.patch[2] = 1;
+    sg.kind[0] = 0; sg.rows[0] = 5;
+    sg.kind[1] = 1; sg.shape[1][0] = 1; sg.shape[1][1] = 2; sg.shape[1][2] = 5;
+    sg.kind[2] = 0; sg.rows[2] = 3;
+    sg.kind[3] = 1; sg.shape[3][0] = 2; sg.shape[3][1] = 2; sg.shape[3][2] = 2;
+    bsta_geom g = geom(1, 2, 64, 0, 0, 0);
+    g.segments = &sg;
+    int32_t nt = 0;
+    int64_t lpad = 0;
+    CHECK(attn_geometry(&g, &nt, &lpad, nullptr) == BSTA_OK);
+    CHECK(nt == 5 && lpad == 320);
+    std::vector<int32_t> occ(nt);
+    CHECK(attn_geometry(&g, nullptr, nullptr, occ.data()) == BSTA_OK);
+    CHECK(occ[0] == 5 && occ[1] == 3 && occ[2] == 8 && occ[3] == 2 && occ[4] == 8);
+    int32_t npre = 0, nreg = 0, spans[4] = {};
+    int64_t plen = 0;
+    CHECK(attn_packed_info(&g, &npre, &nreg, spans, &plen) == BSTA_OK);
+    CHECK(npre == 2 && nreg == 2 && plen == 26);
+    CHECK(spans[0] == 2 && spans[1] == 4 && spans[2] == 4 && spans[3] == 5);
+    // per head: 2 prefix rows of 5, 3 video rows of 2 + 1 + 1
+    const int64_t cap = attn_packed_capacity(&g, 0.5, 0.5, 1);
+    CHECK(cap == 2 * (2 * 5 + 3 * 4));
+    CHECK(attn_packed_capacity(&g, 0.5, 0.5, 0) == BSTA_ERR_UNSUPPORTED);
+    CHECK(attn_packed_capacity(&g, 0.5, NAN, 1) == BSTA_ERR_SHAPE);
+    CHECK(attn_packed_capacity(&g, NAN, 0.5, 1) == BSTA_ERR_SHAPE);
+    const int64_t ws = attn_workspace_bytes(&g, BSTA_SELECT_TOPK);
+    const int before = stub_launches();
+    CHECK(attn_select_packed(&g, F, F, 0, 0.5, 0.5, 1, FU8, FI, FI, cap - 1, F, ws, nullptr) ==
+          BSTA_ERR_CAPACITY);
+    CHECK(attn_select_packed(&g, F, F, 0, 0.5, 0.5, 1, FU8, FI, FI, cap, F, ws - 1, nullptr) ==
+          BSTA_ERR_CAPACITY);
+    CHECK(attn_select_packed(&g, nullptr, F, 0, 0.5, 0.5, 1, FU8, FI, FI, cap, F, ws, nullptr) ==
+          BSTA_ERR_NULL);
+    CHECK(stub_launches() == before);
+    CHECK(attn_select_packed(&g, F, F, 0, 0.5, 0.5, 1, FU8, FI, FI, cap, F, ws, nullptr) == BSTA_OK);
+    CHECK(stub_launches() == before + 3);
+    CHECK(attn_select_packed(&g, nullptr, nullptr, BSTA_SELECT_PREPOOLED, 0.5, 0.5, 1, FU8, FI, FI,
+                             cap, F, ws, nullptr) == BSTA_OK);
+    CHECK(stub_launches() == before + 5);
+    // the most segments, each its own region, and one past it
+    bsta_segments big = {};
+    big.patch[0] = big.patch[1] = big.patch[2] = 2;
+    big.count = BSTA_MAX_SEGMENTS;
+    for (int i = 0; i < BSTA_MAX_SEGMENTS; ++i) {
+        big.kind[i] = 1;
+        big.shape[i][0] = big.shape[i][1] = big.shape[i][2] = 8;
+    }
+    g.segments = &big;
+    CHECK(attn_geometry(&g, &nt, nullptr, nullptr) == BSTA_OK);
+    CHECK(nt == BSTA_MAX_SEGMENTS);
+    CHECK(attn_packed_capacity(&g, 0.5, 0.5, 1) == 2 * 16 * 16);
+    big.count = BSTA_MAX_SEGMENTS + 1;
+    CHECK(attn_geometry(&g, nullptr, nullptr, nullptr) == BSTA_ERR_SHAPE);
+    big.count = 1;
+    big.shape[0][1] = 7;  // not a multiple of the patch
+    CHECK(attn_geometry(&g, nullptr, nullptr, nullptr) == BSTA_ERR_SHAPE);
+    // single grid: no packed info
+    bsta_geom single = geom(1, 2, 64, 8, 8, 8);
+    CHECK(attn_packed_info(&single, nullptr, nullptr, nullptr, nullptr) == BSTA_ERR_UNSUPPORTED);
+}
+
 }  // namespace
 
 int main() {
@@ -206,6 +272,7 @@ int main() {
     path_checks();
     bwd_checks();
     thread_checks();
+    packed_checks();
     if (g_failed) return 1;
     printf("OK %d checks, %d stub launches\n", g_checks, stub_launches());
     return 0;

@@ -47,6 +47,11 @@ hipError_t launch_cumulative(const Geo&, float, int, float*, uint8_t*, int32_t*,
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_packed_select(const Geo&, const PackedSpans&, const float*, uint8_t*, int32_t*,
+                                int32_t*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t bwd_scratch(void** out) {
     static char fake_scratch[64];
     *out = fake_scratch;

@@ -371,3 +371,143 @@ def test_binding_argument_errors_before_any_gpu_call():
         bsta.attn_select_cumulative(g, None, None, 0.5, prepooled=True)
     with pytest.raises(ValueError, match="threshold"):
         bsta._select_for(g, None, None, bsta.SELECT_CUMULATIVE, 0, None, None, 0)
+
+
+# ------------------------------------------------------------------ packed sequences
+PACKED_CASES = [
+    ([5, (1, 2, 5), 3, (2, 2, 2)], (1, 1, 1)),
+    ([7, (1, 4, 6), 70, (4, 4, 5)], (1, 1, 1)),
+    ([0, (4, 8, 8), 7], (1, 2, 2)),
+    ([(4, 4, 4), (4, 4, 8)], (1, 1, 1)),
+    ([128, (20, 48, 80)], (1, 1, 1)),
+    ([(5, 6, 7)], (1, 1, 1)),
+]
+
+
+def _pg(segs, patch=(1, 1, 1), B=1, H=2, D=64):
+    return _lib.geom(B, H, D, 0, 0, 0, 4, segs, patch)
+
+
+@pytest.mark.parametrize("segs,patch", PACKED_CASES)
+def test_packed_geometry_matches_oracle(lib, segs, patch):
+    """Tile count, padded length, per-tile occupancy, prefix, spans and
+    packed length of a packed sequence against oracle/packed.py."""
+    from oracle import packed
+    lay = packed.layout(packed.token_segments(segs, patch))
+    g = _pg(segs, patch)
+    nt, lpad = ctypes.c_int32(), ctypes.c_int64()
+    assert lib.attn_geometry(ctypes.byref(g), ctypes.byref(nt), ctypes.byref(lpad), None) == 0
+    assert nt.value == len(lay["occ"])
+    assert lpad.value == 64 * len(lay["occ"])
+    occ = (ctypes.c_int32 * nt.value)()
+    assert lib.attn_geometry(ctypes.byref(g), None, None, occ) == 0
+    assert np.array_equal(np.array(occ), lay["occ"])
+    npre, nreg, plen = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    spans = (ctypes.c_int32 * 32)()
+    assert lib.attn_packed_info(ctypes.byref(g), ctypes.byref(npre), ctypes.byref(nreg), spans,
+                                ctypes.byref(plen)) == 0
+    assert npre.value == lay["num_prefix"]
+    assert plen.value == lay["L"]
+    assert [(spans[2 * r], spans[2 * r + 1]) for r in range(nreg.value)] == lay["spans"]
+
+
+@pytest.mark.parametrize("segs,patch", PACKED_CASES[:4])
+@pytest.mark.parametrize("sparsity,ref,exempt", [(0.5, 0.25, 1), (0.9, 0.1, 1), (0.0, None, 1),
+                                                 (0.75, None, 0), (0.8, 1.0, 1), (1.0, 0.0, 1)])
+def test_packed_capacity_matches_oracle(lib, segs, patch, sparsity, ref, exempt):
+    """CSR entries of the packed selection: B*H times the oracle mask's
+    entries of one head (row lengths do not depend on the scores)."""
+    from oracle import packed
+    lay = packed.layout(packed.token_segments(segs, patch))
+    nt, R = len(lay["occ"]), len(lay["spans"])
+    g = _pg(segs, patch, B=2, H=3)
+    rk = float("nan") if ref is None else ref
+    got = lib.attn_packed_capacity(ctypes.byref(g), sparsity, rk, exempt)
+    if (not exempt and R != 1) or (exempt and R > 1 and ref is None):
+        assert got in (_lib.BSTA_ERR_UNSUPPORTED, _lib.BSTA_ERR_SHAPE)
+        return
+    s = np.random.default_rng(7).standard_normal((1, 1, nt, nt))
+    m = packed.select_mask(s, lay, sparsity, ref, exempt=bool(exempt))
+    assert got == 2 * 3 * int(m.sum())
+
+
+def test_packed_keep_count_double_precision(lib):
+    """k = floor((1 - sparsity) * n) is taken in double precision as the
+    oracle does: 1 - 0.9 is just below 0.1, so a 20-tile span keeps 1, not 2
+    (a float32 sparsity would give 2)."""
+    from oracle import packed
+    segs = [(4, 20, 16)]                    # one region of 5 x 4 = 20 tiles
+    g = _pg(segs, B=1, H=1)
+    cap = lib.attn_packed_capacity(ctypes.byref(g), 0.9, float("nan"), 1)
+    assert packed.keep_count(20, 1.0 - 0.9) == 1
+    assert cap == 20 * 1
+
+
+def test_packed_errors(lib):
+    ok_segs = [5, (4, 4, 4)]
+    bad_geoms = [
+        ([(4, 7, 8)], (1, 2, 2)),           # latent side not a multiple of the patch
+        ([12, 0], (1, 1, 1)),               # no video region
+        ([(4, 4, 0)], (1, 1, 1)),           # empty region
+        ([-1, (4, 4, 4)], (1, 1, 1)),       # negative rows
+        ([(4, 4, 4)], (0, 1, 1)),           # patch 0
+    ]
+    for segs, patch in bad_geoms:
+        assert lib.attn_geometry(ctypes.byref(_pg(segs, patch)), None, None, None) == _lib.BSTA_ERR_SHAPE
+    g = _pg(ok_segs)
+    g.segments.contents.kind[0] = 2          # unknown kind
+    assert lib.attn_geometry(ctypes.byref(g), None, None, None) == _lib.BSTA_ERR_SHAPE
+    g = _pg(ok_segs)
+    g.segments.contents.count = 17
+    assert lib.attn_geometry(ctypes.byref(g), None, None, None) == _lib.BSTA_ERR_SHAPE
+    with pytest.raises(ValueError):
+        _lib.segments([1] * 17)
+    g = _pg(ok_segs)
+    g.tile_x = 8                              # packed sequences use 64-token tiles
+    assert lib.attn_geometry(ctypes.byref(g), None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    # single-grid geometry: no packed info, no packed selection
+    assert lib.attn_packed_info(ctypes.byref(_g()), None, None, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert lib.attn_packed_capacity(ctypes.byref(_g()), 0.5, 0.5, 1) == _lib.BSTA_ERR_UNSUPPORTED
+    g = _pg([3, (4, 4, 4), (4, 4, 8)])
+    nan = float("nan")
+    for sp, rk, ex, want in [(nan, 0.5, 1, _lib.BSTA_ERR_SHAPE), (1.5, 0.5, 1, _lib.BSTA_ERR_SHAPE),
+                             (0.5, nan, 1, _lib.BSTA_ERR_SHAPE), (0.5, 1.5, 1, _lib.BSTA_ERR_SHAPE),
+                             (0.5, 0.5, 0, _lib.BSTA_ERR_UNSUPPORTED)]:
+        assert lib.attn_packed_capacity(ctypes.byref(g), sp, rk, ex) == want
+    cap = lib.attn_packed_capacity(ctypes.byref(g), 0.5, 0.5, 1)
+    ws = lib.attn_workspace_bytes(ctypes.byref(g), _lib.SELECT_TOPK)
+    assert cap > 0 and ws > 0
+
+    def sel(flags=0, q=FAKE, k=FAKE, rp=FAKE, ci=FAKE, cap_=cap, w=FAKE, wsb=ws, geom=g):
+        return lib.attn_select_packed(ctypes.byref(geom), q, k, flags, 0.5, 0.5, 1, None, rp, ci,
+                                      cap_, w, wsb, None)
+    assert sel(rp=None) == _lib.BSTA_ERR_NULL
+    assert sel(q=None) == _lib.BSTA_ERR_NULL
+    assert sel(w=None) == _lib.BSTA_ERR_NULL
+    assert sel(flags=7) == _lib.BSTA_ERR_UNSUPPORTED
+    assert sel(cap_=cap - 1) == _lib.BSTA_ERR_CAPACITY
+    assert sel(wsb=ws - 1) == _lib.BSTA_ERR_CAPACITY
+    assert sel(geom=_g()) == _lib.BSTA_ERR_UNSUPPORTED
+    # window mode and query pruning take a single grid
+    w = (ctypes.c_int32 * 6)(1, 1, 1, 1, 1, 1)
+    assert lib.attn_select_capacity(ctypes.byref(_pg(ok_segs)), _lib.SELECT_STA, 0, w) == \
+        _lib.BSTA_ERR_UNSUPPORTED
+    assert lib.attn_prune_queries(ctypes.byref(_pg(ok_segs)), FAKE, 0.5, FAKE, None, FAKE, None) == \
+        _lib.BSTA_ERR_UNSUPPORTED
+    scale = 1.0 / math.sqrt(64)
+    assert lib.attn_block_sparse_fwd_pruned(ctypes.byref(_pg(ok_segs)), FAKE, FAKE, FAKE, FAKE, FAKE, 16,
+                                            scale, 0, FAKE, 1, FAKE, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+
+
+def test_packed_python_geometry(lib):
+    """Geometry.packed: L and the layout come from the library."""
+    import block_sparse_tiled_amd as m
+    from oracle import packed
+    segs = [5, (1, 2, 5), 3, (2, 2, 2)]
+    g = m.Geometry.packed(1, 2, 64, segs)
+    lay = packed.layout(packed.token_segments(segs))
+    assert g.L == lay["L"] and g.num_tiles == len(lay["occ"]) and g.Lpad == 64 * len(lay["occ"])
+    info = m.attn_packed_info(g)
+    assert info["num_prefix"] == lay["num_prefix"] and info["spans"] == lay["spans"]
+    assert m.attn_packed_capacity(g, 0.5, 0.5) == 2 * int(
+        packed.select_mask(np.zeros((1, 1, 5, 5)), lay, 0.5, 0.5).sum())

@@ -24,6 +24,9 @@ Recipe (one per workload, seed = workload index 0..4):
   * STA windows (sta workloads): per head one of (1,3,3), (3,3,3), (3,5,5)
     tiles, index drawn uniformly from a stream of its own; shared by all
     batch items.
+  * packed sequences (make_packed_inputs): Q, K, V ~ N(0, 1) over the packed
+    length; "smooth" adds the smooth term above to each video region (a
+    field of its own per region), none to dense segments.
   * every tensor is rounded once to bf16 with round-to-nearest-even.
 """
 from __future__ import annotations
@@ -169,6 +172,32 @@ def _add_smooth(w: Workload, q, k):
         sm *= (0.5 / sm.std(axis=0, dtype=np.float64)).astype(np.float32)[None]
         q[:, :, h, :] += sm[None]
         k[:, :, h, :] += sm[None]
+
+
+def make_packed_inputs(B, H, D, token_segments, seed, structure="none"):
+    """bf16 bits q, k, v [B, L, H, D] of a packed sequence.  ``token_segments``
+    lists dense segments (ints, rows) and video regions ((T, Y, X) token
+    grids) in packed order; L is their total length.  Q, K, V ~ N(0, 1) as in
+    make_inputs; with ``structure`` "smooth" each video region r gets the
+    smooth term of a (T, Y, X) grid drawn with seed 1000 * seed + r + 1 (its
+    own fields), dense segments none."""
+    L = sum(int(np.prod(s)) if isinstance(s, tuple) else int(s) for s in token_segments)
+    shape = (B, L, H, D)
+    q = _normal(shape, seed, 0)
+    k = _normal(shape, seed, 1)
+    v = _normal(shape, seed, 2)
+    if structure == "smooth":
+        off, r = 0, 0
+        for s in token_segments:
+            n = int(np.prod(s)) if isinstance(s, tuple) else int(s)
+            if isinstance(s, tuple):
+                w = Workload("region", 1000 * seed + r + 1, B, H, D, *s, "topk", 1, "smooth")
+                _add_smooth(w, q[:, off:off + n], k[:, off:off + n])
+                r += 1
+            off += n
+    elif structure != "none":
+        raise ValueError(f"unknown structure {structure!r}")
+    return {"q": bf16_bits(q), "k": bf16_bits(k), "v": bf16_bits(v)}
 
 
 def sta_windows(w: Workload) -> np.ndarray:
