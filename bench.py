@@ -43,10 +43,10 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "23e2e59dfbcf7165",
-    "fetch_kib": 44082642, "write_kib": 794690, "traffic_bytes": 91095013376,
-    "l2_hit": 0.539, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.460, "clock_ghz": 1.684,
+    "src_sha256_16": "191e06c604be79ce",
+    "fetch_kib": 40914791, "write_kib": 839591, "traffic_bytes": 84653232828,
+    "l2_hit": 0.568, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.457, "clock_ghz": 1.592,
 }
 
 
@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--deterministic", action="store_true",
                    help="walk every CSR row in order (attn_set_deterministic) instead of the "
                         "default rotated key walk")
+    p.add_argument("--legs", default="all", choices=["all", "step"],
+                   help="step: time only the step and its per-call events (for profiling the "
+                        "step's kernels without the side measurements' other workloads)")
     p.add_argument("--mode", default="path", choices=["path", "copy"],
                    help="copy: time a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -260,40 +263,48 @@ def main():
         unfused_ms = float(np.median(per_u))
         del sel_u
 
+    # The side measurements below run other attention workloads (the tiled
+    # output, cold caches, other selections and geometries); --legs step
+    # leaves them out.
+    legs = args.legs == "all"
+
     # The standalone untile pass (not in the step: the attention writes raster
     # order itself), for its HBM rate.
-    bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
-    per_ut = []
-    for _ in range(n_calls):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        bsta.attn_untile(g, ot, out=o)
-        e1.record()
-        torch.cuda.synchronize()
-        per_ut.append(e0.elapsed_time(e1))
-    untile_ms = float(np.median(per_ut))
+    untile_ms = cold_ms = None
+    if legs:
+        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot)
+        per_ut = []
+        for _ in range(n_calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsta.attn_untile(g, ot, out=o)
+            e1.record()
+            torch.cuda.synchronize()
+            per_ut.append(e0.elapsed_time(e1))
+        untile_ms = float(np.median(per_ut))
 
     # Cold-L2 row for the attention call: a 512 MB write before each call
     # evicts the key/value tiles a previous call left in the caches.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(n_calls):
-        flush.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del flush
-    cold_ms = float(np.median(cold))
-    print(f"[bench] attention cold-L2 median ms {cold_ms:.3f}", file=sys.stderr, flush=True)
+    if legs:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(n_calls):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=o, raster=True)
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        cold_ms = float(np.median(cold))
+        print(f"[bench] attention cold-L2 median ms {cold_ms:.3f}", file=sys.stderr, flush=True)
 
     # The cumulative-threshold selection (attn_select_cumulative) on the same
     # pooled Q and K, and the attention over its variable-length rows; not
     # part of the step.
     cum = None
-    if fused and nt <= 2048:
+    if legs and fused and nt <= 2048:
         sel_c = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, want_mask=False, device=dev)
         cq, ck = sel_c.pooled(g)
         cq.copy_(pq)
@@ -326,7 +337,7 @@ def main():
     # the pruned attention (attn_block_sparse_fwd_pruned); not part of the
     # step.  Pruned rows are masked in the attention, not skipped.
     pruned = None
-    if fused and nt <= 2048:
+    if legs and fused and nt <= 2048:
         sel_p = bsta.attn_select_alloc(g, bsta.SELECT_CUMULATIVE, want_mask=False, device=dev)
         ppq, ppk = sel_p.pooled(g)
         ppk.copy_(pk)
@@ -363,7 +374,7 @@ def main():
     # a geometry of half as many tiles and top-k halved (same density); not
     # part of the step.
     t128 = None
-    if w.mode == "topk":
+    if legs and w.mode == "topk":
         g8 = bsta.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X, tile_x=8)
         nt8, lpad8 = bsta.attn_geometry(g8)
         k8 = max(1, min(nt8, w.topk * nt8 // nt))
@@ -402,12 +413,66 @@ def main():
         print(f"[bench] 128-token tiles {t128}", file=sys.stderr, flush=True)
         del qt8, kt8, vt8, sel8
 
+    # A packed sequence (reading of the "video_sparse_attn_h3" page's build()):
+    # a 226-row dense prefix, a 4xYxX reference region kept at 0.5 and the
+    # step's grid as the generated region at sparsity 0.9, on seeded N(0,1)
+    # inputs: tile+pool, packed selection (exempt), raster attention; not
+    # part of the step.
+    packed_leg = None
+    if legs and args.workload == "c3":
+        segs = [226, (4, w.Y, w.X), (w.T, w.Y, w.X)]
+        gp = bsta.Geometry.packed(w.B, w.H, w.D, segs)
+        ntp, lpadp = bsta.attn_geometry(gp)
+        info = bsta.attn_packed_info(gp)
+        gen = torch.Generator(device=dev).manual_seed(11)
+        qp, kp, vp = (torch.randn((w.B, info["L"], w.H, w.D), generator=gen, device=dev)
+                      .to(torch.bfloat16) for _ in range(3))
+        qtp, ktp, vtp = (torch.empty((w.B, lpadp, w.H, w.D), dtype=torch.bfloat16, device=dev)
+                         for _ in range(3))
+        op = torch.empty_like(qp)
+        bsta.attn_tile(gp, qp, out=qtp)
+        bsta.attn_tile(gp, kp, out=ktp)
+        selp = bsta.attn_select_packed(gp, qtp, ktp, 0.9, 0.5, want_mask=False)
+        pqp, pkp = selp.pooled(gp)
+        perp = {"tile_qkv": [], "select": [], "attn_fwd": []}
+        for it in range(n_calls + 2):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            bsta.attn_tile_pool(gp, qp, pqp, out=qtp)
+            bsta.attn_tile_pool(gp, kp, pkp, out=ktp)
+            bsta.attn_tile(gp, vp, out=vtp)
+            e[1].record()
+            bsta.attn_select_packed(gp, None, None, 0.9, 0.5, prepooled=True, out=selp)
+            e[2].record()
+            bsta.attn_block_sparse_fwd(gp, qtp, ktp, vtp, selp.row_ptr, selp.col_idx, out=op,
+                                       raster=True)
+            e[3].record()
+            torch.cuda.synchronize()
+            if it >= 2:
+                for idx, n in enumerate(perp):
+                    perp[n].append(e[idx].elapsed_time(e[idx + 1]))
+        nnzp = int(selp.row_ptr[-1].item())
+        msp = {n: float(np.median(v_)) for n, v_ in perp.items()}
+        flopp = attention_flop(w, nnzp)
+        packed_leg = {"segments": [226, [4, w.Y, w.X], [w.T, w.Y, w.X]], "tiles": ntp,
+                      "prefix_tiles": info["num_prefix"], "spans": info["spans"],
+                      "packed_len": info["L"], "sparsity": 0.9, "ref_keep_rate": 0.5,
+                      "selected_tile_pairs": nnzp, "tile_qkv_ms": msp["tile_qkv"],
+                      "select_ms": msp["select"], "attn_ms": msp["attn_fwd"],
+                      "attn_tflops": flopp / (msp["attn_fwd"] * 1e-3) / 1e12,
+                      "attn_frac_mfma_peak": flopp / (msp["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                      "note": "packed sequence: tile_pool/tile, exempt selection from pooled "
+                              "(prefix kept whole, per-region top-k), raster attention; "
+                              "not in the step"}
+        print(f"[bench] packed sequence {packed_leg}", file=sys.stderr, flush=True)
+        del qp, kp, vp, qtp, ktp, vtp, op, selp
+
     # The backward (attn_block_sparse_bwd) on the step's selection, with a
     # seeded synthetic output gradient; not part of the step.  Its
     # algorithmic work is five products per selected pair (S, dP, dV, dQ,
     # dK), 2.5 times the forward's two.
     bwd = None
-    if nt <= 4096:
+    if legs and nt <= 4096:
         _, lse_b = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot,
                                               want_lse=True)
         gen = torch.Generator(device=dev).manual_seed(7)
@@ -469,7 +534,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel<128>",
+            "kernel": "attn_fwd_kernel<128, 1>",
             "achieved": attn_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -488,9 +553,9 @@ def main():
                          "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
                          "calls": n_calls, "stat": "median",
                          "note": "attn_block_sparse_fwd_raster (output in raster order)"},
-            "attn_fwd_cold_l2": {"ms": cold_ms, "tflops": flop / (cold_ms * 1e-3) / 1e12,
-                                 "frac_mfma_peak": flop / (cold_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                 "note": "512 MB write before each call"},
+            "attn_fwd_cold_l2": ({"ms": cold_ms, "tflops": flop / (cold_ms * 1e-3) / 1e12,
+                                  "frac_mfma_peak": flop / (cold_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                  "note": "512 MB write before each call"} if cold_ms else None),
             "tile_qkv": {"ms": ms["tile_qkv"], "gbps": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9,
                          "frac_hbm_peak": tile_bytes / (ms["tile_qkv"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                          "note": ("attn_tile_pool for Q and K (pooling fused), attn_tile for V"
@@ -513,11 +578,13 @@ def main():
             "select_unfused": ({"ms": unfused_ms, "pool_bytes": pool_bytes,
                                 "note": "pool + scores + top-k from the tiled Q and K; not in the step"}
                                if fused else None),
-            "untile": {"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
-                       "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"},
+            "untile": ({"ms": untile_ms, "gbps": untile_bytes / (untile_ms * 1e-3) / 1e9,
+                        "note": "standalone attn_untile; not in the step (attn_fwd writes raster order)"}
+                       if untile_ms else None),
             "select_cumulative": cum,
             "pruned_queries": pruned,
             "tile128": t128,
+            "packed": packed_leg,
             "attn_bwd": bwd,
         },
     }

@@ -201,6 +201,39 @@ def attention(qt, kt, vt, mask, lay, scale=None, rows=None):
     return out, lse
 
 
+def attention_backward(qt, kt, vt, dot, mask, lay, scale=None):
+    """Gradients of sum(dot * out) for out = attention(qt, kt, vt, mask, lay)
+    (float64, tile-ordered [B, Nt*64, H, D]): per query tile, the softmax
+    chain rule over the valid tokens of its selected tiles
+    (attention.tile_attention_backward), the key/value gradients summed over
+    every query tile that selects them; pad slots get zero."""
+    from .attention import tile_attention_backward
+    B, lpad, H, D = qt.shape
+    occ = lay["occ"]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = (np.zeros((B, lpad, H, D)) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            for i in range(len(occ)):
+                sel = np.nonzero(mask[b, h, i])[0]
+                if len(sel) == 0:
+                    continue
+                keys = np.concatenate([kt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
+                vals = np.concatenate([vt[b, j * E:j * E + occ[j], h] for j in sel]).astype(np.float64)
+                rows = slice(i * E, i * E + occ[i])
+                gq, gk, gv = tile_attention_backward(qt[b, rows, h].astype(np.float64), keys, vals,
+                                                     dot[b, rows, h].astype(np.float64), scale)
+                dq[b, rows, h] = gq
+                at = 0
+                for j in sel:
+                    cols = slice(j * E, j * E + occ[j])
+                    dk[b, cols, h] += gk[at:at + occ[j]]
+                    dv[b, cols, h] += gv[at:at + occ[j]]
+                    at += occ[j]
+    return dq, dk, dv
+
+
 def run(q, k, v, packed_segments, patch=(1, 1, 1), sparsity=0.9, ref_keep_rate=None,
         exempt=True, rows=None):
     """The packed path on float arrays [B, L, H, D]: geometry, tile, pool,

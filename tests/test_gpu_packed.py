@@ -176,6 +176,38 @@ def test_packed_dense_is_full_attention(bsta):
     H.compare_outputs(H.bf16_dev_to_f32(r["o"]), ref, "dense packed vs full attention")
 
 
+@pytest.mark.parametrize("name", ["ragged_two_regions", "three_regions"])
+def test_packed_backward(bsta, name):
+    """attn_block_sparse_bwd on a packed geometry: dQ, dK, dV against the
+    packed oracle under the per-element bound of the single-grid backward
+    tests; pad slots +0.0."""
+    import torch
+    c = _setup(CASES[name])
+    lay = c["lay"]
+    r = _run(bsta, c)
+    g = r["g"]
+    rng = np.random.default_rng(309)
+    do_bits = workloads.bf16_bits(rng.standard_normal((c["B"], g.L, c["H"], c["D"])).astype(np.float32))
+    dot = bsta.attn_tile(g, H.to_dev(do_bits))
+    grads = bsta.attn_block_sparse_bwd(g, r["qt"], r["kt"], r["vt"], r["ot"], dot, r["lse"],
+                                       r["sel"].row_ptr, r["sel"].col_idx)
+    torch.cuda.synchronize()
+    mask = r["sel"].block_mask.cpu().numpy().astype(bool)
+    tf = {n: workloads.bf16_to_f32(packed.tile(c["inp"][n], lay)) for n in ("q", "k", "v")}
+    dtf = workloads.bf16_to_f32(packed.tile(do_bits, lay))
+    ref = packed.attention_backward(tf["q"], tf["k"], tf["v"], dtf, mask, lay)
+    bnd = H.backward_error_bounds(tf["q"], tf["k"], tf["v"], dtf, mask, 0, 0, 0, occ=lay["occ"])
+    valid = lay["slot_token"] >= 0
+    for nm, gt, rf, bd in zip(("dq", "dk", "dv"), grads, ref, bnd):
+        bits = H.from_dev(gt)
+        got = workloads.bf16_to_f32(bits).astype(np.float64)
+        err = np.abs(got[:, valid] - rf[:, valid])
+        ratio = float((err / (bd[:, valid] + 1e-6)).max())
+        H.log(f"  {nm}: max err {err.max():.3g}, max err/bound {ratio:.3f}")
+        assert np.all(err <= bd[:, valid] + 1e-6), f"{nm}: error above its bound (ratio {ratio:.3f})"
+        assert np.all(bits[:, ~valid] == 0), f"{nm}: pad slots must be +0.0"
+
+
 @pytest.mark.timeout(900)
 def test_packed_full_size(bsta):
     """A 226-row dense prefix, a 4x48x80 reference region at keep 0.5 and the

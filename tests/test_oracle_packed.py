@@ -145,3 +145,47 @@ def test_pool_matches_grouped_sums():
     np.add.at(sums, tile_of, x[0])
     want = (sums / np.bincount(tile_of)[:, None, None]).astype(np.float32).transpose(1, 0, 2)
     assert np.array_equal(packed.pool(packed.tile(x, lay), lay)[0], want)
+
+
+def test_backward_against_autograd():
+    """The packed gradients equal torch autograd (float64) of softmax
+    attention over the packed tokens under the token mask the tile mask
+    implies, on a prefix plus two regions with ragged tiles."""
+    rng = np.random.default_rng(105)
+    segs = [9, (2, 4, 6), (3, 5, 4)]
+    lay = packed.layout(packed.token_segments(segs))
+    L = lay["L"]
+    q, k, v, do = (rng.standard_normal((1, L, 2, 8)) for _ in range(4))
+    r = packed.run(q, k, v, segs, sparsity=0.6, ref_keep_rate=0.5)
+    dot = packed.tile(do, lay)
+    dq, dk, dv = packed.attention_backward(r["qt"], r["kt"], r["vt"], dot, r["mask"], lay)
+    tile_of = np.empty(L, dtype=np.int64)
+    valid = lay["slot_token"] >= 0
+    tile_of[lay["slot_token"][valid]] = np.nonzero(valid)[0] // 64
+    tq, tk, tv = (torch.from_numpy(x.transpose(0, 2, 1, 3).copy()).requires_grad_() for x in (q, k, v))
+    allowed = torch.from_numpy(r["mask"][0][:, tile_of][:, :, tile_of])          # [H, L, L]
+    s = tq @ tk.transpose(-1, -2) / math.sqrt(8)
+    s = s.masked_fill(~allowed[None], float("-inf"))
+    out = torch.softmax(s, dim=-1) @ tv
+    (out * torch.from_numpy(do.transpose(0, 2, 1, 3))).sum().backward()
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        want = ref.numpy().transpose(0, 2, 1, 3)
+        assert np.allclose(packed.untile(got, lay), want, rtol=0, atol=1e-12)
+        assert np.all(got[:, ~valid] == 0)
+
+
+def test_backward_single_region_is_the_grid_backward():
+    """One region, no dense segment: the grid backward of the single-grid
+    oracle on the same mask."""
+    from oracle import attention as oatt
+    rng = np.random.default_rng(106)
+    T, Y, X = 5, 6, 7
+    lay = packed.layout(packed.token_segments([(T, Y, X)]))
+    nt = len(lay["occ"])
+    qt, kt, vt, dot = (packed.tile(rng.standard_normal((1, T * Y * X, 2, 16)), lay) for _ in range(4))
+    mask = rng.random((1, 2, nt, nt)) < 0.5
+    mask[..., 0] = True
+    got = packed.attention_backward(qt, kt, vt, dot, mask, lay)
+    ref = oatt.block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=0, atol=1e-12)
