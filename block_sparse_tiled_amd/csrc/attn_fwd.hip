@@ -177,10 +177,11 @@ __device__ inline int sweep_target(uint32_t c, uint32_t period, int nt) {
 }
 
 // Read of the sweep clock: an atomic load, which is served by the XCD's L2
-// (where the counter's atomic adds happen), not by a CU's L1.
-__device__ inline uint32_t read_sweep(const unsigned int* ctr) {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+// (where the counter's atomic adds happen), not by a CU's L1.  The caller
+// takes the value with readfirstlane where it needs it, so that the load's
+// latency can overlap other work.
+__device__ inline uint32_t sweep_load(const unsigned int* ctr) {
+    return __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 }  // namespace
@@ -258,16 +259,54 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int half4 = 4 * half;
 
     // Persistent, XCD-aware schedule.  Workgroups are dealt round-robin over
-    // the 8 XCDs, so workgroup w runs on XCD w%8.  XCD e owns the contiguous
-    // run [e*items_per_xcd, (e+1)*items_per_xcd) of query tiles in (b, h, i)
-    // order; its resident workgroups take them in rounds of S.
+    // the 8 XCDs, so workgroup w runs on XCD w%8.  XCD e owns a contiguous
+    // run of query units in (b, h, i) order (below); its resident
+    // workgroups take them in rounds of S.
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int S = gridDim.x >> 3;
     const int64_t n_rows = (int64_t)g.B * g.H * g.Nt;  // CSR rows
     const int64_t n_items = n_rows * SUB;
-    const int64_t first = (int64_t)xcd * items_per_xcd;
-    const int64_t last = first + items_per_xcd < n_items ? first + items_per_xcd : n_items;
+    int64_t nnz = rp_s[n_rows];
+    nnz = nnz < 0 ? 0 : (nnz > col_len ? col_len : nnz);
+    // Rows of equal length (every top-k CSR): the even split, items_per_xcd
+    // units each.  Otherwise XCD e owns the rows [r_e, r_e+1), r_e the first
+    // row whose CSR start reaches e/8 of the entries, so that every XCD
+    // walks the same number of key tiles (window rows differ per head, and
+    // threshold rows per row).  Both of the XCD's boundaries are found at
+    // once, each by a 32-way search in one half of the wave (a row_ptr
+    // that decreases somewhere, which the interface rules out, can only
+    // make two XCDs share rows, never leave one out).
+    int64_t first, last;
+    const int64_t len0 = (int64_t)rp_s[1] - (int64_t)rp_s[0];
+    if (rp_s[0] == 0 && len0 * n_rows == (int64_t)rp_s[n_rows]) {
+        first = (int64_t)xcd * items_per_xcd;
+        last = first + items_per_xcd < n_items ? first + items_per_xcd : n_items;
+    } else {
+        const int hsel = lane >> 5, j = lane & 31;
+        const int64_t target = nnz * (xcd + hsel) / 8;
+        int64_t lo = 0, hi = n_rows;  // smallest r with r == n_rows or row_ptr[r] >= target
+        int iters = 1;
+        for (int64_t span = 32; span <= n_rows; span *= 32) ++iters;
+        for (int it = 0; it <= iters; ++it) {
+            const int64_t step = (hi - lo + 31) / 32 > 0 ? (hi - lo + 31) / 32 : 1;
+            const int64_t p = lo + step * j < hi ? lo + step * j : hi;
+            const bool ge = p >= n_rows || (int64_t)row_ptr[p] >= target;
+            const uint64_t m = (__builtin_amdgcn_ballot_w64(ge) >> (32 * hsel)) & 0xffffffffull;
+            const int js = m ? __builtin_ctzll(m) : 32;
+            const int64_t pj = lo + step * js < hi ? lo + step * js : hi;
+            if (js > 0) lo = lo + step * (js - 1) + 1;
+            hi = js < 32 ? pj : hi;
+            if (lo > hi) lo = hi;
+        }
+        // The first and last boundaries are fixed: trailing empty rows (and
+        // rows before a negative start) still get their outputs written.
+        const int64_t r0 = xcd == 0 ? 0 : __builtin_amdgcn_readlane((int)lo, 0);
+        int64_t r1 = xcd == 7 ? n_rows : __builtin_amdgcn_readlane((int)lo, 32);
+        if (r1 < r0) r1 = r0;
+        first = r0 * SUB;
+        last = r1 * SUB;
+    }
 
     // Key-order rotation for L2 reuse.  The rows' key tiles are scattered
     // over the whole head, so the K/V working set of one XCD's resident
@@ -280,8 +319,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // then touch neighbouring key ids whatever their start times.  Any
     // rotation visits the same set of keys, so only rounding depends on it.
     unsigned int* const sweep = &g_sweep[xcd * 32];
-    int64_t nnz = rp_s[n_rows];
-    nnz = nnz < 0 ? 0 : (nnz > col_len ? col_len : nnz);
     const uint64_t per_raw = (uint64_t)S * SUB * (uint64_t)nnz / (uint64_t)(n_rows > 0 ? n_rows : 1);
     const uint32_t period = per_raw == 0 ? 1u : (per_raw > 0x7fffffffu ? 0x7fffffffu : (uint32_t)per_raw);
     // Wave 0 hands each item's rotation start to wave 1 through the first
@@ -307,36 +344,34 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int ne = (int)(p1 - p0);  // CSR entries
         const int n = ne * SUB;         // key steps
 
-        // Rotation start k0: the number of the row's entries below the sweep
-        // target, i.e. for a sorted row the first entry at or above it (any
-        // start visits the same entries).  With rotation off (deterministic
-        // mode) every row is walked from its first entry.
+        // Rotation start k0: the step at the same fraction of the row as the
+        // sweep target is of the key range, target * n / NU.  For a row
+        // whose ids spread evenly over the head that is about the first
+        // entry at or above the target, without reading the row's ids (an
+        // exact count, one pass over them, measured 1.5-3% slower per call);
+        // any start visits the same entries.  With rotation off
+        // (deterministic mode) every row is walked from its first entry.
         int k0 = 0;
+        const bool rot = rotate && n > 1;  // workgroup-uniform
+        // The sweep clock is read first, so that its latency overlaps the
+        // check of the row's ids below.
+        const uint32_t clock_v = rot && wave == 0 ? sweep_load(sweep) : 0u;
         // A clean row (every tile full, every id in range) needs no key
         // masking, so its steps skip the tile lookup that masking needs.
-        // Both waves read the same ids and reach the same verdict.
+        // The ids of the first 128 entries are loaded here and checked after
+        // the first acquire, whose wait for K(0) hides their latency (the
+        // rest of a longer row is checked there too).  Both waves read the
+        // same ids and reach the same verdict.
         bool clean = all_full;
+        int idc0 = 0, idc1 = 0;
         if (all_full) {
-            for (int base = 0; base < ne; base += 64) {
-                const int idx = base + lane;
-                const int j = idx < ne ? col_idx[p0 + idx] : 0;
-                clean = clean && __builtin_amdgcn_ballot_w64((unsigned)j >= (unsigned)g.Nt) == 0;
-            }
+            idc0 = lane < ne ? col_idx[p0 + lane] : 0;
+            idc1 = 64 + lane < ne ? col_idx[p0 + 64 + lane] : 0;
         }
-        if (rotate && n > 1) {  // workgroup-uniform
+        if (rot) {
             if (wave == 0) {
-                const uint32_t c = read_sweep(sweep);
-                const int target = sweep_target(c, period, NU);
-                // Key units below the target (entry j stands for units
-                // SUB*j .. SUB*j + SUB-1).
-                int cnt = 0;
-                for (int base = 0; base < ne; base += 64) {
-                    const int idx = base + lane;
-                    const int j = idx < ne ? col_idx[p0 + idx] : 0x3fffffff;
-#pragma unroll
-                    for (int u = 0; u < SUB; ++u)
-                        cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(SUB * j + u < target));
-                }
+                const int target = sweep_target(__builtin_amdgcn_readfirstlane(clock_v), period, NU);
+                const int cnt = (int)(((int64_t)target * n) / NU);
                 if (lane == 0) *handoff = cnt < n ? cnt : 0;
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -542,6 +577,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (n > 0) {
             int sl;
             BSTA_ACQUIRE(sl);
+            if (all_full) {
+                clean = __builtin_amdgcn_ballot_w64((unsigned)idc0 >= (unsigned)g.Nt ||
+                                                    (unsigned)idc1 >= (unsigned)g.Nt) == 0;
+                for (int base = 128; base < ne; base += 64) {
+                    const int idx = base + lane;
+                    const int j = idx < ne ? col_idx[p0 + idx] : 0;
+                    clean = clean && __builtin_amdgcn_ballot_w64((unsigned)j >= (unsigned)g.Nt) == 0;
+                }
+            }
             scores(sl, sc_cur, [](int) {});
             nj_cur = clean ? 64 : mask(sc_cur, tile_id(0));
         }
