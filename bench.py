@@ -37,16 +37,19 @@ PRUNE_RATIO = 0.5
 METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI355X"
 
 # Counter readings of the attention kernel on the default workload, from the
-# rocprofv3 summaries under profiles/ (attn_path_c3_counters.txt).  HBM bytes per
+# rocprofv3 summaries under profiles/ (attn_path_c3_counters.txt, and
+# attn_fwd_c3_instruction_mix.txt for the instructions per key tile and wave).  HBM bytes per
 # launch = FETCH_SIZE KiB * 1024 * 2.0 + WRITE_SIZE KiB * 1024 * 1.0, the
 # factors read off a plain 1 GiB copy (copy_1GiB_hbm_calibration.txt).  The
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "191e06c604be79ce",
-    "fetch_kib": 40914791, "write_kib": 839591, "traffic_bytes": 84653232828,
-    "l2_hit": 0.568, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.457, "clock_ghz": 1.592,
+    "src_sha256_16": "3b94c5492f1615ae",
+    "fetch_kib": 37191664, "write_kib": 791945, "traffic_bytes": 76979479629,
+    "l2_hit": 0.607, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.467, "clock_ghz": 1.634,
+    "insts_per_key_tile_wave": {"valu": 193.9, "mfma": 32.0, "salu": 117.9, "lds": 48.0,
+                                "branch": 25.3, "vmem": 16.3, "smem": 1.0},
 }
 
 
@@ -543,7 +546,8 @@ def main():
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
             "algorithmic_flop_per_launch": flop,
             "counters": ({k: prof[k] for k in ("l2_hit", "lds_bank_conflict_per_active",
-                                               "mfma_busy", "clock_ghz")} if prof else None),
+                                               "mfma_busy", "clock_ghz",
+                                               "insts_per_key_tile_wave")} if prof else None),
         },
         "kernels": {
             "attn_fwd": {"ms": ms["attn_fwd"], "tflops": attn_tflops,
