@@ -31,7 +31,8 @@ __all__ = [
     "attn_tile",
     "attn_tile_pool", "attn_pool", "attn_untile", "attn_select_alloc",
     "attn_select_blocks", "attn_block_sparse_fwd", "attn_geometry", "attn_select_capacity",
-    "attn_workspace_bytes", "attn_set_deterministic", "block_sparse_attention",
+    "attn_workspace_bytes", "attn_set_deterministic", "attn_set_key_walk", "WALK_AUTO",
+    "WALK_CSR", "WALK_ROTATED", "block_sparse_attention",
 ]
 
 
@@ -480,11 +481,26 @@ def attn_block_sparse_bwd_noalloc(g: Geometry, q_tiled, k_tiled, v_tiled, o_tile
     return out
 
 
+# Key walks of attn_block_sparse_fwd (attn_set_key_walk).
+WALK_AUTO, WALK_CSR, WALK_ROTATED = 0, 1, 2
+
+
+def attn_set_key_walk(mode: int) -> int:
+    """Process-wide key order of attn_block_sparse_fwd: WALK_AUTO (the
+    default: the cache-friendly rotated walk for large heads whose rows
+    spread over the key range, CSR order otherwise), WALK_CSR (every row in
+    CSR order, bitwise reproducible) or WALK_ROTATED (every row rotated).
+    Returns the previous mode."""
+    if mode not in (WALK_AUTO, WALK_CSR, WALK_ROTATED):
+        raise ValueError(f"key walk {mode!r}: WALK_AUTO, WALK_CSR or WALK_ROTATED")
+    return int(_lib.load().attn_set_deterministic(int(mode)))
+
+
 def attn_set_deterministic(enable: bool) -> bool:
-    """Process-wide key order of attn_block_sparse_fwd: True walks every CSR
-    row in order (bitwise reproducible), False (the default) uses the
-    cache-friendly rotated walk.  Returns the previous setting."""
-    return bool(_lib.load().attn_set_deterministic(int(bool(enable))))
+    """True: every CSR row walked in order (WALK_CSR, bitwise reproducible);
+    False: the default walk (WALK_AUTO).  Returns whether the previous mode
+    was WALK_CSR."""
+    return attn_set_key_walk(WALK_CSR if enable else WALK_AUTO) == WALK_CSR
 
 
 def block_sparse_attention(g: Geometry, q, k, v, mode: int = SELECT_TOPK, topk: int = 0,

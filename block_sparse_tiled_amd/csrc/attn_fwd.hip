@@ -319,6 +319,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // then touch neighbouring key ids whatever their start times.  Any
     // rotation visits the same set of keys, so only rounding depends on it.
     unsigned int* const sweep = &g_sweep[xcd * 32];
+    // rotate: 0 = CSR order, 2 = always rotated, 1 = rotated where it pays.
+    // The rotation shares cache lines among workgroups whose rows scatter
+    // over a head too large for the caches.  A head of at most two L2s of
+    // K and V, or rows that keep to a part of the key range (sliding
+    // windows), reuse lines in CSR order already, and there the walk's
+    // handoff and counter traffic cost more than they save.  The XCD's first
+    // row stands for the rest: its first and last ids span under 3/4 of the
+    // head's tiles in a window selection, nearly all of them otherwise.
+    if (rotate == 1) {
+        const uint64_t head_bytes = (uint64_t)NU * 64 * D * 2 * 2;
+        bool wide = head_bytes > (8ull << 20);
+        if (wide && first < last) {
+            const int64_t r = first / SUB;
+            int64_t a = rp_s[r], e = rp_s[r + 1];
+            a = a < 0 ? 0 : (a > col_len ? col_len : a);
+            e = e < a ? a : (e > col_len ? col_len : e);
+            if (e - a >= 2) wide = (int64_t)4 * ((int64_t)ci_s[e - 1] - ci_s[a]) >= (int64_t)3 * g.Nt;
+        }
+        rotate = wide ? 1 : 0;
+    }
     const uint64_t per_raw = (uint64_t)S * SUB * (uint64_t)nnz / (uint64_t)(n_rows > 0 ? n_rows : 1);
     const uint32_t period = per_raw == 0 ? 1u : (per_raw > 0x7fffffffu ? 0x7fffffffu : (uint32_t)per_raw);
     // Wave 0 hands each item's rotation start to wave 1 through the first
@@ -762,7 +782,7 @@ int resident_per_xcd(const void* kernel, int which) {
 template <int D, int SUB>
 hipError_t launch_variant(const Geo& g, const void* q, const void* k, const void* v,
                           const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                          float scale_log2, void* o, float* lse, const uint64_t* keep, bool rotate,
+                          float scale_log2, void* o, float* lse, const uint64_t* keep, int rotate,
                           bool raster, hipStream_t stream) {
     const void* kernel = (const void*)attn_fwd_kernel<D, SUB>;
     const int64_t n_items = (int64_t)g.B * g.H * g.Nt * SUB;
@@ -772,7 +792,7 @@ hipError_t launch_variant(const Geo& g, const void* q, const void* k, const void
     const unsigned blocks = (unsigned)(8 * per_xcd);
     hipLaunchKernelGGL((attn_fwd_kernel<D, SUB>), dim3(blocks), dim3(128), 0, stream, g,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd, rotate ? 1 : 0,
+                       col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd, rotate,
                        raster ? 1 : 0);
     return hipGetLastError();
 }
@@ -781,7 +801,7 @@ hipError_t launch_variant(const Geo& g, const void* q, const void* k, const void
 
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, const uint64_t* keep, bool rotate,
+                           float scale, void* o, float* lse, const uint64_t* keep, int rotate,
                            bool raster, hipStream_t stream) {
     const float sl2 = scale * 1.4426950408889634f;
     if (g.D == 128 && g.sub == 1)

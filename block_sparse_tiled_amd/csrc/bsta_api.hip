@@ -46,7 +46,7 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
                            hipStream_t stream);
 hipError_t launch_attn_fwd(const Geo& g, const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx, int64_t col_len,
-                           float scale, void* o, float* lse, const uint64_t* keep, bool rotate,
+                           float scale, void* o, float* lse, const uint64_t* keep, int rotate,
                            bool raster, hipStream_t stream);
 hipError_t launch_prune(const Geo& g, const void* q_tiled, double ratio, uint64_t* keep_mask,
                         int32_t* keep_count, float* pooled_q, hipStream_t stream);
@@ -59,8 +59,13 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Process-wide key-order mode of attn_block_sparse_fwd (0 = rotated walk).
+// Process-wide key-order mode of attn_block_sparse_fwd (attn_set_deterministic:
+// 0 = rotated where it pays, 1 = CSR order, 2 = rotated on every row).
 std::atomic<int> g_deterministic{0};
+
+// The kernel's rotate argument for a mode: 0 CSR order, 1 rotated where it
+// pays (the kernel decides), 2 rotated always.
+int walk_of(int mode) { return mode == 1 ? 0 : (mode == 2 ? 2 : 1); }
 
 // Largest tile count top-k selection accepts (its per-row keys and flags
 // live in LDS: 5 bytes per tile).
@@ -383,7 +388,7 @@ int32_t block_sparse_fwd(const char* name, const bsta_geom* gin, const void* q_t
     if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
     return hip_status(bsta::launch_attn_fwd(g, q_tiled, k_tiled, v_tiled, row_ptr, col_idx,
                                             col_len, softmax_scale, o, lse, keep,
-                                            g_deterministic.load(std::memory_order_relaxed) == 0,
+                                            walk_of(g_deterministic.load(std::memory_order_relaxed)),
                                             raster, (hipStream_t)stream),
                       name);
 }
@@ -790,7 +795,8 @@ int32_t attn_block_sparse_bwd_noalloc(const bsta_geom* gin, const void* q_tiled,
 }
 
 int32_t attn_set_deterministic(int32_t enable) {
-    return g_deterministic.exchange(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+    const int mode = enable == 0 ? 0 : (enable == 2 ? 2 : 1);
+    return g_deterministic.exchange(mode, std::memory_order_relaxed);
 }
 
 }  // extern "C"

@@ -344,12 +344,16 @@ int32_t attn_select_packed(const bsta_geom* g, const void* q_tiled, const void* 
  *   lse      [out, fp32 [B, H, Lpad], may be NULL] natural-log softmax
  *            normaliser of the scaled scores
  * Key order.  The softmax is a sum over the row's key tiles, so their order
- * changes only rounding.  By default each row is walked cyclically from a
- * start that depends on how far the GPU has progressed through the call (a
- * device-side counter), so that workgroups running at the same time read
- * neighbouring key tiles and share them in cache; results then agree with
- * any other order to rounding but are not bitwise reproducible from call to
- * call.  attn_set_deterministic(1) walks every row in its CSR order instead.
+ * changes only rounding.  By default, when a head's K and V exceed 8 MiB
+ * and rows spread over most of the head (top-k and threshold selections),
+ * each row is walked cyclically from a start that depends on how far the
+ * GPU has progressed through the call (a device-side counter), so that
+ * workgroups running at the same time read neighbouring key tiles and share
+ * them in cache; results then agree with any other order to rounding but
+ * are not bitwise reproducible from call to call.  Smaller heads and rows
+ * that keep to part of the key range (sliding windows) are walked in CSR
+ * order.  attn_set_deterministic(1) walks every row in CSR order,
+ * attn_set_deterministic(2) every row rotated.
  */
 int32_t attn_block_sparse_fwd(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const int32_t* row_ptr, const int32_t* col_idx,
@@ -493,11 +497,12 @@ int32_t attn_block_sparse_bwd_noalloc(const bsta_geom* g, const void* q_tiled,
 
 /*
  * attn_set_deterministic (host only, no HIP call): process-wide key order of
- * attn_block_sparse_fwd for calls made after it returns.  enable != 0: every
- * row is walked in CSR order, so equal inputs give bitwise equal outputs;
- * 0 (the default): the cache-friendly rotated walk described above.
- * Returns the previous setting (0 or 1).  Thread-safe; calls already
- * enqueued keep the mode they were made with.
+ * attn_block_sparse_fwd for calls made after it returns.  0 (the default):
+ * the rotated walk where it pays, CSR order elsewhere (see the key order
+ * above); 1 (or any value other than 0 and 2): every row in CSR order, so
+ * equal inputs give bitwise equal outputs; 2: every row rotated.  Returns
+ * the previous setting (0, 1 or 2).  Thread-safe; calls already enqueued
+ * keep the mode they were made with.
  */
 int32_t attn_set_deterministic(int32_t enable);
 

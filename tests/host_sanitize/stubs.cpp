@@ -65,7 +65,7 @@ hipError_t launch_attn_bwd(const Geo&, const void*, const void*, const void*, co
     return hipSuccess;
 }
 hipError_t launch_attn_fwd(const Geo&, const void*, const void*, const void*, const int32_t*,
-                           const int32_t*, int64_t, float, void*, float*, const uint64_t*, bool,
+                           const int32_t*, int64_t, float, void*, float*, const uint64_t*, int,
                            bool, hipStream_t) {
     ++g_launches;
     return hipSuccess;

@@ -351,16 +351,32 @@ def test_status_strings(lib):
 
 
 def test_set_deterministic_returns_previous(lib):
-    """Host-only switch: each call returns the previous mode (0 or 1)."""
+    """Host-only switch: each call returns the previous mode (0 default walk,
+    1 CSR order, 2 rotated everywhere; other values mean 1)."""
     first = lib.attn_set_deterministic(1)
     try:
-        assert first in (0, 1)
+        assert first in (0, 1, 2)
         assert lib.attn_set_deterministic(1) == 1
         assert lib.attn_set_deterministic(0) == 1
         assert lib.attn_set_deterministic(7) == 0
-        assert lib.attn_set_deterministic(0) == 1
+        assert lib.attn_set_deterministic(2) == 1
+        assert lib.attn_set_deterministic(0) == 2
+        assert lib.attn_set_deterministic(0) == 0
     finally:
         lib.attn_set_deterministic(first)
+
+
+def test_key_walk_binding(lib):
+    import block_sparse_tiled_amd as m
+    first = m.attn_set_key_walk(m.WALK_ROTATED)
+    try:
+        assert m.attn_set_key_walk(m.WALK_CSR) == m.WALK_ROTATED
+        assert m.attn_set_deterministic(False) is True
+        assert m.attn_set_key_walk(m.WALK_AUTO) == m.WALK_AUTO
+        with pytest.raises(ValueError):
+            m.attn_set_key_walk(3)
+    finally:
+        m.attn_set_key_walk(first)
 
 
 def test_binding_argument_errors_before_any_gpu_call():

@@ -294,7 +294,7 @@ def test_fwd_raster_equals_fwd_then_untile(bsta, name):
 def test_heads_first_layout(bsta, name):
     """A heads-first [B, H, L, D] layout is the geometry (B*H, 1): every call
     runs unchanged on it.  Its selection is the oracle's (tie band), its
-    output (default rotated key walk) matches the oracle's attention under
+    output (default key walk) matches the oracle's attention under
     that selection, and with the CSR-order walk tiles, CSR and output equal
     those of the standard [B, L, H, D] layout head by head, bit for bit."""
     import torch
@@ -356,16 +356,21 @@ def test_concurrent_calls_on_two_streams(bsta):
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = []
-    for rep in range(3):
-        pair = []
-        for (w, inp, r), st in zip(prep, streams):
-            with torch.cuda.stream(st):
-                o = torch.full((w.B, w.L, w.H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
-                bsta.attn_block_sparse_fwd(r["g"], r["qt"], r["kt"], r["vt"], r["sel"].row_ptr,
-                                           r["sel"].col_idx, out=o, raster=True)
-            pair.append(o)
-        outs.append(pair)
-    torch.cuda.synchronize()
+    prev = bsta.attn_set_key_walk(bsta.WALK_ROTATED)  # both calls use the counters
+    try:
+        for rep in range(3):
+            pair = []
+            for (w, inp, r), st in zip(prep, streams):
+                with torch.cuda.stream(st):
+                    o = torch.full((w.B, w.L, w.H, w.D), float("nan"), dtype=torch.bfloat16,
+                                   device="cuda")
+                    bsta.attn_block_sparse_fwd(r["g"], r["qt"], r["kt"], r["vt"], r["sel"].row_ptr,
+                                               r["sel"].col_idx, out=o, raster=True)
+                pair.append(o)
+            outs.append(pair)
+        torch.cuda.synchronize()
+    finally:
+        bsta.attn_set_key_walk(prev)
     for n, (w, inp, r) in enumerate(prep):
         H.log(f"two streams: {w.name}")
         _, tf = _oracle_tiled(w, inp)
@@ -994,24 +999,26 @@ def test_deterministic(bsta):
     assert np.array_equal(a["sel"].col_idx.cpu().numpy(), b["sel"].col_idx.cpu().numpy())
 
 
-def test_rotated_walk_matches_deterministic(bsta):
-    """The default rotated key walk differs from the CSR-order walk by
-    rounding only: the same selection, outputs within the parity bound of each
-    other and of the oracle, over several calls (each starts its rows at
-    different keys)."""
+@pytest.mark.parametrize("walk", ["rotated", "auto"])
+def test_rotated_walk_matches_deterministic(bsta, walk):
+    """The rotated key walk (forced on every row, and the default walk that
+    rotates where it pays) differs from the CSR-order walk by rounding only:
+    the same selection, outputs within the parity bound of each other, over
+    several calls (each starts its rows at different keys)."""
     w = SMALL["smooth_40"]
     inp = H.inputs(w)
-    prev = bsta.attn_set_deterministic(True)
+    prev = bsta.attn_set_key_walk(bsta.WALK_CSR)
     try:
+        assert prev == bsta.WALK_AUTO, "the default mode is the automatic walk"
         ref = _run_gpu(bsta, w, inp)
+        bsta.attn_set_key_walk(bsta.WALK_ROTATED if walk == "rotated" else bsta.WALK_AUTO)
+        want = H.bf16_dev_to_f32(ref["o"])
+        for _ in range(3):
+            r = _run_gpu(bsta, w, inp)
+            assert np.array_equal(r["sel"].col_idx.cpu().numpy(), ref["sel"].col_idx.cpu().numpy())
+            H.compare_outputs(H.bf16_dev_to_f32(r["o"]), want, f"{walk} walk vs CSR order")
     finally:
-        bsta.attn_set_deterministic(prev)
-    assert prev is False, "the default mode is the rotated walk"
-    want = H.bf16_dev_to_f32(ref["o"])
-    for _ in range(3):
-        r = _run_gpu(bsta, w, inp)
-        assert np.array_equal(r["sel"].col_idx.cpu().numpy(), ref["sel"].col_idx.cpu().numpy())
-        H.compare_outputs(H.bf16_dev_to_f32(r["o"]), want, "rotated vs CSR order")
+        bsta.attn_set_key_walk(prev)
 
 
 # ---------------------------------------------------------------- full sizes
@@ -1096,7 +1103,8 @@ def _bench_route(m, w, inp):
     attn_tile tiles V, and attn_select_blocks starts from the pooled vectors
     (SELECT_PREPOOLED); with windows, attn_tile tiles all three.  The
     attention writes raster order itself (attn_block_sparse_fwd_raster) in
-    the library's default rotated key walk, into a buffer that starts as
+    the library's default key walk (rotated for the top-k workloads, CSR
+    order for windows), into a buffer that starts as
     NaN, so a row left unwritten shows.  No block mask is requested."""
     import torch
     g = _geom(m, w)
@@ -1133,7 +1141,7 @@ def _bench_route_check(bsta, w, inp, tb, tf, s, pq, pk):
     query tile of every (b, h) (plus the first and last tiles) element-wise
     against the oracle's attention under the GPU's validated selection."""
     import torch
-    assert bsta.attn_set_deterministic(False) is False, "default mode is the rotated walk"
+    assert bsta.attn_set_deterministic(False) is False, "the default mode is the automatic walk"
     H.log(f"full size {w.name}: benchmark route")
     r = _bench_route(bsta, w, inp)
     g = r["g"]
@@ -1165,7 +1173,7 @@ def _bench_route_check(bsta, w, inp, tb, tf, s, pq, pk):
 
 
 def _oracle_csr_full_head(bsta, w, r, tf, s, h0):
-    """The benchmarked attention call (raster output, rotated walk) on the
+    """The benchmarked attention call (raster output, default walk) on the
     oracle's own top-k selection for head h0, every other row empty: all of
     head h0's query tiles against the oracle; the other heads' rows are zero."""
     import torch
