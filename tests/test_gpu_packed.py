@@ -30,6 +30,10 @@ CASES = {
     "three_regions": (1, 4, 128, [226, (8, 16, 20), (6, 16, 20), (12, 16, 20)], (1, 1, 1), 0.8, 0.3,
                       True, "smooth", 305),
     "dense_build": (1, 2, 64, [33, (5, 6, 7), (4, 4, 9)], (1, 1, 1), 0.0, 0.5, True, "none", 306),
+    # the most segments: eight dense (one empty, dropped) and eight regions, one of a single token
+    "sixteen_segments": (1, 2, 64, [3, (1, 2, 3), 70, (2, 4, 4), 1, (4, 4, 4), 65, (1, 1, 1), 0,
+                                    (3, 5, 2), 128, (2, 2, 9), 5, (4, 8, 4), 7, (1, 3, 3)],
+                         (1, 1, 1), 0.5, 0.4, True, "none", 310),
 }
 
 
