@@ -31,10 +31,11 @@
  *     comment says host.  The caller allocates and owns all memory and the
  *     stream.  The library allocates nothing, frees nothing, never
  *     synchronises, and enqueues every kernel on the given stream (a
- *     hipStream_t passed as void*; NULL = the null stream).  Its only device
+ *     hipStream_t passed as void*; NULL = the null stream).  Its device
  *     state is a small static array of counters that attn_block_sparse_fwd
- *     uses to order its walk over each row's key tiles (see there); it
- *     never decides which keys are attended.
+ *     uses to order its walk over each row's key tiles (see there; it
+ *     never decides which keys are attended), and the static scratch of
+ *     attn_block_sparse_bwd_noalloc, used by that call alone.
  *   - Every call checks its arguments on the host before any HIP call and
  *     returns a status (0 = BSTA_OK).  On failure nothing is enqueued and
  *     attn_last_error() returns a thread-local message with the detail.
