@@ -44,11 +44,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "3b94c5492f1615ae",
-    "fetch_kib": 37191664, "write_kib": 791945, "traffic_bytes": 76979479629,
-    "l2_hit": 0.607, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.467, "clock_ghz": 1.634,
-    "insts_per_key_tile_wave": {"valu": 193.9, "mfma": 32.0, "salu": 117.9, "lds": 48.0,
+    "src_sha256_16": "63064fd9b4a2d06c",
+    "fetch_kib": 37253826, "write_kib": 792400, "traffic_bytes": 77107253749,
+    "l2_hit": 0.606, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.469, "clock_ghz": 1.653,
+    "insts_per_key_tile_wave": {"valu": 194.0, "mfma": 32.0, "salu": 117.9, "lds": 48.0,
                                 "branch": 25.3, "vmem": 16.3, "smem": 1.0},
 }
 
