@@ -112,8 +112,11 @@ enum { BSTA_SELECT_PREPOOLED = 0x100 };
  * the last one keeping the remainder; the count of a tile is the product of
  * its three extents; tiles are numbered j = (a*nY + b)*nX + c.
  *   num_tiles  [out, host, may be NULL]  Nt
- *   padded_len [out, host, may be NULL]  Lpad = 64*Nt
+ *   padded_len [out, host, may be NULL]  Lpad = 64*Nt (128*Nt for 4x4x8 tiles)
  *   occupancy  [out, host int32 [Nt], may be NULL]  valid tokens of tile j
+ * With 4x4x8 tiles the x axis is cut into ceil(X/8) tiles of 8; for a
+ * packed sequence the tiles are those of its layout (see bsta_segments),
+ * dense segments' tiles first.
  */
 int32_t attn_geometry(const bsta_geom* g, int32_t* num_tiles, int64_t* padded_len,
                       int32_t* occupancy);
