@@ -44,11 +44,11 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "63064fd9b4a2d06c",
-    "fetch_kib": 37253826, "write_kib": 792400, "traffic_bytes": 77107253749,
-    "l2_hit": 0.606, "lds_bank_conflict_per_active": 0.0,
-    "mfma_busy": 0.469, "clock_ghz": 1.653,
-    "insts_per_key_tile_wave": {"valu": 194.0, "mfma": 32.0, "salu": 117.9, "lds": 48.0,
+    "src_sha256_16": "e072ceccce2f5fc9",
+    "fetch_kib": 37409783, "write_kib": 792684, "traffic_bytes": 77426943184,
+    "l2_hit": 0.604, "lds_bank_conflict_per_active": 0.0,
+    "mfma_busy": 0.464, "clock_ghz": 1.674,
+    "insts_per_key_tile_wave": {"valu": 194.1, "mfma": 32.0, "salu": 117.9, "lds": 48.0,
                                 "branch": 25.3, "vmem": 16.3, "smem": 1.0},
 }
 

@@ -5,11 +5,13 @@
 // i of head h, attention runs over the valid tokens of the key tiles listed
 // in CSR row (b*H + h)*Nt + i, with an online (streaming) softmax.
 //
-// Work decomposition: a workgroup of two wave64s owns one query tile (64
-// rows); wave w owns query rows 32w..32w+31 for the whole key list.  Four
-// such workgroups share a CU, so each SIMD runs two waves whose softmax and
-// MFMA phases overlap (a wave raises its priority for the score/softmax
-// phase below, so that phase's VALU work issues first).  Per selected key
+// Work decomposition: a workgroup owns one query tile; wave w owns query
+// rows 32w..32w+31 for the whole key list.  A 64-token tile takes two
+// wave64s, and four such workgroups share a CU, so each SIMD runs two waves
+// whose softmax and MFMA phases overlap (a wave raises its priority for the
+// score/softmax phase below, so that phase's VALU work issues first).  A
+// 128-token tile takes four wave64s, two workgroups per CU, all four waves
+// reading the key tiles that waves 0 and 1 bring in.  Per selected key
 // tile:
 //   1. K and V arrive in LDS by direct global->LDS DMA (global_load_lds_
 //      dwordx4, 1 KB per instruction; each half-tile is issued whole by one
@@ -187,11 +189,12 @@ __device__ inline uint32_t sweep_load(const unsigned int* ctr) {
 }  // namespace
 
 // SUB = 64-slot units per tile: 1 for 64-token tiles, 2 for 128-token tiles.
-// With 128-token tiles a work item is one 64-row unit of a query tile (the
-// two units of a tile share its CSR row), and each CSR entry j stands for the
-// key units 2j and 2j+1, walked as consecutive key steps.
+// A work item is one query tile (one CSR row).  With 128-token tiles waves 0
+// and 1 hold query unit 0 of the tile and waves 2 and 3 unit 1, and each CSR
+// entry j stands for the key units 2j and 2j+1, walked as consecutive key
+// steps.
 template <int D, int SUB>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+__global__ __launch_bounds__(128 * SUB) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const int32_t* __restrict__ row_ptr,
         const int32_t* __restrict__ col_idx, int64_t col_len, float scale_log2,
@@ -218,6 +221,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t rs2 = rs * 2;           // bytes
     const bool all_full = g.full != 0;
     const int NU = g.Nt * SUB;  // 64-slot units per (batch, head)
+    // Waves 0 and 1 hold rows 0-31 and 32-63 of query unit 0 and issue the
+    // DMA; with 128-token tiles waves 2 and 3 hold those of unit 1 and only
+    // read the ring, so each key tile crosses into LDS once for 128 rows.
+    const bool issuer = SUB == 1 || wave < 2;
 
     // Per-lane DMA source offsets (bytes, relative to the half-tile's first
     // row) of blocks 0..3: block u covers slot bytes [1024u, 1024u+1024),
@@ -255,7 +262,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int c = db * 32 + vcol;
         vaddr[db] = ring0 + 2 * (vrow0 * D + v_phys<D>(vrow0, c >> 3) * 8 + (c & 7));
     }
-    const int qi = wave * 32 + l32;  // this lane's query row in the tile
+    const int qi = (SUB == 1 ? wave : (wave & 1)) * 32 + l32;  // query row in its unit
+    const int qsub = SUB == 1 ? 0 : wave >> 1;                  // unit within the tile
     const int half4 = 4 * half;
 
     // Persistent, XCD-aware schedule.  Workgroups are dealt round-robin over
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int slot = blockIdx.x >> 3;
     const int S = gridDim.x >> 3;
     const int64_t n_rows = (int64_t)g.B * g.H * g.Nt;  // CSR rows
-    const int64_t n_items = n_rows * SUB;
+    const int64_t n_items = n_rows;  // a work item is one query tile
     int64_t nnz = rp_s[n_rows];
     nnz = nnz < 0 ? 0 : (nnz > col_len ? col_len : nnz);
     // Rows of equal length (every top-k CSR): the even split, items_per_xcd
@@ -304,8 +312,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t r0 = xcd == 0 ? 0 : __builtin_amdgcn_readlane((int)lo, 0);
         int64_t r1 = xcd == 7 ? n_rows : __builtin_amdgcn_readlane((int)lo, 32);
         if (r1 < r0) r1 = r0;
-        first = r0 * SUB;
-        last = r1 * SUB;
+        first = r0;
+        last = r1;
     }
 
     // Key-order rotation for L2 reuse.  The rows' key tiles are scattered
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint64_t head_bytes = (uint64_t)NU * 64 * D * 2 * 2;
         bool wide = head_bytes > (8ull << 20);
         if (wide && first < last) {
-            const int64_t r = first / SUB;
+            const int64_t r = first;
             int64_t a = rp_s[r], e = rp_s[r + 1];
             a = a < 0 ? 0 : (a > col_len ? col_len : a);
             e = e < a ? a : (e > col_len ? col_len : e);
@@ -349,15 +357,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int* const handoff = (int*)&ring[(kRing - 1) * HALF_ELEMS];
 
     for (int64_t item = first + slot; item < last; item += S) {
-        const int bh = (int)(item / NU);
-        const int i = (int)(item - (int64_t)bh * NU);  // query unit
+        const int bh = (int)(item / g.Nt);
+        const int i = (int)(item - (int64_t)bh * g.Nt);  // query tile
+        const int iu = i * SUB + qsub;                   // this wave's query unit
         const int b = bh / g.H, h = bh - b * g.H;
         const int64_t head_off = (int64_t)h * D;
         const int64_t batch_row0 = (int64_t)b * g.Lpad;
         const uint64_t kbase = (uint64_t)(uintptr_t)(k + batch_row0 * rs + head_off);
         const uint64_t vbase = (uint64_t)(uintptr_t)(v + batch_row0 * rs + head_off);
 
-        const int64_t row = (int64_t)bh * g.Nt + i / SUB;
+        const int64_t row = (int64_t)bh * g.Nt + i;
         int64_t p0 = rp_s[row], p1 = rp_s[row + 1];
         p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
         p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // Query fragment (B operand of S^T = K Q^T): query row qi,
         // d = 16*dc + 8*half.
         bf16x8 qf[NDC];
-        const __bf16* qrow = q + (batch_row0 + (int64_t)i * 64 + qi) * rs + head_off;
+        const __bf16* qrow = q + (batch_row0 + (int64_t)iu * 64 + qi) * rs + head_off;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) qf[dc] = *(const bf16x8*)(qrow + dc * 16 + half * 8);
         // The compiler cannot see the DMA issued below: make it finish the
@@ -471,11 +480,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         int read_pos = 0, read_slot = 0;
 #define BSTA_ACQUIRE(sl_out)                                                               \
     do {                                                                                   \
-        wait_dma<NP>((my_next - (read_pos + wave) - 2) >> 1);                              \
+        if (issuer) wait_dma<NP>((my_next - (read_pos + wave) - 2) >> 1);                  \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
         __builtin_amdgcn_s_barrier();                                                      \
         const int lim_ = read_pos + kRing < NSEQ ? read_pos + kRing : NSEQ;                \
-        while (my_next < lim_) BSTA_ISSUE_NEXT();                                          \
+        if (issuer)                                                                        \
+            while (my_next < lim_) BSTA_ISSUE_NEXT();                                      \
         (sl_out) = read_slot;                                                              \
         read_pos += 2;                                                                     \
         read_slot = read_slot >= kRing - 2 ? read_slot + 2 - kRing : read_slot + 2;        \
@@ -493,17 +503,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #define BSTA_ACQUIRE_STEADY(sl_out, do_k)                                                  \
     do {                                                                                   \
         if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP) : "memory");          \
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                              \
+        else if (SUB == 1 || wave == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
         __builtin_amdgcn_s_barrier();                                                      \
         const uint32_t slot_ = ring0 + (uint32_t)my_slot * SLOT_BYTES;                     \
-        if (do_k) {                                                                        \
-            off_km1 = off_k;                                                               \
-            off_k = (unsigned)jraw2 < (unsigned)g.Nt                                       \
-                        ? (uint64_t)(jraw2 * SUB + (r2 % SUB)) * tile_stride : 0;            \
-            dma_half<D>(kbase + off_k + hi_off, rows16, koff, slot_);                      \
-        } else {                                                                           \
-            dma_half<D>(vbase + off_km1 + hi_off, rows16, voff, slot_);                    \
+        if (issuer) {                                                                      \
+            if (do_k) {                                                                    \
+                off_km1 = off_k;                                                           \
+                off_k = (unsigned)jraw2 < (unsigned)g.Nt                                   \
+                            ? (uint64_t)(jraw2 * SUB + (r2 % SUB)) * tile_stride : 0;        \
+                dma_half<D>(kbase + off_k + hi_off, rows16, koff, slot_);                  \
+            } else {                                                                       \
+                dma_half<D>(vbase + off_km1 + hi_off, rows16, voff, slot_);                \
+            }                                                                              \
         }                                                                                  \
         my_next += 2;                                                                      \
         my_slot = my_slot >= kRing - 2 ? my_slot + 2 - kRing : my_slot + 2;                \
@@ -513,7 +525,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } while (0)
         // Prologue: positions 0..2.  Every slot of the previous item was
         // retired behind a barrier.
-        while (my_next < 3 && my_next < NSEQ) BSTA_ISSUE_NEXT();
+        if (issuer)
+            while (my_next < 3 && my_next < NSEQ) BSTA_ISSUE_NEXT();
 
         f32x16 oacc[NDB];
 #pragma unroll
@@ -722,17 +735,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // Finalise: l is split over lanes l and l^32.  With a keep mask (query
         // pruning) a row outside it is written like a pad row.
-        const int ni = unit_occupancy(g, i);
+        const int ni = unit_occupancy(g, iu);
         const float l_tot = l_run + wave_xor32(l_run);
-        const bool kept = keep == nullptr || ((keep[item] >> qi) & 1) != 0;
+        const bool kept = keep == nullptr || ((keep[(int64_t)bh * NU + iu] >> qi) & 1) != 0;
         const bool valid = qi < ni && l_tot > 0.f && kept;
         const float inv = valid ? 1.0f / l_tot : 0.f;
         // Output row: slot i*64 + qi of the tiled tensor, or with `raster`
         // the token that slot holds in [B, L, H, D] (a pad slot has none).
-        int64_t orow_idx = batch_row0 + (int64_t)i * 64 + qi;
+        int64_t orow_idx = batch_row0 + (int64_t)iu * 64 + qi;
         bool has_row = true;
         if (raster) {
-            const int64_t tok = slot_to_token(g, (int64_t)i * 64 + qi);
+            const int64_t tok = slot_to_token(g, (int64_t)iu * 64 + qi);
             has_row = tok >= 0;
             orow_idx = (int64_t)b * g.L + (tok < 0 ? 0 : tok);
         }
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         if (lse != nullptr && half == 0) {
             const float val = valid ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-            lse[(int64_t)bh * g.Lpad + (int64_t)i * 64 + qi] = val;
+            lse[(int64_t)bh * g.Lpad + (int64_t)iu * 64 + qi] = val;
         }
     }
 }
@@ -761,7 +774,7 @@ namespace {
 // Workgroups of the attention kernel resident per XCD on the current device
 // (computed once per device and kernel variant).  Host threads may race here:
 // each entry is an atomic, and racing threads store the same value.
-int resident_per_xcd(const void* kernel, int which) {
+int resident_per_xcd(const void* kernel, int which, int block) {
     static std::atomic<int> cache[4][64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 16;
@@ -769,10 +782,10 @@ int resident_per_xcd(const void* kernel, int which) {
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 128, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         cus = 256;
-        per_cu = 4;
+        per_cu = 512 / block;
     }
     const int r = (cus / 8) * per_cu > 0 ? (cus / 8) * per_cu : 1;
     cache[which][dev].store(r, std::memory_order_relaxed);
@@ -785,12 +798,12 @@ hipError_t launch_variant(const Geo& g, const void* q, const void* k, const void
                           float scale_log2, void* o, float* lse, const uint64_t* keep, int rotate,
                           bool raster, hipStream_t stream) {
     const void* kernel = (const void*)attn_fwd_kernel<D, SUB>;
-    const int64_t n_items = (int64_t)g.B * g.H * g.Nt * SUB;
+    const int64_t n_items = (int64_t)g.B * g.H * g.Nt;  // one query tile per item
     const int64_t items_per_xcd = (n_items + 7) / 8;
-    int64_t per_xcd = resident_per_xcd(kernel, (D == 128 ? 0 : 1) + (SUB == 2 ? 2 : 0));
+    int64_t per_xcd = resident_per_xcd(kernel, (D == 128 ? 0 : 1) + (SUB == 2 ? 2 : 0), 128 * SUB);
     if (per_xcd > items_per_xcd) per_xcd = items_per_xcd;
     const unsigned blocks = (unsigned)(8 * per_xcd);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, SUB>), dim3(blocks), dim3(128), 0, stream, g,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, SUB>), dim3(blocks), dim3(128 * SUB), 0, stream, g,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
                        col_len, scale_log2, (__bf16*)o, lse, keep, items_per_xcd, rotate,
                        raster ? 1 : 0);
