@@ -20,11 +20,12 @@
 //             dQ^T += K^T dS^T with K^T read by LDS transpose reads; each
 //             wave takes 32 queries and one 32-key half of every key tile,
 //             and K and V arrive by direct-to-LDS DMA.
-//   dkdv      one workgroup of two waves per key tile, walking its CSC
+//   dkdv      one workgroup of four waves per key tile, walking its CSC
 //             column: S = Q K^T and dP = dO V^T (queries as M, keys as N, so
 //             each lane holds one key), then dV^T += dO^T P and
-//             dK^T += Q^T dS.
-// The products use v_mfma_f32_32x32x16_bf16 with the lane layouts of the
+//             dK^T += Q^T dS; each wave takes 16 keys of the tile, on the
+//             16x16x32 matrix instruction (its layouts are given with it).
+// The dQ products use v_mfma_f32_32x32x16_bf16 with the lane layouts of the
 // forward kernel (checked on hardware there): A[m][k] in lane m + 32*(k/8),
 // element k%8; B[k][n] in lane n + 32*(k/8), element k%8; accumulator
 // register r of lane l holds D[8*(r/4) + 4*(l/32) + r%4][l%32].  A score
@@ -114,28 +115,14 @@ __device__ inline bf16x8 lds_row8(uint32_t base, int lstr, int row, int col) {
     return *(const lds_bf16x8b*)(uintptr_t)(base + (uint32_t)(row * lstr + 2 * col));
 }
 
-// A operand (transposed) of a product over 16 rows of an LDS tile: rows
-// 16*step + 4*half + [0,4) and +8, columns 32*db + 16*dsub + 4*(s16%4) for
-// source lane s16 (see the header for the transpose read).
-__device__ inline bf16x8 lds_tr8(uint32_t base, int lstr, int step, int db, int lane) {
-    const int s16 = lane & 15, dsub = (lane >> 4) & 1, half = lane >> 5;
-    const int row = 16 * step + 4 * half + (s16 >> 2);
-    const int col = 32 * db + 16 * dsub + 4 * (s16 & 3);
-    const uint32_t a0 = base + (uint32_t)(row * lstr + 2 * col);
-    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a0);
-    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)(a0 + 8 * lstr));
-    const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
 // Copy of the 64 slot rows of a tile (D bf16 each, global row stride `rs`
-// elements) into LDS rows of `lstr` bytes, in two halves so that the loads
-// of the next tile can be in flight while the current one is used:
-// load_tile fills this thread's NCH chunks (16 bytes each) into registers,
-// store_tile writes them to LDS.
+// elements) into LDS rows of `lstr` bytes by the 256 threads of a
+// workgroup, in two halves so that the loads of the next tile can be in
+// flight while the current one is used: load_tile fills this thread's NCH
+// chunks (16 bytes each) into registers, store_tile writes them to LDS.
 template <int D>
 struct TileRegs {
-    static constexpr int NCH = 64 * (D / 8) / 128;  // chunks per thread (128 threads)
+    static constexpr int NCH = 64 * (D / 8) / 256;  // chunks per thread
     u32x4 c[NCH];
 };
 
@@ -144,7 +131,7 @@ __device__ inline void load_tile(TileRegs<D>& r, const __bf16* src, int64_t rs) 
     constexpr int CH = D / 8;
 #pragma unroll
     for (int n = 0; n < TileRegs<D>::NCH; ++n) {
-        const int c = threadIdx.x + 128 * n;
+        const int c = threadIdx.x + 256 * n;
         const int row = c / CH, k = c - row * CH;
         r.c[n] = *(const u32x4*)(src + (int64_t)row * rs + k * 8);
     }
@@ -155,10 +142,30 @@ __device__ inline void store_tile(const TileRegs<D>& r, char* lds, int lstr) {
     constexpr int CH = D / 8;
 #pragma unroll
     for (int n = 0; n < TileRegs<D>::NCH; ++n) {
-        const int c = threadIdx.x + 128 * n;
+        const int c = threadIdx.x + 256 * n;
         const int row = c / CH, k = c - row * CH;
         *(u32x4*)(lds + row * lstr + k * 16) = r.c[n];
     }
+}
+
+// A operand of a 16x16x32 product whose 32 k-rows are the rows q0 + 4G +
+// [0, 4) and q1 + 4G + [0, 4) of an LDS tile with `lstr`-byte rows, for lane
+// group G = lane/16, and whose 16 m-columns are its columns c0 + [0, 16):
+// per 16-lane group, source lane s points at row q + s/4, columns c0 +
+// 4*(s%4), and lane d receives rows q + [0, 4) of column c0 + d.
+__device__ inline bf16x8 lds_tr16(uint32_t base, int lstr, int q0, int q1, int c0, int lane) {
+    const int s = lane & 15, G = lane >> 4;
+    const uint32_t col = (uint32_t)(2 * (c0 + 4 * (s & 3)));
+    const uint32_t a0 = base + (uint32_t)((q0 + 4 * G + (s >> 2)) * lstr) + col;
+    const uint32_t a1 = base + (uint32_t)((q1 + 4 * G + (s >> 2)) * lstr) + col;
+    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a0);
+    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a1);
+    const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace
@@ -464,42 +471,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ dk, dv
+// One workgroup of four waves per key tile, on v_mfma_f32_16x16x32_bf16
+// (lane layouts checked on hardware: A[m][k] in lane m%16 + 16*(k/8),
+// element k%8; B[k][n] in lane n + 16*(k/8), element k%8; register r of
+// lane l holds D[4*(l/16) + r][l%16]).  Wave w owns keys 16w + [0, 16) of
+// the tile, one per lane l%16, and walks the tile's CSC column: per query
+// tile, S = Q K^T and dP = dO V^T in four 16-query blocks (queries as M,
+// keys as N; the key fragments stay in registers), then dV^T += dO^T P and
+// dK^T += Q^T dS in two 32-query steps (d as M).  A 32-query step takes the
+// two 16-query blocks' registers as its B operand, so its queries run in
+// the order 4*(l/16) + [0, 4), then 16 + 4*(l/16) + [0, 4); the dO^T and Q^T
+// operands come in the same order from two transpose reads (per 16-lane
+// group, source lane s points at row q0 + s/4, columns c0 + 4*(s%4), and
+// lane d receives rows q0 + [0, 4) of column c0 + d).  Sixteen keys per wave
+// keep the accumulators, fragments and staged tiles within the registers
+// of two waves per SIMD.
 template <int D>
-__global__ __launch_bounds__(128) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
         const float* __restrict__ lse, const float* __restrict__ delta,
         const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_cnt,
         const int32_t* __restrict__ row_idx, int64_t col_len, float scale,
         __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
-    constexpr int NDC = D / 16, NDB = D / 32, LSTR = 2 * D + 16;
+    constexpr int NS = D / 32, NDB = D / 16, LSTR = 2 * D + 16;
     __shared__ __attribute__((aligned(16))) char qt[64 * LSTR];
     __shared__ __attribute__((aligned(16))) char dt[64 * LSTR];
     __shared__ __attribute__((aligned(16))) float lse_s[64];
     __shared__ __attribute__((aligned(16))) float del_s[64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int half = lane >> 5, l32 = lane & 31;
+    const int G = lane >> 4, l16 = lane & 15;
     const int64_t item = blockIdx.x;
     const int j = (int)(item % g.Nt);
     const int64_t bh = item / g.Nt;
     const int h = (int)(bh % g.H);
     const int64_t b = bh / g.H;
     const int64_t rs = (int64_t)g.H * D;
-    const int kj = wave * 32 + l32;
+    const int kj = wave * 16 + l16;
     const bool kvalid = kj < tile_occupancy(g, j);
     const int64_t koff = ((b * g.Lpad + (int64_t)j * 64 + kj) * g.H + h) * D;
-    bf16x8 kf[NDC], vf[NDC];
+    // Key fragments (B operand of S and dP): key kj, d = 32s + 8G + [0, 8).
+    bf16x8 kf[NS], vf[NS];
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-        kf[dc] = *(const bf16x8*)(k + koff + dc * 16 + half * 8);
-        vf[dc] = *(const bf16x8*)(v + koff + dc * 16 + half * 8);
+    for (int s = 0; s < NS; ++s) {
+        kf[s] = *(const bf16x8*)(k + koff + 32 * s + 8 * G);
+        vf[s] = *(const bf16x8*)(v + koff + 32 * s + 8 * G);
     }
     const float scale_log2 = scale * kLog2e;
-    f32x16 adv[NDB], adk[NDB];
+    f32x4 adv[NDB], adk[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-        adv[db] = (f32x16){};
-        adk[db] = (f32x16){};
+        adv[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        adk[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     int64_t c0 = col_start[bh * g.Nt + j];
     int64_t c1 = c0 + col_cnt[bh * g.Nt + j];
@@ -539,90 +562,71 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(
         __syncthreads();
         e = next_valid(e + 1);
         if (e < c1) prefetch(row_idx[e]);
-        // Operand reads in batches of kBatch k-steps ahead of their products
-        // (the scheduling barriers keep each read from being serialised
-        // with its product).
-        constexpr int kBatch = NDC < 8 ? NDC : 8;
-        f32x16 s[2], dp[2];
+        // S and dP in four 16-query blocks (A = row l16 of the block, d =
+        // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
+        // r of block mb holds query 16mb + 4G + r.
+        bf16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            s[mb] = (f32x16){};
-            dp[mb] = (f32x16){};
+        for (int mb = 0; mb < 4; ++mb) {
+            bf16x8 qa[NS], da[NS];
 #pragma unroll
-            for (int d0 = 0; d0 < NDC; d0 += kBatch) {
-                bf16x8 qa[kBatch], da[kBatch];
+            for (int s = 0; s < NS; ++s) {
+                qa[s] = lds_row8(qb0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
+                da[s] = lds_row8(db0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int col = 16 * (d0 + u) + 8 * half;
-                    qa[u] = lds_row8(qb0, LSTR, l32 + 32 * mb, col);
-                    da[u] = lds_row8(db0, LSTR, l32 + 32 * mb, col);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int s = 0; s < NS; ++s) {
+                s4 = mma16(qa[s], kf[s], s4);
+                p4 = mma16(da[s], vf[s], p4);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int q0 = 16 * mb + 4 * G;
+            const f32x4 l4 = *(const f32x4*)&lse_s[q0];
+            const f32x4 d4 = *(const f32x4*)&del_s[q0];
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    s[mb] = mma(qa[u], kf[d0 + u], s[mb]);
-                    dp[mb] = mma(da[u], vf[d0 + u], dp[mb]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 4; ++r) {
+                const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]) : 0.f;
+                pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
             }
         }
-        // P and dS in bf16 chunks of 16 queries (chunk c: query block c/2,
-        // registers 8*(c%2) + [0, 8); register rr holds query
-        // 32*(c/2) + 8*(rr/4) + 4*half + rr%4).
-        bf16x8 pf[4], dsf[4];
-        auto p_chunk = [&](int c) {
-            const int mb = c >> 1, r0 = (c & 1) * 8;
+        // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps.
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int q0 = 32 * mb + 8 * ((r0 >> 2) + rb) + 4 * half;
-                const f32x4 l4 = *(const f32x4*)&lse_s[q0];
-                const f32x4 d4 = *(const f32x4*)&del_s[q0];
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = r0 + 4 * rb + e;
-                    const float pr = q0 + e < ni
-                                             ? __builtin_amdgcn_exp2f(s[mb][rr] * scale_log2 - l4[e])
-                                             : 0.f;
-                    pf[c][4 * rb + e] = (__bf16)pr;
-                    dsf[c][4 * rb + e] = (__bf16)(pr * (dp[mb][rr] - d4[e]));
-                }
+            for (int db0i = 0; db0i < NDB; db0i += 4) {
+                bf16x8 ta[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    ta[u] = lds_tr16(db0, LSTR, 32 * ks, 32 * ks + 16, 16 * (db0i + u), lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    ta[u] = lds_tr16(qb0, LSTR, 32 * ks, 32 * ks + 16, 16 * (db0i + u), lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        // dV^T += dO^T P and dK^T += Q^T dS; the P and dS chunk of step c+1
-        // is computed while the MFMAs of step c run.
-        p_chunk(0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            bf16x8 ta[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) ta[db] = lds_tr8(db0, LSTR, c, db, lane);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) adv[db] = mma(ta[db], pf[c], adv[db]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) ta[db] = lds_tr8(qb0, LSTR, c, db, lane);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) adk[db] = mma(ta[db], dsf[c], adk[db]);
-            if (c + 1 < 4) p_chunk(c + 1);
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // Lane holds dV^T, dK^T[d = 32*db + 8*(r/4) + 4*half + r%4][key kj].
+    // Lane holds dV^T, dK^T[d = 16*db + 4*G + r][key kj].
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
+        bf16x4 wv, wk;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            bf16x4 wv, wk;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wv[e] = (__bf16)(kvalid ? adv[db][4 * rb + e] : 0.f);
-                wk[e] = (__bf16)(kvalid ? adk[db][4 * rb + e] * scale : 0.f);
-            }
-            *(bf16x4*)(dv + koff + 32 * db + 8 * rb + 4 * half) = wv;
-            *(bf16x4*)(dk + koff + 32 * db + 8 * rb + 4 * half) = wk;
+        for (int r = 0; r < 4; ++r) {
+            wv[r] = (__bf16)(kvalid ? adv[db][r] : 0.f);
+            wk[r] = (__bf16)(kvalid ? adk[db][r] * scale : 0.f);
         }
+        *(bf16x4*)(dv + koff + 16 * db + 4 * G) = wv;
+        *(bf16x4*)(dk + koff + 16 * db + 4 * G) = wk;
+    }
 }
 
 // ------------------------------------------------------------------ launcher
@@ -679,14 +683,14 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
     if (g.D == 128) {
         hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO,
+        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
                            lse, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
     } else {
         hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(items), dim3(128), 0, stream, g, Q, K, V, DO,
+        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
                            lse, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
