@@ -67,51 +67,52 @@ __device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // LDS ring layout of the dQ kernel: half-tiles of 32 rows of D bf16 (2*D
 // bytes, unpadded); the 16-byte chunk c of row r sits at chunk position
-// c ^ swz(r).  The K tile is read both ways, by rows (ds_read_b128: row l32,
+// c ^ ring_swz(r).  The K tile is read both ways, by rows (ds_read_b128: row l32,
 // one chunk per lane half) and transposed (ds_read_b64_tr_b16: 4 rows x 32
-// bytes per 16-lane group), and swz is chosen so that neither read has a
-// bank conflict (64 banks of 4 bytes): it permutes the chunk positions of
+// bytes per 16-lane group), and ring_swz is chosen so that neither read has a
+// bank conflict (64 banks of 4 bytes): ring_swz permutes the chunk positions of
 // any 16 consecutive rows (row reads), and it sends 4 consecutive rows from
 // a multiple of 4 to distinct 64-byte quarters of the bank range (D = 128)
 // or, for D = 64 (two rows per bank range), rows of equal parity to
-// distinct 64-byte halves of their 128 bytes (transpose reads).  swz
+// distinct 64-byte halves of their 128 bytes (transpose reads).  It
 // depends on the row modulo 16 only, as the DMA's offsets require.
 template <int D>
-__device__ inline int swz(int r) {
+__device__ inline int ring_swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
 }
 
 // LDS byte offset of element `col` (a multiple of 4) of row `row`.
 template <int D>
-__device__ inline uint32_t tile_off(int row, int col) {
-    return (uint32_t)(row * 2 * D + ((col >> 3) ^ swz<D>(row)) * 16 + (col & 7) * 2);
+__device__ inline uint32_t ring_off(int row, int col) {
+    return (uint32_t)(row * 2 * D + ((col >> 3) ^ ring_swz<D>(row)) * 16 + (col & 7) * 2);
 }
 
 // 8 bf16 of row `row`, from element `col` (a multiple of 8), swizzled layout.
 template <int D>
-__device__ inline bf16x8 lds_row8(uint32_t base, int row, int col) {
-    return *(const lds_bf16x8b*)(uintptr_t)(base + tile_off<D>(row, col));
+__device__ inline bf16x8 ring_row8(uint32_t base, int row, int col) {
+    return *(const lds_bf16x8b*)(uintptr_t)(base + ring_off<D>(row, col));
 }
 
 // A operand (transposed) of a product over 16 rows of a swizzled half-tile:
 // rows 16*step + 4*half + [0,4) and +8, columns 32*db + 16*dsub +
 // 4*(s16%4) for source lane s16 (see the header for the transpose read).
 template <int D>
-__device__ inline bf16x8 lds_tr8(uint32_t base, int step, int db, int lane) {
+__device__ inline bf16x8 ring_tr8(uint32_t base, int step, int db, int lane) {
     const int s16 = lane & 15, dsub = (lane >> 4) & 1, half = lane >> 5;
     const int row = 16 * step + 4 * half + (s16 >> 2);
     const int col = 32 * db + 16 * dsub + 4 * (s16 & 3);
     const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4b*)(uintptr_t)(base + tile_off<D>(row, col)));
+            (lds_i16x4b*)(uintptr_t)(base + ring_off<D>(row, col)));
     const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4b*)(uintptr_t)(base + tile_off<D>(row + 8, col)));
+            (lds_i16x4b*)(uintptr_t)(base + ring_off<D>(row + 8, col)));
     const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, w);
 }
 
-// 8 bf16 of LDS row `row`, starting at element `col` (16-byte aligned).
-__device__ inline bf16x8 lds_row8(uint32_t base, int lstr, int row, int col) {
+// 8 bf16 of row `row` of a padded LDS tile (`lstr`-byte rows), from element
+// `col` (16-byte aligned).
+__device__ inline bf16x8 pad_row8(uint32_t base, int lstr, int row, int col) {
     return *(const lds_bf16x8b*)(uintptr_t)(base + (uint32_t)(row * lstr + 2 * col));
 }
 
@@ -358,14 +359,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Per-lane DMA source offsets of blocks 0..3 of a half-tile: block u
     // fills slot bytes [1024u, 1024u + 1024), row r = (1024u + 16*lane) /
     // (2D), chunk position c; the lane fetches the chunk the swizzle puts
-    // there, c ^ swz(r).  K and V share the layout.
+    // there, c ^ ring_swz(r).  K and V share the layout.
     int32_t off[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int byte = u * 1024 + lane * 16;
         const int r = byte / (2 * D);
         const int c = (byte % (2 * D)) / 16;
-        off[u] = 2 * ((int32_t)(r * rs) + (c ^ swz<D>(r)) * 8) - (1024 * u - kDmaBias<D>);
+        off[u] = 2 * ((int32_t)(r * rs) + (c ^ ring_swz<D>(r)) * 8) - (1024 * u - kDmaBias<D>);
     }
     const int64_t rs2 = rs * 2;  // bytes per slot row
     const uint64_t rows16 = (uint64_t)(16 * rs2);
@@ -413,8 +414,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
             const int col = 16 * dc + 8 * half;
-            ka[dc] = lds_row8<D>(kbuf, l32, col);
-            va[dc] = lds_row8<D>(vbuf, l32, col);
+            ka[dc] = ring_row8<D>(kbuf, l32, col);
+            va[dc] = ring_row8<D>(vbuf, l32, col);
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int c = 0; c < 2; ++c) {
             bf16x8 kt2[NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) kt2[db] = lds_tr8<D>(kbuf, c, db, lane);
+            for (int db = 0; db < NDB; ++db) kt2[db] = ring_tr8<D>(kbuf, c, db, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[db], dsf[c], acc[db]);
@@ -585,8 +586,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             bf16x8 qa[NS], da[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                qa[s] = lds_row8(qb0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
-                da[s] = lds_row8(db0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
+                qa[s] = pad_row8(qb0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
+                da[s] = pad_row8(db0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
