@@ -35,9 +35,9 @@
 // 16-lane group, lane d receives element d%4 of the value addressed by lane
 // d/4 + 4m, m = 0..3).
 //
-// The dK/dV kernel stages its tiles in LDS (rows padded by 16 bytes) from
-// registers loaded one tile ahead, so the next tile's loads overlap the
-// products (the dQ kernel's DMA ring is described with it); P and
+// Both walk kernels bring their tiles into LDS by direct-to-LDS DMA into a
+// ring of half-tile slots, ahead of the products (each ring is described
+// with its kernel); P and
 // dS are rounded to bf16 for the second product, accumulators are fp32 and
 // each gradient is rounded once to bf16 at the end.  Pad query rows and pad
 // key rows contribute nothing and are written as +0.0.
@@ -106,61 +106,6 @@ __device__ inline bf16x8 ring_tr8(uint32_t base, int step, int db, int lane) {
             (lds_i16x4b*)(uintptr_t)(base + ring_off<D>(row, col)));
     const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4b*)(uintptr_t)(base + ring_off<D>(row + 8, col)));
-    const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-// 8 bf16 of row `row` of a padded LDS tile (`lstr`-byte rows), from element
-// `col` (16-byte aligned).
-__device__ inline bf16x8 pad_row8(uint32_t base, int lstr, int row, int col) {
-    return *(const lds_bf16x8b*)(uintptr_t)(base + (uint32_t)(row * lstr + 2 * col));
-}
-
-// Copy of the 64 slot rows of a tile (D bf16 each, global row stride `rs`
-// elements) into LDS rows of `lstr` bytes by the 256 threads of a
-// workgroup, in two halves so that the loads of the next tile can be in
-// flight while the current one is used: load_tile fills this thread's NCH
-// chunks (16 bytes each) into registers, store_tile writes them to LDS.
-template <int D>
-struct TileRegs {
-    static constexpr int NCH = 64 * (D / 8) / 256;  // chunks per thread
-    u32x4 c[NCH];
-};
-
-template <int D>
-__device__ inline void load_tile(TileRegs<D>& r, const __bf16* src, int64_t rs) {
-    constexpr int CH = D / 8;
-#pragma unroll
-    for (int n = 0; n < TileRegs<D>::NCH; ++n) {
-        const int c = threadIdx.x + 256 * n;
-        const int row = c / CH, k = c - row * CH;
-        r.c[n] = *(const u32x4*)(src + (int64_t)row * rs + k * 8);
-    }
-}
-
-template <int D>
-__device__ inline void store_tile(const TileRegs<D>& r, char* lds, int lstr) {
-    constexpr int CH = D / 8;
-#pragma unroll
-    for (int n = 0; n < TileRegs<D>::NCH; ++n) {
-        const int c = threadIdx.x + 256 * n;
-        const int row = c / CH, k = c - row * CH;
-        *(u32x4*)(lds + row * lstr + k * 16) = r.c[n];
-    }
-}
-
-// A operand of a 16x16x32 product whose 32 k-rows are the rows q0 + 4G +
-// [0, 4) and q1 + 4G + [0, 4) of an LDS tile with `lstr`-byte rows, for lane
-// group G = lane/16, and whose 16 m-columns are its columns c0 + [0, 16):
-// per 16-lane group, source lane s points at row q + s/4, columns c0 +
-// 4*(s%4), and lane d receives rows q + [0, 4) of column c0 + d.
-__device__ inline bf16x8 lds_tr16(uint32_t base, int lstr, int q0, int q1, int c0, int lane) {
-    const int s = lane & 15, G = lane >> 4;
-    const uint32_t col = (uint32_t)(2 * (c0 + 4 * (s & 3)));
-    const uint32_t a0 = base + (uint32_t)((q0 + 4 * G + (s >> 2)) * lstr) + col;
-    const uint32_t a1 = base + (uint32_t)((q1 + 4 * G + (s >> 2)) * lstr) + col;
-    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a0);
-    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a1);
     const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, w);
 }
@@ -495,8 +440,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // operands come in the same order from two transpose reads (per 16-lane
 // group, source lane s points at row q0 + s/4, columns c0 + 4*(s%4), and
 // lane d receives rows q0 + [0, 4) of column c0 + d).  Sixteen keys per wave
-// keep the accumulators, fragments and staged tiles within the registers
-// of two waves per SIMD.
+// keep the accumulators and fragments well within the registers of two
+// waves per SIMD.
+//
+// Q and dO reach LDS by direct-to-LDS DMA into a ring of kKvSlots half-tile
+// slots, as in the dQ kernel: walk entry t is positions 4t + r, r = 0..3 (Q
+// rows 0-31, Q rows 32-63, dO rows 0-31, dO rows 32-63), position s in slot
+// s % kKvSlots, issued by wave s % 4; waves 0 and 1 also bring the query
+// tile's lse and delta (64 floats each) into the 256-byte side slot of
+// their position's slot.  Nine slots are the fewest with which every
+// position of an entry is issued before its acquire; with the side slots
+// they keep a workgroup under 80 KB, two per CU.  Every wave reads the whole
+// Q and dO tiles.  The 16-byte chunk c of row r sits at position
+// c ^ kv_swz(r), a map that the 64-bank model rates free of conflicts for
+// both of the kernel's 16x16 read shapes (16 rows x 4 chunks, and per
+// 16-lane group 4 rows x 32 bytes), and that depends on the row modulo 16
+// only, as the DMA's offsets require.
+template <int D>
+__device__ inline int kv_swz(int r) {
+    if constexpr (D == 128) return (2 * (r & 7)) | ((r >> 3) & 1);
+    else return (r & 6) | ((r >> 3) & 1);
+}
+
+template <int D>
+__device__ inline uint32_t kv_off(int row, int col) {
+    return (uint32_t)(row * 2 * D + (((col >> 3) ^ kv_swz<D>(row)) * 16) + (col & 7) * 2);
+}
+
+template <int D>
+__device__ inline bf16x8 kv_tr16(uint32_t base, int q0, int q1, int c0, int lane) {
+    const int s = lane & 15, G = lane >> 4;
+    const int col = c0 + 4 * (s & 3);
+    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4b*)(uintptr_t)(base + kv_off<D>(q0 + 4 * G + (s >> 2), col)));
+    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4b*)(uintptr_t)(base + kv_off<D>(q1 + 4 * G + (s >> 2), col)));
+    const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+constexpr int kKvSlots = 9;
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -505,11 +489,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_cnt,
         const int32_t* __restrict__ row_idx, int64_t col_len, float scale,
         __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
-    constexpr int NS = D / 32, NDB = D / 16, LSTR = 2 * D + 16;
-    __shared__ __attribute__((aligned(16))) char qt[64 * LSTR];
-    __shared__ __attribute__((aligned(16))) char dt[64 * LSTR];
-    __shared__ __attribute__((aligned(16))) float lse_s[64];
-    __shared__ __attribute__((aligned(16))) float del_s[64];
+    constexpr int NS = D / 32, NDB = D / 16;
+    constexpr int HALF = 32 * D * 2;  // bytes of one half-tile slot
+    constexpr int NP = HALF / 1024;   // DMA instructions per half-tile
+    __shared__ __attribute__((aligned(1024))) char ring[kKvSlots * HALF];
+    __shared__ __attribute__((aligned(16))) float side[kKvSlots * 64];
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const cptr ri_s = (cptr)row_idx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int G = lane >> 4, l16 = lane & 15;
     // Key tiles are dealt to the XCDs in runs of 16 neighbours: the columns
@@ -525,13 +511,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int kj = wave * 16 + l16;
     const bool kvalid = kj < tile_occupancy(g, j);
     const int64_t koff = ((b * g.Lpad + (int64_t)j * 64 + kj) * g.H + h) * D;
-    // Key fragments (B operand of S and dP): key kj, d = 32s + 8G + [0, 8).
     bf16x8 kf[NS], vf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         kf[s] = *(const bf16x8*)(k + koff + 32 * s + 8 * G);
         vf[s] = *(const bf16x8*)(v + koff + 32 * s + 8 * G);
     }
+    // The compiler cannot see the DMA below: make these loads finish first,
+    // so that the waits on the DMA count only DMA.
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
     const float scale_log2 = scale * kLog2e;
     f32x4 adv[NDB], adk[NDB];
 #pragma unroll
@@ -543,51 +532,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int64_t c1 = c0 + col_cnt[bh * g.Nt + j];
     c0 = c0 < 0 ? 0 : (c0 > col_len ? col_len : c0);
     c1 = c1 < c0 ? c0 : (c1 > col_len ? col_len : c1);
-    const uint32_t qb0 = lds_base(qt), db0 = lds_base(dt);
-    auto next_valid = [&](int64_t e) {
-        while (e < c1 && (unsigned)row_idx[e] >= (unsigned)g.Nt) ++e;
-        return e;
+    const int m = (int)(c1 - c0);
+
+    // Per-lane DMA source offsets of blocks 0..3 of a half-tile (as in the
+    // dQ kernel, with this ring's swizzle).
+    int32_t off[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int byte = u * 1024 + lane * 16;
+        const int r = byte / (2 * D);
+        const int c = (byte % (2 * D)) / 16;
+        off[u] = 2 * ((int32_t)(r * rs) + (c ^ kv_swz<D>(r)) * 8) - (1024 * u - kDmaBias<D>);
+    }
+    const int64_t rs2 = rs * 2;
+    const uint64_t rows16 = (uint64_t)(16 * rs2);
+    // Position r of an entry: Q rows 0-31 (with the tile's lse), Q rows
+    // 32-63 (with its delta), dO rows 0-31, dO rows 32-63; issued by wave r.
+    const uint64_t src0 = (uint64_t)(uintptr_t)((wave < 2 ? q : dO) + (b * g.Lpad * g.H + h) * D) +
+                          (uint64_t)((wave & 1) * 32 * rs2);
+    const uint64_t fsrc = (uint64_t)(uintptr_t)((wave == 0 ? lse : delta) + bh * g.Lpad);
+    const uint32_t ring0 = lds_base(ring), side0 = lds_base(side);
+    // Query tile of walk entry t, or -1 for an id outside [0, Nt) (its slots
+    // are filled from tile 0 and its products skipped).
+    auto query_of = [&](int t) -> int {
+        const int i = ri_s[c0 + t];
+        return (unsigned)i < (unsigned)g.Nt ? i : -1;
     };
-    TileRegs<D> rq, rd;
-    float nl = 0.f, nd = 0.f;
-    auto prefetch = [&](int i) {
-        const int64_t qoff = ((b * g.Lpad + (int64_t)i * 64) * g.H + h) * D;
-        load_tile<D>(rq, q + qoff, rs);
-        load_tile<D>(rd, dO + qoff, rs);
-        if (threadIdx.x < 64) {
-            const int t = threadIdx.x;
-            const int64_t at = bh * g.Lpad + (int64_t)i * 64 + t;
-            const bool ok = t < tile_occupancy(g, i);
-            nl = ok ? lse[at] * kLog2e : 0.f;
-            nd = ok ? delta[at] : 0.f;
+    const int NSEQ = 4 * m;
+    int my_next = wave, my_slot = wave;
+    auto issue = [&]() {
+        const int i = query_of(my_next >> 2);
+        const int64_t ii = i < 0 ? 0 : i;
+        dma_half<D>(src0 + (uint64_t)ii * 64 * rs2, rows16, off, ring0 + (uint32_t)my_slot * HALF);
+        if (wave < 2) dma_floats64(fsrc + (uint64_t)ii * 256, side0 + (uint32_t)my_slot * 256);
+        my_next += 4;
+        my_slot = my_slot >= kKvSlots - 4 ? my_slot + 4 - kKvSlots : my_slot + 4;
+    };
+    while (my_next < NSEQ && my_next < kKvSlots) issue();
+
+    int rslot = 0;  // slot of position 4t
+    for (int t = 0; t < m; ++t) {
+        // Own position of entry t done (a position is NP DMA instructions,
+        // one more for waves 0 and 1, whose side slot rides along), then the
+        // barrier publishes the other waves' and retires entry t-1.
+        {
+            const int newer = (my_next - (4 * t + 4 + wave)) >> 2;
+            if (newer <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else if (wave < 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP + 1) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP) : "memory");
         }
-    };
-    int64_t e = next_valid(c0);
-    if (e < c1) prefetch(row_idx[e]);
-    while (e < c1) {
-        const int i = row_idx[e];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int lim = 4 * t + kKvSlots < NSEQ ? 4 * t + kKvSlots : NSEQ;
+        while (my_next < lim) issue();
+        int sl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sl[r] = rslot + r < kKvSlots ? rslot + r : rslot + r - kKvSlots;
+        const uint32_t qh0 = ring0 + (uint32_t)sl[0] * HALF, qh1 = ring0 + (uint32_t)sl[1] * HALF;
+        const uint32_t dh0 = ring0 + (uint32_t)sl[2] * HALF, dh1 = ring0 + (uint32_t)sl[3] * HALF;
+        const float* const lse_t = side + sl[0] * 64;
+        const float* const del_t = side + sl[1] * 64;
+        rslot = rslot + 4 < kKvSlots ? rslot + 4 : rslot + 4 - kKvSlots;
+        const int i = query_of(t);
+        if (i < 0) continue;
         const int ni = tile_occupancy(g, i);
-        __syncthreads();
-        store_tile<D>(rq, qt, LSTR);
-        store_tile<D>(rd, dt, LSTR);
-        if (threadIdx.x < 64) {
-            lse_s[threadIdx.x] = nl;
-            del_s[threadIdx.x] = nd;
-        }
-        __syncthreads();
-        e = next_valid(e + 1);
-        if (e < c1) prefetch(row_idx[e]);
         // S and dP in four 16-query blocks (A = row l16 of the block, d =
         // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
         // r of block mb holds query 16mb + 4G + r.
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
+            const uint32_t qb = mb < 2 ? qh0 : qh1, dbb = mb < 2 ? dh0 : dh1;
+            const int row = 16 * (mb & 1) + l16;
             bf16x8 qa[NS], da[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                qa[s] = pad_row8(qb0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
-                da[s] = pad_row8(db0, LSTR, 16 * mb + l16, 32 * s + 8 * G);
+                qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + kv_off<D>(row, 32 * s + 8 * G));
+                da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + kv_off<D>(row, 32 * s + 8 * G));
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -598,31 +620,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
             __builtin_amdgcn_sched_barrier(0);
             const int q0 = 16 * mb + 4 * G;
-            const f32x4 l4 = *(const f32x4*)&lse_s[q0];
-            const f32x4 d4 = *(const f32x4*)&del_s[q0];
+            const f32x4 l4 = *(const f32x4*)&lse_t[q0];
+            const f32x4 d4 = *(const f32x4*)&del_t[q0];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]) : 0.f;
+                const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e) : 0.f;
                 pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
                 dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
             }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps.
+        // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks
+        // reads the ks-th half-tiles).
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            const uint32_t qb = ks ? qh1 : qh0, dbb = ks ? dh1 : dh0;
 #pragma unroll
             for (int db0i = 0; db0i < NDB; db0i += 4) {
                 bf16x8 ta[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    ta[u] = lds_tr16(db0, LSTR, 32 * ks, 32 * ks + 16, 16 * (db0i + u), lane);
+                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16<D>(dbb, 0, 16, 16 * (db0i + u), lane);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    ta[u] = lds_tr16(qb0, LSTR, 32 * ks, 32 * ks + 16, 16 * (db0i + u), lane);
+                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16<D>(qb, 0, 16, 16 * (db0i + u), lane);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);

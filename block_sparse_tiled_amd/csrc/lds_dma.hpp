@@ -70,6 +70,27 @@ __device__ inline void dma_half(uint64_t base_any, uint64_t rows16, const int32_
     }
 }
 
+// 64 consecutive floats (256 bytes) from `base_any` to LDS byte address
+// `lds` by direct-to-LDS DMA: lane l's 4 bytes land at lds + 4*l (one
+// instruction of the calling wave).
+__device__ inline void dma_floats64(uint64_t base_any, uint32_t lds) {
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base_any >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base_any);
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const int32_t voff = 4 * (int32_t)(threadIdx.x & 63);
+    uint32_t saved;
+    asm volatile(
+            "s_mov_b32 %[t], m0\n\t"
+            "s_mov_b32 m0, %[l]\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dword %[v], %[b]\n\t"
+            "s_mov_b32 m0, %[t]"
+            : [t] "=&s"(saved)
+            : [l] "s"(m0v), [b] "s"(base), [v] "v"(voff)
+            : "memory");
+}
+
 // Wait until at most `newer` (0..2) half-tiles this wave issued after the
 // one about to be read are still in flight (each half-tile is NP DMA
 // instructions of the issuing wave).
