@@ -285,7 +285,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         qf[dc] = *(const bf16x8*)(q + qoff + dc * 16 + half * 8);
         df[dc] = *(const bf16x8*)(dO + qoff + dc * 16 + half * 8);
     }
-    const float lse2 = qvalid ? lse[bh * g.Lpad + qslot] * kLog2e : 0.f;
+    // A pad query row takes lse = +inf, so that its probabilities come out
+    // as exp2(-inf) = 0 without a per-element select.
+    const float lse2 = qvalid ? lse[bh * g.Lpad + qslot] * kLog2e : INFINITY;
     const float dl = qvalid ? delta[bh * g.Lpad + qslot] : 0.f;
     const float scale_log2 = scale * kLog2e;
     // The compiler cannot see the DMA below: make these loads finish first,
@@ -352,7 +354,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rslot = rslot + 4 < kDqSlots ? rslot + 4 : rslot + 4 - kDqSlots;
         const int j = tile_of(t);
         if (j < 0) continue;
-        const int nk = tile_occupancy(g, j) - 32 * kh;  // valid keys of this half
+        // Valid keys of this half (every tile full: no lookup per entry).
+        const int nk = (g.full ? 64 : tile_occupancy(g, j)) - 32 * kh;
         // S^T and dP^T over this wave's 32 keys (row l32 of the half-slot),
         // operand reads batched ahead of their products.
         bf16x8 ka[NDC], va[NDC];
@@ -372,18 +375,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_sched_barrier(0);
         // dS^T in two bf16 chunks of 16 keys (chunk c: registers 8c + [0, 8),
         // key 8*(rr/4) + 4*half + rr%4 of the half for register rr).
+        // When every key of the half is valid (nk >= 32: full tiles) no key
+        // is masked, so that path has no per-element compare or select.
         bf16x8 dsf[2];
+        if (nk >= 32) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int rr = 8 * c + r;
-                const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
-                const float pr = (qvalid && key < nk)
-                                         ? __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2)
-                                         : 0.f;
-                dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
-            }
+                for (int r = 0; r < 8; ++r) {
+                    const int rr = 8 * c + r;
+                    const float pr = __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2);
+                    dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
+                }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int rr = 8 * c + r;
+                    const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
+                    const float pr = key < nk ? __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2) : 0.f;
+                    dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
+                }
+        }
         // dQ^T += K^T dS^T over the half's two 16-key steps.
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -596,7 +610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rslot = rslot + 4 < kKvSlots ? rslot + 4 : rslot + 4 - kKvSlots;
         const int i = query_of(t);
         if (i < 0) continue;
-        const int ni = tile_occupancy(g, i);
+        const int ni = g.full ? 64 : tile_occupancy(g, i);  // (no lookup when every tile is full)
         // S and dP in four 16-query blocks (A = row l16 of the block, d =
         // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
         // r of block mb holds query 16mb + 4G + r.
@@ -622,11 +636,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int q0 = 16 * mb + 4 * G;
             const f32x4 l4 = *(const f32x4*)&lse_t[q0];
             const f32x4 d4 = *(const f32x4*)&del_t[q0];
+            // A full query tile (ni == 64) masks no row: that path has no
+            // per-element compare or select.
+            if (ni == 64) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e) : 0.f;
-                pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e);
+                    pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e) : 0.f;
+                    pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                }
             }
         }
         // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks
