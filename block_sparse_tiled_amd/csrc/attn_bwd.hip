@@ -481,14 +481,15 @@ __device__ inline uint32_t kv_off(int row, int col) {
     return (uint32_t)(row * 2 * D + (((col >> 3) ^ kv_swz<D>(row)) * 16) + (col & 7) * 2);
 }
 
-template <int D>
-__device__ inline bf16x8 kv_tr16(uint32_t base, int q0, int q1, int c0, int lane) {
-    const int s = lane & 15, G = lane >> 4;
-    const int col = c0 + 4 * (s & 3);
-    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4b*)(uintptr_t)(base + kv_off<D>(q0 + 4 * G + (s >> 2), col)));
-    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4b*)(uintptr_t)(base + kv_off<D>(q1 + 4 * G + (s >> 2), col)));
+// A operand of a 16x16x32 product by two transpose reads: rows 4G + [0, 4)
+// and 16 + 4G + [0, 4) of a half-tile slot for lane group G = lane/16 (per
+// 16-lane group, source lane s points at row 4G + s/4, columns c0 +
+// 4*(s%4), and lane d receives the four rows' elements of column c0 + d),
+// given this lane's address `a` in the first four rows and the byte
+// distance `r16` of 16 rows.
+__device__ inline bf16x8 kv_tr16o(uint32_t a, uint32_t r16) {
+    const i16x4b lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)a);
+    const i16x4b hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4b*)(uintptr_t)(a + r16));
     const i16x8b w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, w);
 }
@@ -572,6 +573,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int i = ri_s[c0 + t];
         return (unsigned)i < (unsigned)g.Nt ? i : -1;
     };
+    // Per-lane LDS offsets inside a half-tile slot, fixed for the walk.  The
+    // swizzle depends on the row modulo 16 only, so rows 16..31 of a slot
+    // sit at the same offsets plus 16 rows (an immediate): row reads use row
+    // l16, chunk 4s + G; transpose reads row 4G + l16/4, columns 16u +
+    // 4*(l16%4).
+    uint32_t ro[NS], to[NDB];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ro[s] = kv_off<D>(l16, 32 * s + 8 * G);
+#pragma unroll
+    for (int u = 0; u < NDB; ++u) to[u] = kv_off<D>(4 * G + (l16 >> 2), 16 * u + 4 * (l16 & 3));
+    constexpr uint32_t R16 = 16 * 2 * D;  // bytes of 16 rows
     const int NSEQ = 4 * m;
     int my_next = wave, my_slot = wave;
     auto issue = [&]() {
@@ -618,12 +630,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const uint32_t qb = mb < 2 ? qh0 : qh1, dbb = mb < 2 ? dh0 : dh1;
-            const int row = 16 * (mb & 1) + l16;
+            const uint32_t rimm = (mb & 1) * R16;
             bf16x8 qa[NS], da[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + kv_off<D>(row, 32 * s + 8 * G));
-                da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + kv_off<D>(row, 32 * s + 8 * G));
+                qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + ro[s] + rimm);
+                da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + ro[s] + rimm);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -663,13 +675,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int db0i = 0; db0i < NDB; db0i += 4) {
                 bf16x8 ta[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16<D>(dbb, 0, 16, 16 * (db0i + u), lane);
+                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(dbb + to[db0i + u], R16);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16<D>(qb, 0, 16, 16 * (db0i + u), lane);
+                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(qb + to[db0i + u], R16);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);
