@@ -127,11 +127,14 @@ __device__ inline int64_t chunked_item(int64_t b, int64_t n, int c) {
 }  // namespace
 
 // ------------------------------------------------------------------ delta
-// One thread per (batch, slot, head): delta = sum_d dO * O in fp32.
+// One thread per (batch, slot, head): delta = sum_d dO * O in fp32, and
+// the slot's lse scaled to base 2 (log2(e) * lse) for the dK/dV walk.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __restrict__ o,
                                                         const __bf16* __restrict__ dO,
-                                                        float* __restrict__ delta) {
+                                                        const float* __restrict__ lse,
+                                                        float* __restrict__ delta,
+                                                        float* __restrict__ lse2) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = (int64_t)g.B * g.Lpad * g.H;
     if (t >= total) return;
@@ -151,7 +154,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __r
             acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(w[e] & 0xffff0000u);
         }
     }
-    delta[(b * g.H + h) * g.Lpad + slot] = acc;
+    const int64_t at = (b * g.H + h) * g.Lpad + slot;
+    delta[at] = acc;
+    lse2[at] = lse[at] * kLog2e;  // the dK/dV walk reads it by DMA, scaled once
 }
 
 // ------------------------------------------------------------------ csc
@@ -461,7 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // slots, as in the dQ kernel: walk entry t is positions 4t + r, r = 0..3 (Q
 // rows 0-31, Q rows 32-63, dO rows 0-31, dO rows 32-63), position s in slot
 // s % kKvSlots, issued by wave s % 4; waves 0 and 1 also bring the query
-// tile's lse and delta (64 floats each) into the 256-byte side slot of
+// tile's base-2 lse and delta (64 floats each) into the 256-byte side slot of
 // their position's slot.  Nine slots are the fewest with which every
 // position of an entry is issued before its acquire; with the side slots
 // they keep a workgroup under 80 KB, two per CU.  Every wave reads the whole
@@ -500,7 +505,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
         Geo g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
-        const float* __restrict__ lse, const float* __restrict__ delta,
+        const float* __restrict__ lse2, const float* __restrict__ delta,
         const int32_t* __restrict__ col_start, const int32_t* __restrict__ col_cnt,
         const int32_t* __restrict__ row_idx, int64_t col_len, float scale,
         __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
@@ -565,7 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // 32-63 (with its delta), dO rows 0-31, dO rows 32-63; issued by wave r.
     const uint64_t src0 = (uint64_t)(uintptr_t)((wave < 2 ? q : dO) + (b * g.Lpad * g.H + h) * D) +
                           (uint64_t)((wave & 1) * 32 * rs2);
-    const uint64_t fsrc = (uint64_t)(uintptr_t)((wave == 0 ? lse : delta) + bh * g.Lpad);
+    const uint64_t fsrc = (uint64_t)(uintptr_t)((wave == 0 ? lse2 : delta) + bh * g.Lpad);
     const uint32_t ring0 = lds_base(ring), side0 = lds_base(side);
     // Query tile of walk entry t, or -1 for an id outside [0, Nt) (its slots
     // are filled from tile 0 and its products skipped).
@@ -653,14 +658,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (ni == 64) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e);
+                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
                     pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
                     dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r] * kLog2e) : 0.f;
+                    const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]) : 0.f;
                     pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
                     dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
                 }
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ------------------------------------------------------------------ launcher
 // Device scratch of attn_block_sparse_bwd_noalloc: the same workspace
-// (rowsum(dO*O) and the CSR's transpose) in a static array, so that callers
+// (rowsum(dO*O), the base-2 lse and the CSR's transpose) in a static array, so that callers
 // that cannot allocate (graph capture, tight serving loops) need no
 // workspace argument.  Every GPU the library runs on holds its own copy
 // until the process ends.  Each call writes every word of it that its
@@ -743,29 +748,33 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
                            int32_t* col_start, int32_t* col_cnt, int32_t* row_idx,
                            hipStream_t stream) {
     const int64_t slots = (int64_t)g.B * g.Lpad * g.H;
+    // The workspace's delta region holds rowsum(dO*O), then log2(e)*lse.
+    float* const lse2 = delta + (int64_t)g.B * g.H * g.Lpad;
     const unsigned dblocks = (unsigned)((slots + 255) / 256);
     const unsigned items = (unsigned)((int64_t)g.B * g.H * g.Nt);
     const size_t csc_lds = (size_t)3 * g.Nt * sizeof(int);
     const __bf16 *Q = (const __bf16*)q, *K = (const __bf16*)k, *V = (const __bf16*)v,
                  *O = (const __bf16*)o, *DO = (const __bf16*)dO;
     if (g.D == 128)
-        hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3(dblocks), dim3(256), 0, stream, g, O, DO, delta);
+        hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3(dblocks), dim3(256), 0, stream, g, O, DO, lse,
+                           delta, lse2);
     else
-        hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(dblocks), dim3(256), 0, stream, g, O, DO, delta);
+        hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(dblocks), dim3(256), 0, stream, g, O, DO, lse,
+                           delta, lse2);
     hipLaunchKernelGGL(bwd_csc_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), csc_lds, stream, g,
                        row_ptr, col_idx, col_len, col_start, col_cnt, row_idx);
     if (g.D == 128) {
         hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
-                           lse, (const float*)delta, (const int32_t*)col_start,
+                           (const float*)lse2, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
     } else {
         hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
                            (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
-                           lse, (const float*)delta, (const int32_t*)col_start,
+                           (const float*)lse2, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
     }

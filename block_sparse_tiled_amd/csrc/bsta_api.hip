@@ -352,7 +352,8 @@ BwdLayout bwd_layout(const Geo& g, int64_t col_len) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     BwdLayout l;
     l.delta = 0;
-    l.col_start = up(l.delta + (int64_t)g.B * g.H * g.Lpad * 4);
+    // rowsum(dO*O) per query slot, then log2(e)*lse per query slot.
+    l.col_start = up(l.delta + (int64_t)2 * g.B * g.H * g.Lpad * 4);
     l.col_cnt = up(l.col_start + (int64_t)g.B * g.H * g.Nt * 4);
     l.row_idx = up(l.col_cnt + (int64_t)g.B * g.H * g.Nt * 4);
     l.total = up(l.row_idx + (col_len > 0 ? col_len : 0) * 4);

@@ -430,8 +430,9 @@ int32_t attn_block_sparse_fwd_pruned(const bsta_geom* g, const void* q_tiled,
 
 /*
  * attn_bwd_workspace_bytes (host only): bytes of device workspace
- * attn_block_sparse_bwd needs for a CSR of col_len entries (per-query
- * rowsum(dO*O) and the CSR's transpose); a negative status on bad arguments.
+ * attn_block_sparse_bwd needs for a CSR of col_len entries (per query slot
+ * rowsum(dO*O) and the lse scaled to base 2, and the CSR's transpose); a
+ * negative status on bad arguments.
  */
 int64_t attn_bwd_workspace_bytes(const bsta_geom* g, int64_t col_len);
 

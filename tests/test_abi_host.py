@@ -258,7 +258,8 @@ def test_bwd_workspace_and_errors(lib):
     nt = geometry.num_tiles(16, 48, 80)
     lpad = 64 * nt
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = up(up(up(2 * 3 * lpad * 4) + 2 * 3 * nt * 4) + 2 * 3 * nt * 4) + up(1000 * 4)
+    # rowsum(dO*O) and log2(e)*lse per query slot, then the CSR transpose.
+    want = up(up(up(2 * 2 * 3 * lpad * 4) + 2 * 3 * nt * 4) + 2 * 3 * nt * 4) + up(1000 * 4)
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(g), 1000) == want
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(g), -1) == _lib.BSTA_ERR_SHAPE
     s = _g()
