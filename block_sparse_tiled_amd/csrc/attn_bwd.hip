@@ -270,7 +270,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // CSR reads are wave-uniform: read them through the scalar cache.
     typedef const __attribute__((address_space(4))) int32_t* cptr;
     const cptr rp_s = (cptr)row_ptr, ci_s = (cptr)col_idx;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Wave-uniform by construction; readfirstlane tells the compiler so, which
+    // keeps the DMA bookkeeping and the tile-id reads scalar.
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
     const int qb = wave & 1, kh = wave >> 1;  // query block, key half
     const int64_t item = blockIdx.x;
@@ -516,7 +518,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) float side[kKvSlots * 64];
     typedef const __attribute__((address_space(4))) int32_t* cptr;
     const cptr ri_s = (cptr)row_idx;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Wave-uniform by construction; readfirstlane tells the compiler so, which
+    // keeps the DMA bookkeeping and the tile-id reads scalar.
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = lane >> 4, l16 = lane & 15;
     // Key tiles are dealt to the XCDs in runs of 16 neighbours: the columns
     // of neighbouring key tiles hold many of the same query tiles, so the
