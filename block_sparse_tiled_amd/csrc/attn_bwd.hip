@@ -329,21 +329,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                           (uint64_t)((wave & 1) * 32 * rs2);
     const uint32_t ring0 = lds_base(ring);
     // Tile of walk entry t, or -1 for an id outside [0, Nt) (its slots are
-    // filled from tile 0 and its products skipped).
-    auto tile_of = [&](int t) -> int {
-        const int j = ci_s[p0 + t];
-        return (unsigned)j < (unsigned)g.Nt ? j : -1;
-    };
+    // filled from tile 0 and its products skipped).  The read and the check
+    // are apart, so that a read made ahead is not waited for at once.
+    auto raw_of = [&](int t) -> int { return ci_s[p0 + t]; };
+    auto checked = [&](int j) -> int { return (unsigned)j < (unsigned)g.Nt ? j : -1; };
     const int NSEQ = 4 * n;
     int my_next = wave, my_slot = wave;
-    auto issue = [&]() {
-        const int j = tile_of(my_next >> 2);
+    auto issue = [&](int j) {
         dma_half<D>(src0 + (uint64_t)(j < 0 ? 0 : j) * 64 * rs2, rows16, off,
                     ring0 + (uint32_t)my_slot * HALF);
         my_next += 4;
         my_slot = my_slot >= kDqSlots - 4 ? my_slot + 4 - kDqSlots : my_slot + 4;
     };
-    while (my_next < NSEQ && my_next < kDqSlots) issue();
+    while (my_next < NSEQ && my_next < kDqSlots) issue(checked(raw_of(my_next >> 2)));
+    // Tile ids are read one entry ahead of their use, at the end of the
+    // entry before, so that the scalar loads' latency falls into the wait at
+    // the next barrier (which drains them anyway) instead of the LDS waits
+    // of the products: the id of entry t, and that of this wave's next
+    // position.  In the walk a wave issues at most one position per entry
+    // (the limit grows by 4 per entry, a wave's positions by 4 per issue, and
+    // each entry issues up to the limit).
+    int j_cur = n > 0 ? raw_of(0) : -1;
+    int j_iss = my_next < NSEQ ? raw_of(my_next >> 2) : -1;
 
     int rslot = 0;  // slot of position 4t
     for (int t = 0; t < n; ++t) {
@@ -354,68 +361,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int lim = 4 * t + kDqSlots < NSEQ ? 4 * t + kDqSlots : NSEQ;
-        while (my_next < lim) issue();
+        const int j = checked(j_cur);
+        const bool issued = my_next < lim;
+        if (issued) issue(checked(j_iss));
+        auto read_ahead = [&]() {
+            if (t + 1 < n) j_cur = raw_of(t + 1);
+            if (issued && my_next < NSEQ) j_iss = raw_of(my_next >> 2);
+        };
         const int kslot = rslot + kh < kDqSlots ? rslot + kh : rslot + kh - kDqSlots;
         const int vslot = rslot + 2 + kh < kDqSlots ? rslot + 2 + kh : rslot + 2 + kh - kDqSlots;
         const uint32_t kbuf = ring0 + (uint32_t)kslot * HALF, vbuf = ring0 + (uint32_t)vslot * HALF;
         rslot = rslot + 4 < kDqSlots ? rslot + 4 : rslot + 4 - kDqSlots;
-        const int j = tile_of(t);
-        if (j < 0) continue;
-        // Valid keys of this half (every tile full: no lookup per entry).
-        const int nk = (g.full ? 64 : tile_occupancy(g, j)) - 32 * kh;
-        // S^T and dP^T over this wave's 32 keys (row l32 of the half-slot),
-        // operand reads batched ahead of their products.
-        bf16x8 ka[NDC], va[NDC];
+        if (j >= 0) {
+            // Valid keys of this half (every tile full: no lookup per entry).
+            const int nk = (g.full ? 64 : tile_occupancy(g, j)) - 32 * kh;
+            // S^T and dP^T over this wave's 32 keys (row l32 of the half-slot),
+            // operand reads batched ahead of their products.
+            bf16x8 ka[NDC], va[NDC];
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-            const int col = 16 * dc + 8 * half;
-            ka[dc] = ring_row8<D>(kbuf, l32, col);
-            va[dc] = ring_row8<D>(vbuf, l32, col);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-            s = mma(ka[dc], qf[dc], s);
-            dp = mma(va[dc], df[dc], dp);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // dS^T in two bf16 chunks of 16 keys (chunk c: registers 8c + [0, 8),
-        // key 8*(rr/4) + 4*half + rr%4 of the half for register rr).
-        // When every key of the half is valid (nk >= 32: full tiles) no key
-        // is masked, so that path has no per-element compare or select.
-        bf16x8 dsf[2];
-        if (nk >= 32) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int rr = 8 * c + r;
-                    const float pr = __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2);
-                    dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
-                }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int rr = 8 * c + r;
-                    const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
-                    const float pr = key < nk ? __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2) : 0.f;
-                    dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
-                }
-        }
-        // dQ^T += K^T dS^T over the half's two 16-key steps.
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            bf16x8 kt2[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) kt2[db] = ring_tr8<D>(kbuf, c, db, lane);
+            for (int dc = 0; dc < NDC; ++dc) {
+                const int col = 16 * dc + 8 * half;
+                ka[dc] = ring_row8<D>(kbuf, l32, col);
+                va[dc] = ring_row8<D>(vbuf, l32, col);
+            }
             __builtin_amdgcn_sched_barrier(0);
+            f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[db], dsf[c], acc[db]);
+            for (int dc = 0; dc < NDC; ++dc) {
+                s = mma(ka[dc], qf[dc], s);
+                dp = mma(va[dc], df[dc], dp);
+            }
             __builtin_amdgcn_sched_barrier(0);
+            // dS^T in two bf16 chunks of 16 keys (chunk c: registers 8c + [0, 8),
+            // key 8*(rr/4) + 4*half + rr%4 of the half for register rr).
+            // When every key of the half is valid (nk >= 32: full tiles) no key
+            // is masked, so that path has no per-element compare or select.
+            bf16x8 dsf[2];
+            if (nk >= 32) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int rr = 8 * c + r;
+                        const float pr = __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2);
+                        dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
+                    }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int rr = 8 * c + r;
+                        const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
+                        const float pr =
+                                key < nk ? __builtin_amdgcn_exp2f(s[rr] * scale_log2 - lse2) : 0.f;
+                        dsf[c][r] = (__bf16)(pr * (dp[rr] - dl));
+                    }
+            }
+            // dQ^T += K^T dS^T over the half's two 16-key steps.
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                bf16x8 kt2[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) kt2[db] = ring_tr8<D>(kbuf, c, db, lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = mma(kt2[db], dsf[c], acc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        read_ahead();
     }
     // Key half 1 hands its partial dQ^T to key half 0 through the ring (no
     // DMA is in flight: the last entry waited for every position).
@@ -578,10 +593,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t ring0 = lds_base(ring), side0 = lds_base(side);
     // Query tile of walk entry t, or -1 for an id outside [0, Nt) (its slots
     // are filled from tile 0 and its products skipped).
-    auto query_of = [&](int t) -> int {
-        const int i = ri_s[c0 + t];
-        return (unsigned)i < (unsigned)g.Nt ? i : -1;
-    };
+    auto raw_of = [&](int t) -> int { return ri_s[c0 + t]; };
+    auto checked = [&](int i) -> int { return (unsigned)i < (unsigned)g.Nt ? i : -1; };
     // Per-lane LDS offsets inside a half-tile slot, fixed for the walk.  The
     // swizzle depends on the row modulo 16 only, so rows 16..31 of a slot
     // sit at the same offsets plus 16 rows (an immediate): row reads use row
@@ -595,15 +608,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr uint32_t R16 = 16 * 2 * D;  // bytes of 16 rows
     const int NSEQ = 4 * m;
     int my_next = wave, my_slot = wave;
-    auto issue = [&]() {
-        const int i = query_of(my_next >> 2);
+    auto issue = [&](int i) {
         const int64_t ii = i < 0 ? 0 : i;
         dma_half<D>(src0 + (uint64_t)ii * 64 * rs2, rows16, off, ring0 + (uint32_t)my_slot * HALF);
         if (wave < 2) dma_floats64(fsrc + (uint64_t)ii * 256, side0 + (uint32_t)my_slot * 256);
         my_next += 4;
         my_slot = my_slot >= kKvSlots - 4 ? my_slot + 4 - kKvSlots : my_slot + 4;
     };
-    while (my_next < NSEQ && my_next < kKvSlots) issue();
+    while (my_next < NSEQ && my_next < kKvSlots) issue(checked(raw_of(my_next >> 2)));
+    // Query tile ids are read one entry ahead of their use, at the end of the
+    // entry before, as in the dQ kernel (a wave issues at most one position
+    // per entry of the walk).
+    int i_cur = m > 0 ? raw_of(0) : -1;
+    int i_iss = my_next < NSEQ ? raw_of(my_next >> 2) : -1;
 
     int rslot = 0;  // slot of position 4t
     for (int t = 0; t < m; ++t) {
@@ -620,7 +637,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int lim = 4 * t + kKvSlots < NSEQ ? 4 * t + kKvSlots : NSEQ;
-        while (my_next < lim) issue();
+        const int i = checked(i_cur);
+        const bool issued = my_next < lim;
+        if (issued) issue(checked(i_iss));
+        auto read_ahead = [&]() {
+            if (t + 1 < m) i_cur = raw_of(t + 1);
+            if (issued && my_next < NSEQ) i_iss = raw_of(my_next >> 2);
+        };
         int sl[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sl[r] = rslot + r < kKvSlots ? rslot + r : rslot + r - kKvSlots;
@@ -629,74 +652,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float* const lse_t = side + sl[0] * 64;
         const float* const del_t = side + sl[1] * 64;
         rslot = rslot + 4 < kKvSlots ? rslot + 4 : rslot + 4 - kKvSlots;
-        const int i = query_of(t);
-        if (i < 0) continue;
-        const int ni = g.full ? 64 : tile_occupancy(g, i);  // (no lookup when every tile is full)
-        // S and dP in four 16-query blocks (A = row l16 of the block, d =
-        // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
-        // r of block mb holds query 16mb + 4G + r.
-        bf16x8 pf[2], dsf[2];
+        if (i >= 0) {
+            // (No lookup when every tile is full.)
+            const int ni = g.full ? 64 : tile_occupancy(g, i);
+            // S and dP in four 16-query blocks (A = row l16 of the block, d =
+            // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
+            // r of block mb holds query 16mb + 4G + r.
+            bf16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const uint32_t qb = mb < 2 ? qh0 : qh1, dbb = mb < 2 ? dh0 : dh1;
-            const uint32_t rimm = (mb & 1) * R16;
-            bf16x8 qa[NS], da[NS];
+            for (int mb = 0; mb < 4; ++mb) {
+                const uint32_t qb = mb < 2 ? qh0 : qh1, dbb = mb < 2 ? dh0 : dh1;
+                const uint32_t rimm = (mb & 1) * R16;
+                bf16x8 qa[NS], da[NS];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + ro[s] + rimm);
-                da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + ro[s] + rimm);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                s4 = mma16(qa[s], kf[s], s4);
-                p4 = mma16(da[s], vf[s], p4);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const int q0 = 16 * mb + 4 * G;
-            const f32x4 l4 = *(const f32x4*)&lse_t[q0];
-            const f32x4 d4 = *(const f32x4*)&del_t[q0];
-            // A full query tile (ni == 64) masks no row: that path has no
-            // per-element compare or select.
-            if (ni == 64) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
-                    pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                for (int s = 0; s < NS; ++s) {
+                    qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + ro[s] + rimm);
+                    da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + ro[s] + rimm);
                 }
-            } else {
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float pr = q0 + r < ni ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]) : 0.f;
-                    pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                for (int s = 0; s < NS; ++s) {
+                    s4 = mma16(qa[s], kf[s], s4);
+                    p4 = mma16(da[s], vf[s], p4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const int q0 = 16 * mb + 4 * G;
+                const f32x4 l4 = *(const f32x4*)&lse_t[q0];
+                const f32x4 d4 = *(const f32x4*)&del_t[q0];
+                // A full query tile (ni == 64) masks no row: that path has no
+                // per-element compare or select.
+                if (ni == 64) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
+                        pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                        dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pr = q0 + r < ni
+                                                 ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r])
+                                                 : 0.f;
+                        pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                        dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                    }
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks
+            // reads the ks-th half-tiles).
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t qb = ks ? qh1 : qh0, dbb = ks ? dh1 : dh0;
+#pragma unroll
+                for (int db0i = 0; db0i < NDB; db0i += 4) {
+                    bf16x8 ta[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(dbb + to[db0i + u], R16);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(qb + to[db0i + u], R16);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks
-        // reads the ks-th half-tiles).
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint32_t qb = ks ? qh1 : qh0, dbb = ks ? dh1 : dh0;
-#pragma unroll
-            for (int db0i = 0; db0i < NDB; db0i += 4) {
-                bf16x8 ta[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(dbb + to[db0i + u], R16);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(qb + to[db0i + u], R16);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        read_ahead();
     }
     // Lane holds dV^T, dK^T[d = 16*db + 4*G + r][key kj].
 #pragma unroll
