@@ -488,14 +488,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // position of an entry is issued before its acquire; with the side slots
 // they keep a workgroup under 80 KB, two per CU.  Every wave reads the whole
 // Q and dO tiles.  The 16-byte chunk c of row r sits at position
-// c ^ kv_swz(r), a map that the 64-bank model rates free of conflicts for
-// both of the kernel's 16x16 read shapes (16 rows x 4 chunks, and per
-// 16-lane group 4 rows x 32 bytes), and that depends on the row modulo 16
-// only, as the DMA's offsets require.
+// c ^ kv_swz(r), a map that depends on the row modulo 16 only, as the DMA's
+// offsets require.  It is chosen by measurement: the bank conflict counters
+// of a probe that repeats the kernel's two read shapes (ds_read_b128 of 16
+// rows x 4 chunks, or x 2 for D = 64; transpose reads of 4 rows x 32 bytes
+// per 16-lane group) read zero for it at both head sizes.  The maps
+// 2*(r%8) + (r/8)%2 (D = 128) and (r & 6) + (r/8)%2 (D = 64), which give
+// rows r and r + 8 the same chunks but for the lowest bit, are also
+// conflict-free for the transpose reads but double the cycles of the row
+// reads (8 instead of 4 per instruction), although a model that serves 16
+// consecutive lanes together rates them free of conflicts.
 template <int D>
 __device__ inline int kv_swz(int r) {
-    if constexpr (D == 128) return (2 * (r & 7)) | ((r >> 3) & 1);
-    else return (r & 6) | ((r >> 3) & 1);
+    const int h = (r >> 3) & 1;
+    if constexpr (D == 128) return (2 * ((r & 7) ^ (4 * h))) | h;
+    else return ((r & 6) ^ (4 * h)) | h;
 }
 
 template <int D>
