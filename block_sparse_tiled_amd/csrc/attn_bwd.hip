@@ -128,7 +128,11 @@ __device__ inline int64_t chunked_item(int64_t b, int64_t n, int c) {
 
 // ------------------------------------------------------------------ delta
 // One thread per (batch, slot, head): delta = sum_d dO * O in fp32, and
-// the slot's lse scaled to base 2 (log2(e) * lse) for the dK/dV walk.
+// the slot's lse scaled to base 2 (log2(e) * lse) for the dK/dV walk.  A
+// pad slot (row r >= n_i of its 64-slot tile), or a row that attends to no
+// key (lse = -inf), gets +inf instead: its probabilities in the walk come
+// out as exp2(-inf) = 0 from finite scores (pad rows of Q are zero), with
+// no per-element mask.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __restrict__ o,
                                                         const __bf16* __restrict__ dO,
@@ -156,7 +160,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __r
     }
     const int64_t at = (b * g.H + h) * g.Lpad + slot;
     delta[at] = acc;
-    lse2[at] = lse[at] * kLog2e;  // the dK/dV walk reads it by DMA, scaled once
+    const float l = lse[at];
+    const bool row = (int)(slot & 63) < tile_occupancy(g, (int)(slot >> 6)) && l > -INFINITY;
+    lse2[at] = row ? l * kLog2e : INFINITY;  // the dK/dV walk reads it by DMA
 }
 
 // ------------------------------------------------------------------ csc
@@ -660,8 +666,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float* const del_t = side + sl[1] * 64;
         rslot = rslot + 4 < kKvSlots ? rslot + 4 : rslot + 4 - kKvSlots;
         if (i >= 0) {
-            // (No lookup when every tile is full.)
-            const int ni = g.full ? 64 : tile_occupancy(g, i);
             // S and dP in four 16-query blocks (A = row l16 of the block, d =
             // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
             // r of block mb holds query 16mb + 4G + r.
@@ -687,24 +691,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int q0 = 16 * mb + 4 * G;
                 const f32x4 l4 = *(const f32x4*)&lse_t[q0];
                 const f32x4 d4 = *(const f32x4*)&del_t[q0];
-                // A full query tile (ni == 64) masks no row: that path has no
-                // per-element compare or select.
-                if (ni == 64) {
+                // A pad query row has lse2 = +inf (set by the delta kernel):
+                // its probabilities are exp2(-inf) = 0 with no mask.
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
-                        pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                        dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pr = q0 + r < ni
-                                                 ? __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r])
-                                                 : 0.f;
-                        pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                        dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
+                    pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
+                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks

@@ -448,8 +448,9 @@ int64_t attn_bwd_workspace_bytes(const bsta_geom* g, int64_t col_len);
  *   q_tiled, k_tiled, v_tiled [in] bf16 [B, Lpad, H, D], as given to the
  *            forward
  *   o_tiled  [in] bf16 [B, Lpad, H, D], the forward's tiled output
- *   do_tiled [in] bf16 [B, Lpad, H, D], gradient of the loss w.r.t. O (pad
- *            rows are ignored)
+ *   do_tiled [in] bf16 [B, Lpad, H, D], gradient of the loss w.r.t. O; pad
+ *            rows must be finite (attn_tile writes them as zero) and do not
+ *            change the result
  *   lse      [in] fp32 [B, H, Lpad], the forward's lse
  *   row_ptr, col_idx, col_len  the forward's CSR.  Ranges are clamped and
  *            out-of-range ids skipped as in the forward; an id repeated in
