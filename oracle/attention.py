@@ -85,19 +85,20 @@ def tile_attention_backward(q, keys, vals, do, scale: float):
     return (ds @ keys) * scale, (ds.T @ q) * scale, p.T @ do
 
 
-def block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X, scale=None):
+def block_sparse_attention_backward(qt, kt, vt, dot, mask, T, Y, X, scale=None, tile=geometry.TILE):
     """Gradients of the block-sparse attention of tile-ordered tensors.
 
     For the loss sum(dot * out) with out = block_sparse_attention(...):
     query tile i of head h attends over the valid tokens of the key tiles
     mask[b, h, i] keeps, so its rows receive dq from those keys, and each
     kept key/value tile receives dk, dv from every query tile that keeps it.
-    Padded slots (query or key) get zero gradient.  Inputs [B, Lpad, H, D];
-    returns float64 (dq, dk, dv) of that shape.
+    Padded slots (query or key) get zero gradient.  Inputs [B, Lpad, H, D]
+    in the slot order of `tile` (4x4x4 or 4x4x8 tokens); returns float64
+    (dq, dk, dv) of that shape.
     """
     B, lpad, H, D = qt.shape
-    E = geometry.TILE_ELEMS
-    occ = geometry.occupancy(T, Y, X)
+    E = geometry.tile_elems(tile)
+    occ = geometry.occupancy(T, Y, X, tile)
     nt = len(occ)
     if scale is None:
         scale = 1.0 / math.sqrt(D)

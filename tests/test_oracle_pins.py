@@ -534,24 +534,28 @@ def test_single_tile_matches_textbook_and_logsumexp():
 
 # ---------------------------------------------------------------- backward
 
-def _bwd_case(grid, H=2, D=16, B=1, k=3, seed=0):
+def _bwd_case(grid, H=2, D=16, B=1, k=3, seed=0, tile=geometry.TILE):
     T, Y, X = grid
     rng = np.random.default_rng(seed)
     L = T * Y * X
     q, kk, v, do = (rng.standard_normal((B, L, H, D)) for _ in range(4))
-    nt = geometry.num_tiles(T, Y, X)
+    nt = geometry.num_tiles(T, Y, X, tile)
     s = rng.standard_normal((B, H, nt, nt))
     mask = select.topk_mask(s, min(k, nt))
     return q, kk, v, do, mask
 
 
-@pytest.mark.parametrize("grid,k", [((5, 6, 7), 2), ((8, 8, 4), 3), ((3, 9, 5), 1)])
-def test_backward_equals_autograd(grid, k):
-    """torch autograd (float64) through the dense token-masked attention."""
+@pytest.mark.parametrize("grid,k,tile", [((5, 6, 7), 2, (4, 4, 4)), ((8, 8, 4), 3, (4, 4, 4)),
+                                         ((3, 9, 5), 1, (4, 4, 4)), ((5, 6, 11), 2, (4, 4, 8)),
+                                         ((4, 8, 16), 3, (4, 4, 8))])
+def test_backward_equals_autograd(grid, k, tile):
+    """torch autograd (float64) through the dense token-masked attention, for
+    64-token and 128-token tiles (the token mask comes from each token's tile
+    coordinates, not from the slot order the oracle walks)."""
     T, Y, X = grid
-    q, kk, v, do, mask = _bwd_case(grid, k=k, seed=7)
+    q, kk, v, do, mask = _bwd_case(grid, k=k, seed=7, tile=tile)
     B, L, H, D = q.shape
-    tid = geometry.token_tile_ids(T, Y, X)
+    tid = geometry.token_tile_ids(T, Y, X, tile)
     qt_, kt_, vt_ = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, kk, v))
     out = torch.zeros((B, L, H, D), dtype=torch.float64)
     outs = []
@@ -562,13 +566,13 @@ def test_backward_equals_autograd(grid, k):
             outs.append(torch.softmax(sc, dim=-1) @ vt_[b, :, h])
     out = torch.stack(outs).reshape(B, H, L, D).permute(0, 2, 1, 3)
     (out * torch.tensor(do)).sum().backward()
-    tq, tk, tv, tdo = (tiling.tile(a, T, Y, X) for a in (q, kk, v, do))
-    dq, dk, dv = attention.block_sparse_attention_backward(tq, tk, tv, tdo, mask, T, Y, X)
+    tq, tk, tv, tdo = (tiling.tile(a, T, Y, X, tile) for a in (q, kk, v, do))
+    dq, dk, dv = attention.block_sparse_attention_backward(tq, tk, tv, tdo, mask, T, Y, X, tile=tile)
     for got, ref in ((dq, qt_.grad), (dk, kt_.grad), (dv, vt_.grad)):
-        assert np.allclose(tiling.untile(got, T, Y, X), ref.numpy(), rtol=1e-10, atol=1e-10)
+        assert np.allclose(tiling.untile(got, T, Y, X, tile), ref.numpy(), rtol=1e-10, atol=1e-10)
     # pad slots receive nothing
     valid = np.zeros(tq.shape[1], dtype=bool)
-    valid[geometry.token_slots(T, Y, X)] = True
+    valid[geometry.token_slots(T, Y, X, tile)] = True
     for g in (dq, dk, dv):
         assert np.all(g[:, ~valid] == 0)
 
