@@ -431,13 +431,37 @@ def main():
         nnz8 = int(sel8.row_ptr[-1].item())
         ms8 = {n: float(np.median(v_)) for n, v_ in per8.items()}
         flop8 = 4.0 * w.D * 128 * 128 * nnz8
+        # The backward over the same selection (tiled output and lse from one
+        # more forward call, a seeded dO): five products per selected pair.
+        b8 = None
+        if nt8 <= 4096:
+            ot8, lse8 = bsta.attn_block_sparse_fwd(g8, qt8, kt8, vt8, sel8.row_ptr, sel8.col_idx,
+                                                   want_lse=True)
+            gen8 = torch.Generator(device=dev).manual_seed(7)
+            dot8 = torch.randn(ot8.shape, generator=gen8, device=dev).to(torch.bfloat16)
+            gr8 = tuple(torch.empty_like(qt8) for _ in range(3))
+            per_b8 = []
+            for it in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                bsta.attn_block_sparse_bwd(g8, qt8, kt8, vt8, ot8, dot8, lse8, sel8.row_ptr,
+                                           sel8.col_idx, out=gr8)
+                e1.record()
+                torch.cuda.synchronize()
+                if it >= 1:
+                    per_b8.append(e0.elapsed_time(e1))
+            b8 = float(np.median(per_b8))
+            del ot8, lse8, dot8, gr8
         t128 = {"tile": [4, 4, 8], "tiles": nt8, "topk": k8, "selected_tile_pairs": nnz8,
                 "tile_qkv_ms": ms8["tile_qkv"], "select_ms": ms8["select"],
                 "attn_ms": ms8["attn_fwd"],
                 "attn_tflops": flop8 / (ms8["attn_fwd"] * 1e-3) / 1e12,
                 "attn_frac_mfma_peak": flop8 / (ms8["attn_fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "bwd_ms": b8,
+                "bwd_tflops": None if b8 is None else 2.5 * flop8 / (b8 * 1e-3) / 1e12,
                 "note": "128-token tiles: tile_pool/tile, top-k from pooled, raster attention "
-                        "(each 128-key tile = two 64-key units); not in the step"}
+                        "(each 128-key tile = two 64-key units); the backward walks the same "
+                        "units (3 timed calls, median); not in the step"}
         print(f"[bench] 128-token tiles {t128}", file=sys.stderr, flush=True)
         del qt8, kt8, vt8, sel8
 

@@ -25,6 +25,12 @@
 //             each lane holds one key), then dV^T += dO^T P and
 //             dK^T += Q^T dS; each wave takes 16 keys of the tile, on the
 //             16x16x32 matrix instruction (its layouts are given with it).
+// The walks work on 64-slot units.  A 64-token tile is one unit; a 128-token
+// (4x4x8) tile is two, its valid tokens first, so its first unit holds
+// min(n, 64) of them.  A dq work item is one query unit and a dkdv item one
+// key unit; a CSR entry (or a column's query tile) stands for the tile's
+// units, walked as consecutive entries, so every 64x64 unit pair is one
+// entry of the same code.  The CSR and its transpose stay per tile.
 // The dQ products use v_mfma_f32_32x32x16_bf16 with the lane layouts of the
 // forward kernel (checked on hardware there): A[m][k] in lane m + 32*(k/8),
 // element k%8; B[k][n] in lane n + 32*(k/8), element k%8; accumulator
@@ -129,7 +135,7 @@ __device__ inline int64_t chunked_item(int64_t b, int64_t n, int c) {
 // ------------------------------------------------------------------ delta
 // One thread per (batch, slot, head): delta = sum_d dO * O in fp32, and
 // the slot's lse scaled to base 2 (log2(e) * lse) for the dK/dV walk.  A
-// pad slot (row r >= n_i of its 64-slot tile), or a row that attends to no
+// pad slot (row r >= n_u of its 64-slot unit), or a row that attends to no
 // key (lse = -inf), gets +inf instead: its probabilities in the walk come
 // out as exp2(-inf) = 0 from finite scores (pad rows of Q are zero), with
 // no per-element mask.
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __r
     const int64_t at = (b * g.H + h) * g.Lpad + slot;
     delta[at] = acc;
     const float l = lse[at];
-    const bool row = (int)(slot & 63) < tile_occupancy(g, (int)(slot >> 6)) && l > -INFINITY;
+    const bool row = (int)(slot & 63) < unit_occupancy(g, (int)(slot >> 6)) && l > -INFINITY;
     lse2[at] = row ? l * kLog2e : INFINITY;  // the dK/dV walk reads it by DMA
 }
 
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __r
 }
 
 // ------------------------------------------------------------------ dq
-// One workgroup of four waves per query tile.  Wave w owns query rows
+// One workgroup of four waves per query unit.  Wave w owns query rows
 // 32*(w%2) + [0, 32) and key rows 32*(w/2) + [0, 32) of every key tile it
 // walks: its three products per entry (S^T and dP^T over its 32 keys, then
 // dQ^T += K^T dS^T over them) need one 32-row half of K and one of V.  Two
@@ -281,16 +287,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
     const int qb = wave & 1, kh = wave >> 1;  // query block, key half
+    // A work item is one 64-slot query unit iu of tile i = iu / sub (sub = 2
+    // units per 128-token tile, else 1); every CSR entry j of the tile's row
+    // stands for the key units sub*j + [0, sub), walked as consecutive entries.
+    const int lsub = g.le - 6, msub = g.sub - 1;
+    const int nu = g.Nt << lsub;
     const int64_t item = blockIdx.x;
-    const int i = (int)(item % g.Nt);
-    const int64_t bh = item / g.Nt;
+    const int iu = (int)(item % nu);
+    const int i = iu >> lsub;
+    const int64_t bh = item / nu;
     const int h = (int)(bh % g.H);
     const int64_t b = bh / g.H;
     const int64_t rs = (int64_t)g.H * D;
     const int qi = qb * 32 + l32;
-    const int ni = tile_occupancy(g, i);
+    const int ni = unit_occupancy(g, iu);
     const bool qvalid = qi < ni;
-    const int64_t qslot = (int64_t)i * 64 + qi;
+    const int64_t qslot = (int64_t)iu * 64 + qi;
     const int64_t qoff = ((b * g.Lpad + qslot) * g.H + h) * D;
     bf16x8 qf[NDC], df[NDC];
 #pragma unroll
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int64_t p0 = rp_s[bh * g.Nt + i], p1 = rp_s[bh * g.Nt + i + 1];
     p0 = p0 < 0 ? 0 : (p0 > col_len ? col_len : p0);
     p1 = p1 < p0 ? p0 : (p1 > col_len ? col_len : p1);
-    const int n = (int)(p1 - p0);
+    const int n = (int)(p1 - p0) << lsub;  // walk entries (key units)
 
     // Per-lane DMA source offsets of blocks 0..3 of a half-tile: block u
     // fills slot bytes [1024u, 1024u + 1024), row r = (1024u + 16*lane) /
@@ -334,11 +346,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint64_t src0 = (uint64_t)(uintptr_t)((wave < 2 ? k : v) + (b * g.Lpad * g.H + h) * D) +
                           (uint64_t)((wave & 1) * 32 * rs2);
     const uint32_t ring0 = lds_base(ring);
-    // Tile of walk entry t, or -1 for an id outside [0, Nt) (its slots are
-    // filled from tile 0 and its products skipped).  The read and the check
-    // are apart, so that a read made ahead is not waited for at once.
-    auto raw_of = [&](int t) -> int { return ci_s[p0 + t]; };
-    auto checked = [&](int j) -> int { return (unsigned)j < (unsigned)g.Nt ? j : -1; };
+    // Key unit of walk entry t, or -1 for a tile id outside [0, Nt) (its
+    // slots are filled from unit 0 and its products skipped).  The read of
+    // the tile id and the check are apart, so that a read made ahead is not
+    // waited for at once.
+    auto raw_of = [&](int t) -> int { return ci_s[p0 + (t >> lsub)]; };
+    auto checked = [&](int j, int t) -> int {
+        return (unsigned)j < (unsigned)g.Nt ? (j << lsub) | (t & msub) : -1;
+    };
     const int NSEQ = 4 * n;
     int my_next = wave, my_slot = wave;
     auto issue = [&](int j) {
@@ -347,7 +362,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         my_next += 4;
         my_slot = my_slot >= kDqSlots - 4 ? my_slot + 4 - kDqSlots : my_slot + 4;
     };
-    while (my_next < NSEQ && my_next < kDqSlots) issue(checked(raw_of(my_next >> 2)));
+    while (my_next < NSEQ && my_next < kDqSlots)
+        issue(checked(raw_of(my_next >> 2), my_next >> 2));
     // Tile ids are read one entry ahead of their use, at the end of the
     // entry before, so that the scalar loads' latency falls into the wait at
     // the next barrier (which drains them anyway) instead of the LDS waits
@@ -367,9 +383,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int lim = 4 * t + kDqSlots < NSEQ ? 4 * t + kDqSlots : NSEQ;
-        const int j = checked(j_cur);
+        const int j = checked(j_cur, t);
         const bool issued = my_next < lim;
-        if (issued) issue(checked(j_iss));
+        if (issued) issue(checked(j_iss, my_next >> 2));
         auto read_ahead = [&]() {
             if (t + 1 < n) j_cur = raw_of(t + 1);
             if (issued && my_next < NSEQ) j_iss = raw_of(my_next >> 2);
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rslot = rslot + 4 < kDqSlots ? rslot + 4 : rslot + 4 - kDqSlots;
         if (j >= 0) {
             // Valid keys of this half (every tile full: no lookup per entry).
-            const int nk = (g.full ? 64 : tile_occupancy(g, j)) - 32 * kh;
+            const int nk = (g.full ? 64 : unit_occupancy(g, j)) - 32 * kh;
             // S^T and dP^T over this wave's 32 keys (row l32 of the half-slot),
             // operand reads batched ahead of their products.
             bf16x8 ka[NDC], va[NDC];
@@ -469,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ dk, dv
-// One workgroup of four waves per key tile, on v_mfma_f32_16x16x32_bf16
+// One workgroup of four waves per key unit, on v_mfma_f32_16x16x32_bf16
 // (lane layouts checked on hardware: A[m][k] in lane m%16 + 16*(k/8),
 // element k%8; B[k][n] in lane n + 16*(k/8), element k%8; register r of
 // lane l holds D[4*(l/16) + r][l%16]).  Wave w owns keys 16w + [0, 16) of
@@ -554,15 +570,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // of neighbouring key tiles hold many of the same query tiles, so the
     // workgroups that run together on an XCD share more of their Q and dO
     // reads in its L2 (2% on the 40-head 1200-tile top-120 backward).
+    // A work item is one 64-slot key unit ju of tile j = ju / sub; every
+    // query tile i of the tile's column stands for the query units sub*i +
+    // [0, sub), walked as consecutive entries.
+    const int lsub = g.le - 6, msub = g.sub - 1;
+    const int nu = g.Nt << lsub;
     const int64_t item = chunked_item(blockIdx.x, (int64_t)gridDim.x, 16);
-    const int j = (int)(item % g.Nt);
-    const int64_t bh = item / g.Nt;
+    const int ju = (int)(item % nu);
+    const int j = ju >> lsub;
+    const int64_t bh = item / nu;
     const int h = (int)(bh % g.H);
     const int64_t b = bh / g.H;
     const int64_t rs = (int64_t)g.H * D;
     const int kj = wave * 16 + l16;
-    const bool kvalid = kj < tile_occupancy(g, j);
-    const int64_t koff = ((b * g.Lpad + (int64_t)j * 64 + kj) * g.H + h) * D;
+    const bool kvalid = kj < unit_occupancy(g, ju);
+    const int64_t koff = ((b * g.Lpad + (int64_t)ju * 64 + kj) * g.H + h) * D;
     bf16x8 kf[NS], vf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -584,7 +606,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int64_t c1 = c0 + col_cnt[bh * g.Nt + j];
     c0 = c0 < 0 ? 0 : (c0 > col_len ? col_len : c0);
     c1 = c1 < c0 ? c0 : (c1 > col_len ? col_len : c1);
-    const int m = (int)(c1 - c0);
+    const int m = (int)(c1 - c0) << lsub;  // walk entries (query units)
 
     // Per-lane DMA source offsets of blocks 0..3 of a half-tile (as in the
     // dQ kernel, with this ring's swizzle).
@@ -604,10 +626,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                           (uint64_t)((wave & 1) * 32 * rs2);
     const uint64_t fsrc = (uint64_t)(uintptr_t)((wave == 0 ? lse2 : delta) + bh * g.Lpad);
     const uint32_t ring0 = lds_base(ring), side0 = lds_base(side);
-    // Query tile of walk entry t, or -1 for an id outside [0, Nt) (its slots
-    // are filled from tile 0 and its products skipped).
-    auto raw_of = [&](int t) -> int { return ri_s[c0 + t]; };
-    auto checked = [&](int i) -> int { return (unsigned)i < (unsigned)g.Nt ? i : -1; };
+    // Query unit of walk entry t, or -1 for a tile id outside [0, Nt) (its
+    // slots are filled from unit 0 and its products skipped).
+    auto raw_of = [&](int t) -> int { return ri_s[c0 + (t >> lsub)]; };
+    auto checked = [&](int i, int t) -> int {
+        return (unsigned)i < (unsigned)g.Nt ? (i << lsub) | (t & msub) : -1;
+    };
     // Per-lane LDS offsets inside a half-tile slot, fixed for the walk.  The
     // swizzle depends on the row modulo 16 only, so rows 16..31 of a slot
     // sit at the same offsets plus 16 rows (an immediate): row reads use row
@@ -628,7 +652,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         my_next += 4;
         my_slot = my_slot >= kKvSlots - 4 ? my_slot + 4 - kKvSlots : my_slot + 4;
     };
-    while (my_next < NSEQ && my_next < kKvSlots) issue(checked(raw_of(my_next >> 2)));
+    while (my_next < NSEQ && my_next < kKvSlots)
+        issue(checked(raw_of(my_next >> 2), my_next >> 2));
     // Query tile ids are read one entry ahead of their use, at the end of the
     // entry before, as in the dQ kernel (a wave issues at most one position
     // per entry of the walk).
@@ -650,9 +675,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int lim = 4 * t + kKvSlots < NSEQ ? 4 * t + kKvSlots : NSEQ;
-        const int i = checked(i_cur);
+        const int i = checked(i_cur, t);
         const bool issued = my_next < lim;
-        if (issued) issue(checked(i_iss));
+        if (issued) issue(checked(i_iss, my_next >> 2));
         auto read_ahead = [&]() {
             if (t + 1 < m) i_cur = raw_of(t + 1);
             if (issued && my_next < NSEQ) i_iss = raw_of(my_next >> 2);
@@ -783,7 +808,7 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
     // The workspace's delta region holds rowsum(dO*O), then log2(e)*lse.
     float* const lse2 = delta + (int64_t)g.B * g.H * g.Lpad;
     const unsigned dblocks = (unsigned)((slots + 255) / 256);
-    const unsigned items = (unsigned)((int64_t)g.B * g.H * g.Nt);
+    const unsigned items = (unsigned)((int64_t)g.B * g.H * g.Nt * g.sub);  // 64-slot units
     const size_t csc_lds = (size_t)3 * g.Nt * sizeof(int);
     const __bf16 *Q = (const __bf16*)q, *K = (const __bf16*)k, *V = (const __bf16*)v,
                  *O = (const __bf16*)o, *DO = (const __bf16*)dO;

@@ -725,8 +725,6 @@ int32_t check_bwd(const bsta_geom* gin, Geo* g, const void* q_tiled, const void*
     if (g->Nt > kMaxBwdTiles)
         return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
                     g->Nt);
-    if (g->tx != 4)
-        return fail(BSTA_ERR_UNSUPPORTED, "%s: 64-token tiles only (4x4x4)", who);
     return BSTA_OK;
 }
 

@@ -460,10 +460,12 @@ int64_t attn_bwd_workspace_bytes(const bsta_geom* g, int64_t col_len);
  *   dq_tiled, dk_tiled, dv_tiled [out] bf16 [B, Lpad, H, D]; pad rows and
  *            key tiles that no row selects are written as +0.0
  *   workspace [scratch, >= attn_bwd_workspace_bytes(g, col_len)]
- * Requires Nt <= 4096 (BSTA_ERR_SHAPE otherwise).  Gradients accumulate in
- * fp32, key tiles in CSR row order for dQ and query tiles in ascending
- * order for dK and dV, so equal inputs give bitwise equal gradients; P and
- * dS are rounded to bf16 for the second products.
+ * Requires Nt <= 4096 (BSTA_ERR_SHAPE otherwise).  Tiles of 64 or 128
+ * tokens, a single grid or a packed sequence; a 128-token tile is walked as
+ * its two 64-slot units (valid tokens first), in unit order.  Gradients
+ * accumulate in fp32, key tiles in CSR row order for dQ and query tiles in
+ * ascending order for dK and dV, so equal inputs give bitwise equal
+ * gradients; P and dS are rounded to bf16 for the second products.
  */
 int32_t attn_block_sparse_bwd(const bsta_geom* g, const void* q_tiled, const void* k_tiled,
                               const void* v_tiled, const void* o_tiled, const void* do_tiled,

@@ -156,18 +156,20 @@ def row_backward_bounds(q, keys, vals, do, scale):
             scale * eds @ np.abs(keys), scale * eds.T @ np.abs(q), e_p * p.T @ np.abs(do))
 
 
-def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X, occ=None):
+def backward_error_bounds(qt, kt, vt, dot, mask, T, Y, X, occ=None, tile=None):
     """Per-element error bounds for the GPU gradients (float64, tiled shapes):
     row_backward_bounds summed over the selection, plus the final bf16
     rounding of each gradient (u times its magnitude).  ``occ`` (valid
     tokens per tile) replaces the (T, Y, X) grid's, e.g. for a packed
-    sequence.  Returns (bound_dq, bound_dk, bound_dv)."""
+    sequence; ``tile`` is the tile shape (default 4x4x4).  Returns
+    (bound_dq, bound_dk, bound_dv)."""
     from oracle import geometry as ogeo
     u = BF16_U
     B, lpad, Hh, D = qt.shape
-    E = ogeo.TILE_ELEMS
+    tile = ogeo.TILE if tile is None else tile
+    E = ogeo.tile_elems(tile)
     if occ is None:
-        occ = ogeo.occupancy(T, Y, X)
+        occ = ogeo.occupancy(T, Y, X, tile)
     scale = 1.0 / np.sqrt(D)
     bq, bk, bv = (np.zeros((B, lpad, Hh, D)) for _ in range(3))
     gq, gk, gv = (np.zeros((B, lpad, Hh, D)) for _ in range(3))

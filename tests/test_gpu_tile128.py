@@ -3,7 +3,9 @@ with the same tile shape (reading R23).
 
 Bars as for 64-token tiles: tile/untile and window masks bit-exact, top-k
 rows exact outside the 1e-4 tie band, pooled vectors within 1e-5(1+|x|),
-attention within max-abs 2e-2 / mean-abs 2e-3 (lse 5e-3), pad rows +0.0.
+attention within max-abs 2e-2 / mean-abs 2e-3 (lse 5e-3), pad rows +0.0;
+gradients within the per-element bound of tests/gpu_helpers.py
+(backward_error_bounds), pad slots +0.0.
 """
 import numpy as np
 import pytest
@@ -199,3 +201,87 @@ def test_tile128_full_size(bsta):
     rs = [ref[b, i * 128:(i + 1) * 128, h] for b, h, i in rows]
     mx, mean = H.compare_outputs(np.concatenate(gs), np.concatenate(rs), "raster rows")
     H.log(f"  raster rows max-abs {mx:.3g}, mean-abs {mean:.3g}")
+
+
+def _bwd_run(m, w, inp, r, seed=41):
+    import torch
+    rng = np.random.default_rng(seed)
+    do_bits = workloads.bf16_bits(rng.standard_normal((w.B, w.L, w.H, w.D)).astype(np.float32))
+    dot = m.attn_tile(r["g"], H.to_dev(do_bits))
+    grads = m.attn_block_sparse_bwd(r["g"], r["qt"], r["kt"], r["vt"], r["ot"], dot, r["lse"],
+                                    r["sel"].row_ptr, r["sel"].col_idx)
+    torch.cuda.synchronize()
+    return do_bits, dot, grads
+
+
+def _check_bwd(w, grads, tf, dtf, mask, heads=None):
+    hs = list(range(w.H)) if heads is None else heads
+    sub = lambda a: a[:, :, hs]  # noqa: E731
+    args = [sub(tf["q"]), sub(tf["k"]), sub(tf["v"]), sub(dtf)]
+    ref = oatt.block_sparse_attention_backward(*args, mask[:, hs], w.T, w.Y, w.X, tile=T448)
+    bnd = H.backward_error_bounds(*args, mask[:, hs], w.T, w.Y, w.X, tile=T448)
+    valid = np.zeros(ref[0].shape[1], dtype=bool)
+    valid[geometry.token_slots(w.T, w.Y, w.X, T448)] = True
+    for nm, gt, rf, bd in zip(("dq", "dk", "dv"), grads, ref, bnd):
+        bits = H.from_dev(gt)[:, :, hs]
+        got = workloads.bf16_to_f32(bits).astype(np.float64)
+        err = np.abs(got[:, valid] - rf[:, valid])
+        ratio = float((err / (bd[:, valid] + 1e-6)).max())
+        H.log(f"  {nm}: max err {err.max():.3g}, max err/bound {ratio:.3f}")
+        assert np.all(err <= bd[:, valid] + 1e-6), f"{nm}: error above its bound (ratio {ratio:.3f})"
+        assert np.all(bits[:, ~valid] == 0), f"{nm}: pad slots must be +0.0"
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_tile128_backward(bsta, name):
+    """Gradients over 128-token tiles (each tile walked as its two 64-slot
+    units, an empty second unit included: the ragged grids end in tiles of
+    fewer than 64 tokens) against the oracle's backward with the same tile
+    shape, under the GPU's selection; a second call is bitwise equal."""
+    w = CASES[name]
+    inp = H.inputs(w)
+    H.log(f"128-token tiles backward {name}")
+    r = _run(bsta, w, inp)
+    do_bits, dot, grads = _bwd_run(bsta, w, inp, r)
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits, w.T, w.Y, w.X, T448))
+    _check_bwd(w, grads, tf, dtf, r["sel"].block_mask.cpu().numpy().astype(bool))
+    again = bsta.attn_block_sparse_bwd(r["g"], r["qt"], r["kt"], r["vt"], r["ot"], dot, r["lse"],
+                                       r["sel"].row_ptr, r["sel"].col_idx)
+    for a, b in zip(grads, again):
+        assert np.array_equal(H.from_dev(a), H.from_dev(b)), "backward is deterministic"
+
+
+@pytest.mark.parametrize("windows", [[[1, 3, 1], [2, 2, 3]]])
+def test_tile128_backward_windows(bsta, windows):
+    """Gradients over per-head sliding windows of 128-token tiles (rows of
+    different lengths per head)."""
+    w = workloads.custom("t128_sta", 1, 2, 128, 8, 16, 24, "sta", seed=97)
+    inp = H.inputs(w)
+    H.log(f"128-token tiles backward, windows {windows}")
+    r = _run(bsta, w, inp, windows=windows)
+    do_bits, _, grads = _bwd_run(bsta, w, inp, r)
+    _, tf = _oracle_tiled(w, inp)
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits, w.T, w.Y, w.X, T448))
+    om = select.sta_mask(w.T, w.Y, w.X, np.array(windows), w.B, T448)
+    _check_bwd(w, grads, tf, dtf, om)
+
+
+@pytest.mark.timeout(900)
+def test_tile128_backward_full_size(bsta):
+    """The 40-head 20x48x80 grid in 600 tiles of 4x4x8, top-60: every
+    gradient of one head against the oracle (the heads are independent)."""
+    base = workloads.WORKLOADS["c3"]
+    w = workloads.Workload("c3_t128", base.index, base.B, base.H, base.D, base.T, base.Y, base.X,
+                           "topk", 60, base.structure)
+    H.log("128-token tiles backward, full size")
+    inp = H.inputs(w)
+    r = _run(bsta, w, inp, fused=True)
+    do_bits, _, grads = _bwd_run(bsta, w, inp, r)
+    heads = [w.H - 1]
+    tf = {n: workloads.bf16_to_f32(tiling.tile(inp[n][:, :, heads], w.T, w.Y, w.X, T448))
+          for n in ("q", "k", "v")}
+    dtf = workloads.bf16_to_f32(tiling.tile(do_bits[:, :, heads], w.T, w.Y, w.X, T448))
+    mask = r["sel"].block_mask.cpu().numpy().astype(bool)[:, heads]
+    wsub = workloads.custom("c3_t128_heads", w.B, len(heads), w.D, w.T, w.Y, w.X, "topk", w.topk)
+    _check_bwd(wsub, tuple(t[:, :, heads] for t in grads), tf, dtf, mask)
