@@ -692,61 +692,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         rslot = rslot + 4 < kKvSlots ? rslot + 4 : rslot + 4 - kKvSlots;
         if (i >= 0) {
             // S and dP in four 16-query blocks (A = row l16 of the block, d =
-            // 32s + 8G + [0, 8)), each block's P and dS taken at once: register
-            // r of block mb holds query 16mb + 4G + r.
+            // 32s + 8G + [0, 8)): register r of block mb holds query 16mb + 4G +
+            // r.  Block mb+1's products are issued before block mb's P and dS
+            // are taken, and block mb+2's operands are read before that.
             bf16x8 pf[2], dsf[2];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            bf16x8 qa[4][NS], da[4][NS];
+            f32x4 l4[4], d4[4], s4[4], p4[4];
+            auto rd = [&](int mb) {
                 const uint32_t qb = mb < 2 ? qh0 : qh1, dbb = mb < 2 ? dh0 : dh1;
                 const uint32_t rimm = (mb & 1) * R16;
-                bf16x8 qa[NS], da[NS];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    qa[s] = *(const lds_bf16x8b*)(uintptr_t)(qb + ro[s] + rimm);
-                    da[s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + ro[s] + rimm);
+                    qa[mb][s] = *(const lds_bf16x8b*)(uintptr_t)(qb + ro[s] + rimm);
+                    da[mb][s] = *(const lds_bf16x8b*)(uintptr_t)(dbb + ro[s] + rimm);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4 s4 = (f32x4){0.f, 0.f, 0.f, 0.f}, p4 = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    s4 = mma16(qa[s], kf[s], s4);
-                    p4 = mma16(da[s], vf[s], p4);
-                }
-                __builtin_amdgcn_sched_barrier(0);
                 const int q0 = 16 * mb + 4 * G;
-                const f32x4 l4 = *(const f32x4*)&lse_t[q0];
-                const f32x4 d4 = *(const f32x4*)&del_t[q0];
-                // A pad query row has lse2 = +inf (set by the delta kernel):
-                // its probabilities are exp2(-inf) = 0 with no mask.
+                l4[mb] = *(const f32x4*)&lse_t[q0];
+                d4[mb] = *(const f32x4*)&del_t[q0];
+            };
+            auto mm = [&](int mb) {
+                s4[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                p4[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    s4[mb] = mma16(qa[mb][s], kf[s], s4[mb]);
+                    p4[mb] = mma16(da[mb][s], vf[s], p4[mb]);
+                }
+            };
+            // A pad query row has lse2 = +inf (set by the delta kernel): its
+            // probabilities are exp2(-inf) = 0 with no mask.
+            auto pds = [&](int mb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(s4[r] * scale_log2 - l4[r]);
+                    const float pr = __builtin_amdgcn_exp2f(s4[mb][r] * scale_log2 - l4[mb][r]);
                     pf[mb >> 1][4 * (mb & 1) + r] = (__bf16)pr;
-                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[r] - d4[r]));
+                    dsf[mb >> 1][4 * (mb & 1) + r] = (__bf16)(pr * (p4[mb][r] - d4[mb][r]));
                 }
+            };
+            rd(0);
+            rd(1);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                if (mb + 2 < 4) rd(mb + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (mb + 1 < 4) mm(mb + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                pds(mb);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // dV^T += dO^T P and dK^T += Q^T dS over two 32-query steps (step ks
-            // reads the ks-th half-tiles).
+            // reads the ks-th half-tiles), in groups of four products over four
+            // d blocks: group g is step g / (NDB/2), d blocks 4*((g/2) % (NDB/4))
+            // + [0, 4), dV (g even, dO^T operands) or dK (g odd, Q^T operands).
+            // The operands of group g+1 are read while group g multiplies.
+            constexpr int NG = NDB;  // 2 steps x NDB/4 block groups x (dV, dK)
+            bf16x8 ta[2][4];
+            auto rd2 = [&](int gi) {
+                const int ks = gi / (NG / 2), db0i = 4 * ((gi >> 1) % (NDB / 4));
+                const uint32_t base = (gi & 1) ? (ks ? qh1 : qh0) : (ks ? dh1 : dh0);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint32_t qb = ks ? qh1 : qh0, dbb = ks ? dh1 : dh0;
+                for (int u = 0; u < 4; ++u) ta[gi & 1][u] = kv_tr16o(base + to[db0i + u], R16);
+            };
+            auto mm2 = [&](int gi) {
+                const int ks = gi / (NG / 2), db0i = 4 * ((gi >> 1) % (NDB / 4));
 #pragma unroll
-                for (int db0i = 0; db0i < NDB; db0i += 4) {
-                    bf16x8 ta[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(dbb + to[db0i + u], R16);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) adv[db0i + u] = mma16(ta[u], pf[ks], adv[db0i + u]);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) ta[u] = kv_tr16o(qb + to[db0i + u], R16);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        adk[db0i + u] = mma16(ta[u], dsf[ks], adk[db0i + u]);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < 4; ++u) {
+                    if (gi & 1)
+                        adk[db0i + u] = mma16(ta[1][u], dsf[ks], adk[db0i + u]);
+                    else
+                        adv[db0i + u] = mma16(ta[0][u], pf[ks], adv[db0i + u]);
                 }
+            };
+            rd2(0);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                if (gi + 1 < NG) rd2(gi + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mm2(gi);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         read_ahead();
