@@ -9,11 +9,12 @@
 //   dS = P * (dP - delta),  delta = rowsum(dO * O)   (one value per query)
 //   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D),  dV = P^T dO.
 //
-// Four kernels:
+// Three launches:
 //   delta     rowsum(dO * O) per query slot (fp32).
 //   csc       per (batch, head), the transpose of the CSR: for every key
 //             tile the query tiles whose rows list it, in row order, so that
-//             the dK/dV sums run in a fixed order.
+//             the dK/dV sums run in a fixed order (the first workgroups of
+//             the dq launch).
 //   dq        one workgroup of four waves per query tile, walking its CSR
 //             row: S^T = K Q^T and dP^T = V dO^T on the matrix cores (keys
 //             as M, queries as N, so each lane holds one query), then
@@ -172,34 +173,32 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(Geo g, const __bf16* __r
 }
 
 // ------------------------------------------------------------------ csc
-// One workgroup of 1024 threads per (batch, head).  LDS: cnt, start, cur
-// (Nt ints each).  Column j of head bh lists, in row order, the query tiles
-// whose CSR rows hold j; it occupies row_idx[col_start[bh*Nt + j] + [0,
-// col_cnt[bh*Nt + j])), inside the head's own CSR range.  Row ranges are
-// clamped to [0, col_len) and ids outside [0, Nt) are skipped.  A row that
-// repeats an id appears that many times in the id's column (the fill takes
-// its positions with an LDS atomic), so the dK/dV walk counts the repeat as
-// the forward and the dQ walk do.
-__global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __restrict__ row_ptr,
-                                                       const int32_t* __restrict__ col_idx,
-                                                       int64_t col_len, int32_t* __restrict__ col_start,
-                                                       int32_t* __restrict__ col_cnt,
-                                                       int32_t* __restrict__ row_idx) {
-    extern __shared__ int sm[];
-    __shared__ int part[1024];
+// The transpose of head bh's CSR, by one workgroup of 256 threads (the
+// first B*H workgroups of the dq launch run it, beside the dq walks, which
+// do not read it; the dkdv launch after them does).  LDS `sm` holds 2*Nt +
+// 256 ints: per-column counts (reused as fill cursors) and starts, and the
+// scan's partial sums.  Column j of head bh lists, in row order, the query
+// tiles whose CSR rows hold j; it occupies row_idx[col_start[bh*Nt + j] +
+// [0, col_cnt[bh*Nt + j])), inside the head's own CSR range.  Row ranges
+// are clamped to [0, col_len) and ids outside [0, Nt) are skipped.  A row
+// that repeats an id appears that many times in the id's column (the fill
+// takes its positions with an LDS atomic), so the dK/dV walk counts the
+// repeat as the forward and the dQ walk do.
+__device__ inline void csc_head(const Geo& g, int64_t bh, const int32_t* __restrict__ row_ptr,
+                                const int32_t* __restrict__ col_idx, int64_t col_len,
+                                int32_t* __restrict__ col_start, int32_t* __restrict__ col_cnt,
+                                int32_t* __restrict__ row_idx, int* sm) {
+    constexpr int NT = 256;
     const int Nt = g.Nt;
-    int* cnt = sm;
+    int* cnt = sm;  // counts, then fill cursors
     int* start = sm + Nt;
-    int* cur = sm + 2 * Nt;
+    int* part = sm + 2 * Nt;
     const int tid = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * Nt;
+    const int64_t base = bh * Nt;
     auto clampp = [&](int64_t p) { return p < 0 ? (int64_t)0 : (p > col_len ? col_len : p); };
-    for (int j = tid; j < Nt; j += 1024) {
-        cnt[j] = 0;
-        cur[j] = 0;
-    }
+    for (int j = tid; j < Nt; j += NT) cnt[j] = 0;
     __syncthreads();
-    for (int i = tid; i < Nt; i += 1024) {
+    for (int i = tid; i < Nt; i += NT) {
         const int64_t p0 = clampp(row_ptr[base + i]);
         const int64_t p1 = clampp(row_ptr[base + i + 1]);
         for (int64_t p = p0; p < p1; ++p) {
@@ -209,39 +208,41 @@ __global__ __launch_bounds__(1024) void bwd_csc_kernel(Geo g, const int32_t* __r
     }
     __syncthreads();
     // Exclusive scan of cnt: each thread a run of `per` columns.
-    const int per = (Nt + 1023) / 1024;
+    const int per = (Nt + NT - 1) / NT;
     const int j0 = tid * per < Nt ? tid * per : Nt;
     const int j1 = j0 + per < Nt ? j0 + per : Nt;
-    int s = 0;
-    for (int j = j0; j < j1; ++j) s += cnt[j];
-    part[tid] = s;
+    int sum = 0;
+    for (int j = j0; j < j1; ++j) sum += cnt[j];
+    part[tid] = sum;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
         const int add = tid >= off ? part[tid - off] : 0;
         __syncthreads();
         part[tid] += add;
         __syncthreads();
     }
-    int run = part[tid] - s;
+    int run = part[tid] - sum;
     for (int j = j0; j < j1; ++j) {
         start[j] = run;
         run += cnt[j];
     }
     __syncthreads();
     const int64_t head_off = clampp(row_ptr[base]);
-    for (int j = tid; j < Nt; j += 1024) {
+    for (int j = tid; j < Nt; j += NT) {
         col_start[base + j] = (int32_t)(head_off + start[j]);
         col_cnt[base + j] = cnt[j];
+        cnt[j] = 0;  // the fill's cursor from here on
     }
+    __syncthreads();
     // Fill in row order: one row at a time, its ids in parallel.  Repeats of
     // an id within the row take distinct positions (all holding the same row).
     for (int i = 0; i < Nt; ++i) {
         const int64_t p0 = clampp(row_ptr[base + i]);
         const int64_t p1 = clampp(row_ptr[base + i + 1]);
-        for (int64_t p = p0 + tid; p < p1; p += 1024) {
+        for (int64_t p = p0 + tid; p < p1; p += NT) {
             const int j = col_idx[p];
             if ((unsigned)j < (unsigned)Nt) {
-                const int r = atomicAdd(&cur[j], 1);
+                const int r = atomicAdd(&cnt[j], 1);
                 const int64_t pos = head_off + start[j] + r;
                 if (pos < col_len) row_idx[pos] = i;
             }
@@ -273,12 +274,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const __bf16* __restrict__ v, const __bf16* __restrict__ dO,
         const float* __restrict__ lse, const float* __restrict__ delta,
         const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t col_len,
-        float scale, __bf16* __restrict__ dq) {
+        float scale, __bf16* __restrict__ dq, int csc_blocks, int32_t* __restrict__ col_start,
+        int32_t* __restrict__ col_cnt, int32_t* __restrict__ row_idx) {
     constexpr int NDC = D / 16, NDB = D / 32;
     constexpr int HALF = 32 * D * 2;  // bytes of one half-tile slot
     constexpr int NP = HALF / 1024;   // DMA instructions per half-tile
     __shared__ __attribute__((aligned(1024))) char ring[kDqSlots * HALF];
     static_assert(2 * NDB * 16 * 64 * 4 <= kDqSlots * HALF, "partial dQ exchange fits the ring");
+    static_assert((2 * kMaxBwdTiles + 256) * 4 <= kDqSlots * HALF, "the CSR transpose fits the ring");
+    // The first csc_blocks workgroups transpose one head's CSR each.
+    if ((int64_t)blockIdx.x < csc_blocks) {
+        csc_head(g, blockIdx.x, row_ptr, col_idx, col_len, col_start, col_cnt, row_idx, (int*)ring);
+        return;
+    }
     // CSR reads are wave-uniform: read them through the scalar cache.
     typedef const __attribute__((address_space(4))) int32_t* cptr;
     const cptr rp_s = (cptr)row_ptr, ci_s = (cptr)col_idx;
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // stands for the key units sub*j + [0, sub), walked as consecutive entries.
     const int lsub = g.le - 6, msub = g.sub - 1;
     const int nu = g.Nt << lsub;
-    const int64_t item = blockIdx.x;
+    const int64_t item = blockIdx.x - csc_blocks;
     const int iu = (int)(item % nu);
     const int i = iu >> lsub;
     const int64_t bh = item / nu;
@@ -835,7 +843,7 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
     float* const lse2 = delta + (int64_t)g.B * g.H * g.Lpad;
     const unsigned dblocks = (unsigned)((slots + 255) / 256);
     const unsigned items = (unsigned)((int64_t)g.B * g.H * g.Nt * g.sub);  // 64-slot units
-    const size_t csc_lds = (size_t)3 * g.Nt * sizeof(int);
+    const int csc_blocks = g.B * g.H;  // the dq launch's first workgroups: the CSR transpose
     const __bf16 *Q = (const __bf16*)q, *K = (const __bf16*)k, *V = (const __bf16*)v,
                  *O = (const __bf16*)o, *DO = (const __bf16*)dO;
     if (g.D == 128)
@@ -844,18 +852,18 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
     else
         hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3(dblocks), dim3(256), 0, stream, g, O, DO, lse,
                            delta, lse2);
-    hipLaunchKernelGGL(bwd_csc_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), csc_lds, stream, g,
-                       row_ptr, col_idx, col_len, col_start, col_cnt, row_idx);
     if (g.D == 128) {
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
-                           (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
+        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(csc_blocks + items), dim3(256), 0, stream, g, Q, K,
+                           V, DO, lse, (const float*)delta, row_ptr, col_idx, col_len, scale,
+                           (__bf16*)dq, csc_blocks, col_start, col_cnt, row_idx);
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
                            (const float*)lse2, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,
                            (__bf16*)dk, (__bf16*)dv);
     } else {
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO, lse,
-                           (const float*)delta, row_ptr, col_idx, col_len, scale, (__bf16*)dq);
+        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(csc_blocks + items), dim3(256), 0, stream, g, Q, K,
+                           V, DO, lse, (const float*)delta, row_ptr, col_idx, col_len, scale,
+                           (__bf16*)dq, csc_blocks, col_start, col_cnt, row_idx);
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(items), dim3(256), 0, stream, g, Q, K, V, DO,
                            (const float*)lse2, (const float*)delta, (const int32_t*)col_start,
                            (const int32_t*)col_cnt, (const int32_t*)row_idx, col_len, scale,

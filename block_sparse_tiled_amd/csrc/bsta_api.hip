@@ -73,9 +73,6 @@ constexpr int kMaxTopkTiles = 12288;
 // Largest tile count the cumulative-threshold selection accepts (one wave
 // holds a row in registers, 32 scores per lane).
 constexpr int kMaxCumulativeTiles = 2048;
-// Largest tile count the backward accepts (its CSR transpose keeps three
-// ints per tile in LDS).
-constexpr int kMaxBwdTiles = 4096;
 // Largest grid side (tile coordinates travel as int16 in window mode).
 constexpr int kMaxDim = 1 << 15;
 
@@ -722,8 +719,8 @@ int32_t check_bwd(const bsta_geom* gin, Geo* g, const void* q_tiled, const void*
     if (col_len < 0) return fail(BSTA_ERR_SHAPE, "col_len %lld < 0", (long long)col_len);
     if (col_len > 0x7fffffffLL)
         return fail(BSTA_ERR_SHAPE, "col_len %lld overflows int32 offsets", (long long)col_len);
-    if (g->Nt > kMaxBwdTiles)
-        return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", kMaxBwdTiles,
+    if (g->Nt > bsta::kMaxBwdTiles)
+        return fail(BSTA_ERR_SHAPE, "the backward supports at most %d tiles, got %d", bsta::kMaxBwdTiles,
                     g->Nt);
     return BSTA_OK;
 }

@@ -20,6 +20,9 @@ constexpr int kTileElems = 64;  // 4 x 4 x 4 tokens
 // Size of the static device scratch behind attn_block_sparse_bwd_noalloc,
 // and the device ordinals whose scratch address is cached.
 constexpr int64_t kBwdScratchBytes = int64_t(64) << 20;
+// Largest tile count the backward accepts (its CSR transpose keeps two ints
+// per tile in the LDS of one workgroup).
+constexpr int kMaxBwdTiles = 4096;
 constexpr int kMaxDevices = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
