@@ -72,9 +72,10 @@ def parse():
     p.add_argument("--deterministic", action="store_true",
                    help="walk every CSR row in order (attn_set_deterministic) instead of the "
                         "default rotated key walk")
-    p.add_argument("--legs", default="all", choices=["all", "step"],
+    p.add_argument("--legs", default="all", choices=["all", "step", "bwd"],
                    help="step: time only the step and its per-call events (for profiling the "
-                        "step's kernels without the side measurements' other workloads)")
+                        "step's kernels without the side measurements' other workloads); bwd: "
+                        "the step and the backward leg")
     p.add_argument("--mode", default="path", choices=["path", "copy"],
                    help="copy: time a plain 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -295,6 +296,7 @@ def main():
     # output, cold caches, other selections and geometries); --legs step
     # leaves them out.
     legs = args.legs == "all"
+    bwd_leg = args.legs in ("all", "bwd")
 
     # The standalone untile pass (not in the step: the attention writes raster
     # order itself), for its HBM rate.
@@ -524,7 +526,7 @@ def main():
     # algorithmic work is five products per selected pair (S, dP, dV, dQ,
     # dK), 2.5 times the forward's two.
     bwd = None
-    if legs and nt <= 4096:
+    if bwd_leg and nt <= 4096:
         _, lse_b = bsta.attn_block_sparse_fwd(g, qt, kt, vt, sel.row_ptr, sel.col_idx, out=ot,
                                               want_lse=True)
         gen = torch.Generator(device=dev).manual_seed(7)
