@@ -60,16 +60,19 @@ def redundancy(q: np.ndarray) -> np.ndarray:
     return out
 
 
-def keep_mask(qt: np.ndarray, T: int, Y: int, X: int, ratio: float) -> np.ndarray:
-    """Kept query slots: bool [B, H, Nt, 64] (readings P1, P2).
+def keep_mask(qt: np.ndarray, T: int, Y: int, X: int, ratio: float,
+              tile=geometry.TILE) -> np.ndarray:
+    """Kept query slots: bool [B, H, Nt, E], E the tile's slot count (readings
+    P1, P2).
 
-    qt: tile-ordered [B, Lpad, H, D].  Slot r of tile j is kept when it is a
-    valid token and among the kept_count(n_j) lowest redundancy scores of
-    its tile (stable order: ties go to the lower slot).
+    qt: tile-ordered [B, Lpad, H, D] in the slot order of `tile`.  Slot r of
+    tile j is kept when it is a valid token and among the kept_count(n_j)
+    lowest redundancy scores of its tile (stable order: ties go to the lower
+    slot).
     """
     B, lpad, H, _ = qt.shape
-    E = geometry.TILE_ELEMS
-    occ = geometry.occupancy(T, Y, X)
+    E = geometry.tile_elems(tile)
+    occ = geometry.occupancy(T, Y, X, tile)
     out = np.zeros((B, H, len(occ), E), dtype=bool)
     for b in range(B):
         for h in range(H):
@@ -81,13 +84,14 @@ def keep_mask(qt: np.ndarray, T: int, Y: int, X: int, ratio: float) -> np.ndarra
     return out
 
 
-def score_gap(qt: np.ndarray, T: int, Y: int, X: int, ratio: float) -> np.ndarray:
+def score_gap(qt: np.ndarray, T: int, Y: int, X: int, ratio: float,
+              tile=geometry.TILE) -> np.ndarray:
     """Per tile, the lowest pruned minus the highest kept redundancy score
     (+inf when nothing is pruned): float64 [B, H, Nt].  A small gap means a
     near-tie at the keep boundary."""
     B, lpad, H, _ = qt.shape
-    E = geometry.TILE_ELEMS
-    occ = geometry.occupancy(T, Y, X)
+    E = geometry.tile_elems(tile)
+    occ = geometry.occupancy(T, Y, X, tile)
     out = np.full((B, H, len(occ)), np.inf)
     for b in range(B):
         for h in range(H):
@@ -101,9 +105,9 @@ def score_gap(qt: np.ndarray, T: int, Y: int, X: int, ratio: float) -> np.ndarra
 
 def pool_kept(qt: np.ndarray, keep: np.ndarray) -> np.ndarray:
     """Mean of each tile's kept query rows (reading P3): float32 [B, H, Nt, D]
-    (float64 sum, one rounding)."""
+    (float64 sum, one rounding).  The tile's slot count is keep's last axis."""
     B, lpad, H, D = qt.shape
-    E = geometry.TILE_ELEMS
+    E = keep.shape[3]
     nt = keep.shape[2]
     out = np.zeros((B, H, nt, D), dtype=np.float32)
     for b in range(B):
@@ -116,32 +120,33 @@ def pool_kept(qt: np.ndarray, keep: np.ndarray) -> np.ndarray:
     return out
 
 
-def pruned_attention(qt, kt, vt, mask, keep, T, Y, X, scale=None, rows=None):
+def pruned_attention(qt, kt, vt, mask, keep, T, Y, X, scale=None, rows=None,
+                     tile=geometry.TILE):
     """Attention of the kept query rows, reconstructed to full tile length
     (readings P4, P5): (out float64 [B, Lpad, H, D], lse float64 [B, H, Lpad]);
     pruned and pad rows are 0 with lse -inf."""
-    out, lse = attention.block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale, rows)
+    out, lse = attention.block_sparse_attention(qt, kt, vt, mask, T, Y, X, scale, rows, tile)
     B, lpad, H, _ = qt.shape
-    E = geometry.TILE_ELEMS
-    kept_slots = keep.transpose(0, 2, 3, 1).reshape(B, lpad, H)   # [B, Nt*64, H]
+    kept_slots = keep.transpose(0, 2, 3, 1).reshape(B, lpad, H)   # [B, Nt*E, H]
     out[~kept_slots] = 0.0
     lse[~kept_slots.transpose(0, 2, 1)] = -np.inf
     return out, lse
 
 
 def run(q_bits, k_bits, v_bits, T, Y, X, ratio, mode="cumulative", threshold=None,
-        min_blocks=0, topk=None, rows=None):
+        min_blocks=0, topk=None, rows=None, tile=geometry.TILE):
     """The pruned path: tile -> prune -> pool (kept Q, all K) -> score ->
     select (cumulative threshold, as the bsa_attn page's forward, or top-k)
-    -> attention of kept rows -> reconstruct -> untile."""
+    -> attention of kept rows -> reconstruct -> untile, for 64-token or
+    128-token (`tile`) tiles."""
     from . import pipeline, tiling
     D = q_bits.shape[-1]
-    qt = tiling.tile(pipeline.widen(q_bits), T, Y, X)
-    kt = tiling.tile(pipeline.widen(k_bits), T, Y, X)
-    vt = tiling.tile(pipeline.widen(v_bits), T, Y, X)
-    keep = keep_mask(qt, T, Y, X, ratio)
+    qt = tiling.tile(pipeline.widen(q_bits), T, Y, X, tile)
+    kt = tiling.tile(pipeline.widen(k_bits), T, Y, X, tile)
+    vt = tiling.tile(pipeline.widen(v_bits), T, Y, X, tile)
+    keep = keep_mask(qt, T, Y, X, ratio, tile)
     pq = pool_kept(qt, keep)
-    pk = select.pool(kt, T, Y, X)
+    pk = select.pool(kt, T, Y, X, tile)
     s = select.scores(pq, pk)
     if mode == "cumulative":
         mask = select.cumulative_mask(s, D, threshold, min_blocks)
@@ -149,6 +154,7 @@ def run(q_bits, k_bits, v_bits, T, Y, X, ratio, mode="cumulative", threshold=Non
         mask = select.topk_mask(s, topk)
     else:
         raise ValueError(f"unknown mode {mode!r}")
-    out_t, lse = pruned_attention(qt, kt, vt, mask, keep, T, Y, X, 1.0 / math.sqrt(D), rows)
+    out_t, lse = pruned_attention(qt, kt, vt, mask, keep, T, Y, X, 1.0 / math.sqrt(D), rows, tile)
     return {"qt": qt, "kt": kt, "vt": vt, "keep": keep, "pq": pq, "pk": pk, "scores": s,
-            "mask": mask, "out_tiled": out_t, "lse": lse, "out": tiling.untile(out_t, T, Y, X)}
+            "mask": mask, "out_tiled": out_t, "lse": lse,
+            "out": tiling.untile(out_t, T, Y, X, tile)}

@@ -114,15 +114,17 @@ def test_keep_mask_order_and_ties():
     assert list(np.nonzero(keep[0, 0, 0])[0]) == [0, 1]
 
 
-@pytest.mark.parametrize("mode", ["cumulative", "topk"])
-def test_keep_all_is_the_unpruned_path(mode):
+@pytest.mark.parametrize("mode,tile", [("cumulative", (4, 4, 4)), ("topk", (4, 4, 4)),
+                                       ("cumulative", (4, 4, 8)), ("topk", (4, 4, 8))])
+def test_keep_all_is_the_unpruned_path(mode, tile):
     """ratio = 1 keeps every valid token: pooled, selection and output equal the
-    unpruned path's."""
-    w = workloads.custom("prune_all", 1, 2, 64, 5, 6, 7, "topk", 3, seed=64)
+    unpruned path's, for 64-token and 128-token tiles."""
+    w = workloads.custom("prune_all", 1, 2, 64, 5, 6, 11, "topk", 3, seed=64)
     inp = workloads.make_inputs(w)
     r = prune.run(inp["q"], inp["k"], inp["v"], w.T, w.Y, w.X, 1.0, mode=mode, threshold=0.6,
-                  topk=w.topk)
-    ref = pipeline.run(inp["q"], inp["k"], inp["v"], w.T, w.Y, w.X, "topk", w.topk)
+                  topk=w.topk, tile=tile)
+    ref = pipeline.run(inp["q"], inp["k"], inp["v"], w.T, w.Y, w.X, "topk", w.topk, tile=tile)
+    assert r["keep"].shape[3] == geometry.tile_elems(tile)
     assert np.array_equal(r["pq"], ref["pq"])
     if mode == "topk":
         assert np.array_equal(r["mask"], ref["mask"])
@@ -132,18 +134,28 @@ def test_keep_all_is_the_unpruned_path(mode):
         assert np.array_equal(r["mask"], select.cumulative_mask(ref["scores"], D, 0.6))
 
 
-def test_kept_rows_match_dense_brute_force_and_pruned_rows_are_zero():
+@pytest.mark.parametrize("tile", [(4, 4, 4), (4, 4, 8)])
+def test_kept_rows_match_dense_brute_force_and_pruned_rows_are_zero(tile):
     """Kept rows equal a dense float64 brute force under the explicit token
     mask of the pruned path's own selection; pruned and pad rows are 0 with
-    lse -inf; the selection is the cumulative rule on the kept queries' means."""
+    lse -inf; the selection is the cumulative rule on the kept queries' means;
+    each tile keeps kept_count(n) tokens, those of lowest redundancy."""
     w = workloads.custom("prune_bf", 1, 2, 64, 6, 5, 9, "topk", 3, seed=65)
     inp = workloads.make_inputs(w)
     T, Y, X = w.T, w.Y, w.X
+    E = geometry.tile_elems(tile)
     r = prune.run(inp["q"], inp["k"], inp["v"], T, Y, X, 0.4, mode="cumulative", threshold=0.5,
-                  min_blocks=1)
+                  min_blocks=1, tile=tile)
     q, k, v = (workloads.bf16_to_f32(inp[n]).astype(np.float64) for n in ("q", "k", "v"))
-    dense, dlse = attention.dense_masked_attention(q, k, v, r["mask"], T, Y, X)
-    slots = geometry.token_slots(T, Y, X)
+    dense, dlse = attention.dense_masked_attention(q, k, v, r["mask"], T, Y, X, tile=tile)
+    slots = geometry.token_slots(T, Y, X, tile)
+    occ = geometry.occupancy(T, Y, X, tile)
+    for h in range(w.H):
+        for j, n in enumerate(occ):
+            kept = np.nonzero(r["keep"][0, h, j])[0]
+            assert len(kept) == prune.kept_count(int(n), 0.4) and kept.max() < n
+            sc = prune.redundancy(r["qt"][0, j * E:j * E + n, h])
+            assert sc[kept].max() <= np.delete(sc, kept).min() if len(kept) < n else True
     keep_tok = r["keep"].transpose(0, 2, 3, 1).reshape(1, -1, w.H)[:, slots]   # [B, L, H]
     assert keep_tok.sum() < keep_tok.size          # something was pruned
     assert np.allclose(r["out"][keep_tok], dense[keep_tok], rtol=0, atol=1e-10)
@@ -155,6 +167,6 @@ def test_kept_rows_match_dense_brute_force_and_pruned_rows_are_zero():
     # the selection is taken from the kept queries' means
     s = select.scores(r["pq"], r["pk"])
     assert np.array_equal(r["mask"], select.cumulative_mask(s, w.D, 0.5, 1))
-    mean_kept = np.stack([[r["qt"][0, j * 64 + np.nonzero(r["keep"][0, h, j])[0], h].mean(axis=0)
+    mean_kept = np.stack([[r["qt"][0, j * E + np.nonzero(r["keep"][0, h, j])[0], h].mean(axis=0)
                            for j in range(r["keep"].shape[2])] for h in range(w.H)])
     assert np.allclose(r["pq"][0], mean_kept, rtol=1e-6, atol=1e-6)
