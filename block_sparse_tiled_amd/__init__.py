@@ -355,21 +355,24 @@ def attn_prune_queries(g: Geometry, q_tiled, keep_ratio: float, pooled=None, kee
                        keep_count=None):
     """Query pruning: each tile keeps min(n, max(1, floor(keep_ratio * n))) of
     its n valid query tokens, those least aligned with the tile's mean query.
-    Returns (keep_mask, keep_count, pooled): keep_mask int64 [B, H, Nt] holding
-    the 64-bit kept-slot mask of each tile (bit r = slot r), keep_count int32
-    [B, H, Nt], pooled fp32 [B, H, Nt, D] the kept queries' means.  Give
-    ``pooled`` = Selection.pooled(g)[0] to select key tiles from them."""
+    Returns (keep_mask, keep_count, pooled): keep_mask int64 [B, H, Nt * U]
+    holding a 64-bit kept-slot mask per 64-slot unit (U = tile_x // 4 units
+    per tile; word u of tile j covers its slots 64u + [0, 64), bit r = slot
+    64u + r), keep_count int32 [B, H, Nt], pooled fp32 [B, H, Nt, D] the kept
+    queries' means.  Give ``pooled`` = Selection.pooled(g)[0] to select key
+    tiles from them."""
     torch = _torch()
     nt, lpad = attn_geometry(g)
+    nu = nt * (g.tile_x // 4)
     _expect(q_tiled, (g.B, lpad, g.H, g.D), torch.bfloat16, "q_tiled")
     dev = q_tiled.device
     if keep_mask is None:
-        keep_mask = torch.empty((g.B, g.H, nt), dtype=torch.int64, device=dev)
+        keep_mask = torch.empty((g.B, g.H, nu), dtype=torch.int64, device=dev)
     if keep_count is None:
         keep_count = torch.empty((g.B, g.H, nt), dtype=torch.int32, device=dev)
     if pooled is None:
         pooled = torch.empty((g.B, g.H, nt, g.D), dtype=torch.float32, device=dev)
-    _expect(keep_mask, (g.B, g.H, nt), torch.int64, "keep_mask")
+    _expect(keep_mask, (g.B, g.H, nu), torch.int64, "keep_mask")
     _expect(keep_count, (g.B, g.H, nt), torch.int32, "keep_count")
     _expect(pooled, (g.B, g.H, nt, g.D), torch.float32, "pooled")
     _lib.check(_lib.load().attn_prune_queries(ctypes.byref(g.c), _ptr(q_tiled), float(keep_ratio),
@@ -406,7 +409,7 @@ def attn_block_sparse_fwd(g: Geometry, q_tiled, k_tiled, v_tiled, row_ptr, col_i
     _expect(lse, (g.B, g.H, lpad), torch.float32, "lse")
     lib = _lib.load()
     if keep is not None:
-        _expect(keep, (g.B, g.H, nt), torch.int64, "keep")
+        _expect(keep, (g.B, g.H, nt * (g.tile_x // 4)), torch.int64, "keep")
         _lib.check(lib.attn_block_sparse_fwd_pruned(
             ctypes.byref(g.c), _ptr(q_tiled), _ptr(k_tiled), _ptr(v_tiled), _ptr(row_ptr),
             _ptr(col_idx), col_idx.numel(), float(softmax_scale), int(bool(causal)), _ptr(keep),

@@ -663,9 +663,8 @@ int32_t attn_prune_queries(const bsta_geom* gin, const void* q_tiled, double kee
     if (st != BSTA_OK) return st;
     if (q_tiled == nullptr || keep_mask == nullptr || pooled_q == nullptr)
         return fail(BSTA_ERR_NULL, "attn_prune_queries: NULL q_tiled, keep_mask or pooled_q");
-    if (g.tx != 4 || g.nseg > 0)
-        return fail(BSTA_ERR_UNSUPPORTED,
-                    "attn_prune_queries: 64-token tiles (4x4x4) of a single grid only");
+    if (g.nseg > 0)
+        return fail(BSTA_ERR_UNSUPPORTED, "attn_prune_queries: a single grid only (not packed)");
     if (!(keep_ratio > 0.0 && keep_ratio <= 1.0))
         return fail(BSTA_ERR_SHAPE, "keep_ratio %g outside (0, 1]", keep_ratio);
     return hip_status(bsta::launch_prune(g, q_tiled, keep_ratio, keep_mask, keep_count, pooled_q,
@@ -681,9 +680,9 @@ int32_t attn_block_sparse_fwd_pruned(const bsta_geom* gin, const void* q_tiled,
                                      float* lse, void* stream) {
     if (keep_mask == nullptr)
         return fail(BSTA_ERR_NULL, "attn_block_sparse_fwd_pruned: NULL keep_mask");
-    if (gin != nullptr && (gin->tile_x != 4 || gin->segments != nullptr))
+    if (gin != nullptr && gin->segments != nullptr)
         return fail(BSTA_ERR_UNSUPPORTED,
-                    "attn_block_sparse_fwd_pruned: 64-token tiles of a single grid only");
+                    "attn_block_sparse_fwd_pruned: a single grid only (not packed)");
     return block_sparse_fwd("attn_block_sparse_fwd_pruned", gin, q_tiled, k_tiled, v_tiled,
                             row_ptr, col_idx, col_len, softmax_scale, causal, keep_mask, o, lse,
                             raster != 0, stream);

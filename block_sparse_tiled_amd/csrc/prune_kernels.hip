@@ -7,11 +7,12 @@
 // not their bodies; the rule built here: a tile of n valid tokens keeps
 // c = min(n, max(1, floor(ratio * n))) of them, those least aligned with the
 // tile's mean query (lowest cos(q_r, m), ties to the lower slot).  The kept
-// set is a 64-bit mask per (batch, head, tile), bit r for slot r; the kept
-// queries' mean is written where the block selection reads the pooled query.
+// set is a 64-bit mask per 64-slot unit (one per 64-token tile, two per
+// 128-token tile, bit r for slot r of the unit); the kept queries' mean is
+// written where the block selection reads the pooled query.
 //
-// One wave per (batch, head, tile): the tile's 64 rows of one head (D bf16
-// each) are staged in LDS with coalesced 16-byte loads, 64 / (D/8) rows per
+// One wave per (batch, head, tile): the tile's 64 or 128 rows of one head (D
+// bf16 each) are staged in LDS with coalesced 16-byte loads, 64 / (D/8) rows per
 // instruction; the mean, the per-row scores, the ranks and the kept mean are
 // then lane-parallel over rows or over d.  The kept mean is summed in fp32
 // in the pooling kernels' order, so with ratio 1 it equals their pooled
@@ -22,13 +23,14 @@ namespace bsta {
 
 namespace {
 
-template <int D>
+template <int D, int SUB>
 __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restrict__ q,
                                                    double ratio, uint64_t* __restrict__ keep_mask,
                                                    int32_t* __restrict__ keep_count,
                                                    float* __restrict__ pooled) {
-    constexpr int CH = D / 8;  // 16-byte chunks per row
-    __shared__ __attribute__((aligned(16))) uint16_t rows[64 * D];
+    constexpr int CH = D / 8;       // 16-byte chunks per row
+    constexpr int E = 64 * SUB;     // slots per tile; lane l holds rows l + 64s, s < SUB
+    __shared__ __attribute__((aligned(16))) uint16_t rows[E * D];
     __shared__ float mean[D];
     const int lane = threadIdx.x;
     const int64_t item = blockIdx.x;  // (b*H + h)*Nt + j
@@ -38,11 +40,11 @@ __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restri
     const int64_t b = bh / g.H;
     const int n = tile_occupancy(g, j);
     const int64_t rs = (int64_t)g.H * D;  // elements between consecutive slots
-    const __bf16* base = q + (b * g.Lpad + (int64_t)j * kTileElems) * rs + (int64_t)h * D;
+    const __bf16* base = q + (b * g.Lpad + (int64_t)j * E) * rs + (int64_t)h * D;
 
     // Stage the valid rows: instruction i covers 64 / CH rows.
     constexpr int RPI = 64 / CH;
-    for (int r0 = 0; r0 < 64; r0 += RPI) {
+    for (int r0 = 0; r0 < E; r0 += RPI) {
         const int r = r0 + lane / CH, c = lane % CH;
         if (r < n)
             *(u32x4*)&rows[r * D + c * 8] = *(const u32x4*)(base + (int64_t)r * rs + c * 8);
@@ -57,34 +59,47 @@ __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restri
         mean[d] = acc / (float)n;
     }
     __syncthreads();
-
-    // cos(q_r, m) of this lane's row (0 when either vector is zero).  |m|^2
+    // cos(q_r, m) of this lane's rows (0 when either vector is zero).  |m|^2
     // is summed in the same order by every lane; a lane walks its own row
     // from d = lane on, so the lanes' LDS reads fall in different banks.
     float mm = 0.f;
     for (int d = 0; d < D; ++d) mm = __builtin_fmaf(mean[d], mean[d], mm);
-    float score = INFINITY;
-    if (lane < n) {
-        float dot = 0.f, qq = 0.f;
-        for (int i = 0; i < D; ++i) {
-            const int d = (i + lane) & (D - 1);
-            const float x = at(lane, d);
-            dot = __builtin_fmaf(x, mean[d], dot);
-            qq = __builtin_fmaf(x, x, qq);
+    float score[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+        const int r = lane + 64 * s;
+        score[s] = INFINITY;
+        if (r < n) {
+            float dot = 0.f, qq = 0.f;
+            for (int i = 0; i < D; ++i) {
+                const int d = (i + lane) & (D - 1);
+                const float x = at(r, d);
+                dot = __builtin_fmaf(x, mean[d], dot);
+                qq = __builtin_fmaf(x, x, qq);
+            }
+            const float den = sqrtf(qq) * sqrtf(mm);
+            score[s] = den > 0.f ? dot / den : 0.f;
         }
-        const float den = sqrtf(qq) * sqrtf(mm);
-        score = den > 0.f ? dot / den : 0.f;
     }
     // Rank among the valid rows: lower scores first, ties to the lower slot.
-    int rank = 0;
+    int rank[SUB] = {};
     for (int i = 0; i < n; ++i) {
-        const float s = __shfl(score, i, 64);
-        rank += (s < score || (s == score && i < lane)) ? 1 : 0;
+        const float si = __shfl(score[SUB > 1 ? (i >> 6) : 0], i & 63, 64);
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            const int r = lane + 64 * s;
+            rank[s] += (si < score[s] || (si == score[s] && i < r)) ? 1 : 0;
+        }
     }
     const int c = (int)fmin((double)n, fmax(1.0, floor(ratio * (double)n)));
-    const uint64_t kept = __builtin_amdgcn_ballot_w64(lane < n && rank < c);
+    // The kept set: one 64-bit mask per 64-slot unit of the tile.
+    uint64_t kept[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s)
+        kept[s] = __builtin_amdgcn_ballot_w64(lane + 64 * s < n && rank[s] < c);
     if (lane == 0) {
-        keep_mask[item] = kept;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) keep_mask[item * SUB + s] = kept[s];
         if (keep_count != nullptr) keep_count[item] = c;
     }
 
@@ -93,10 +108,10 @@ __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restri
     // sums added in order from +0.0).
     for (int d = lane; d < D; d += 64) {
         float tot = 0.f;
-        for (int r0 = 0; r0 < 64; r0 += kPoolGroupRows) {
+        for (int r0 = 0; r0 < E; r0 += kPoolGroupRows) {
             float acc = 0.f;
             for (int r = r0; r < r0 + kPoolGroupRows && r < n; ++r)
-                if ((kept >> r) & 1) acc += at(r, d);
+                if ((kept[SUB > 1 ? (r >> 6) : 0] >> (r & 63)) & 1) acc += at(r, d);
             tot += acc;
         }
         pooled[item * D + d] = tot / (float)c;
@@ -108,12 +123,22 @@ __global__ __launch_bounds__(64) void prune_kernel(Geo g, const __bf16* __restri
 hipError_t launch_prune(const Geo& g, const void* q_tiled, double ratio, uint64_t* keep_mask,
                         int32_t* keep_count, float* pooled_q, hipStream_t stream) {
     const unsigned blocks = (unsigned)((int64_t)g.B * g.H * g.Nt);
-    if (g.D == 128)
-        hipLaunchKernelGGL(prune_kernel<128>, dim3(blocks), dim3(64), 0, stream, g,
-                           (const __bf16*)q_tiled, ratio, keep_mask, keep_count, pooled_q);
-    else
-        hipLaunchKernelGGL(prune_kernel<64>, dim3(blocks), dim3(64), 0, stream, g,
-                           (const __bf16*)q_tiled, ratio, keep_mask, keep_count, pooled_q);
+    const __bf16* qt = (const __bf16*)q_tiled;
+    if (g.sub == 1) {
+        if (g.D == 128)
+            hipLaunchKernelGGL((prune_kernel<128, 1>), dim3(blocks), dim3(64), 0, stream, g, qt, ratio,
+                               keep_mask, keep_count, pooled_q);
+        else
+            hipLaunchKernelGGL((prune_kernel<64, 1>), dim3(blocks), dim3(64), 0, stream, g, qt, ratio,
+                               keep_mask, keep_count, pooled_q);
+    } else {
+        if (g.D == 128)
+            hipLaunchKernelGGL((prune_kernel<128, 2>), dim3(blocks), dim3(64), 0, stream, g, qt, ratio,
+                               keep_mask, keep_count, pooled_q);
+        else
+            hipLaunchKernelGGL((prune_kernel<64, 2>), dim3(blocks), dim3(64), 0, stream, g, qt, ratio,
+                               keep_mask, keep_count, pooled_q);
+    }
     return hipGetLastError();
 }
 

@@ -392,8 +392,10 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
  *   q_tiled    [in]  bf16 [B, Lpad, H, D] tiled queries
  *   keep_ratio [in]  in (0, 1] (host double; floor(keep_ratio * n) is taken
  *              in double precision)
- *   keep_mask  [out] uint64 [B, H, Nt]: bit r set iff slot r of the tile is
- *              kept (pad slots never are)
+ *   keep_mask  [out] uint64 [B, H, Nt * U], U = 1 for 64-token tiles and 2
+ *              for 128-token tiles: word u of a tile covers its slots 64u +
+ *              [0, 64), bit r set iff slot 64u + r is kept (pad slots never
+ *              are)
  *   keep_count [out] int32 [B, H, Nt] kept tokens per tile, or NULL
  *   pooled_q   [out] fp32 [B, H, Nt, D]: the mean of each tile's kept
  *              queries (fp32 sum in slot order, one division).  Pass the
@@ -403,8 +405,8 @@ int32_t attn_block_sparse_fwd_raster(const bsta_geom* g, const void* q_tiled,
  *              BSTA_SELECT_PREPOOLED) or attn_select_cumulative (prepooled)
  *              then select key tiles from the kept queries.
  * Errors: ERR_NULL (q_tiled, keep_mask or pooled_q NULL), ERR_SHAPE (ratio
- * outside (0, 1]), ERR_UNSUPPORTED (128-token tiles or a packed
- * sequence), ERR_HIP.  One wave per (batch, head, tile); computed in fp32.
+ * outside (0, 1]), ERR_UNSUPPORTED (a packed sequence), ERR_HIP.  One wave
+ * per (batch, head, tile); computed in fp32.
  */
 int32_t attn_prune_queries(const bsta_geom* g, const void* q_tiled, double keep_ratio,
                            uint64_t* keep_mask, int32_t* keep_count, float* pooled_q,
@@ -417,9 +419,9 @@ int32_t attn_prune_queries(const bsta_geom* g, const void* q_tiled, double keep_
  * is written as +0.0 with lse = -inf, as the "bsa_attn" page's forward
  * restores full length from the kept positions (reading: pruned positions
  * hold zero).  Arguments otherwise as attn_block_sparse_fwd; keep_mask is
- * uint64 [B, H, Nt] on the device (ERR_NULL if NULL).  Pruned rows are
- * masked, not skipped: the call costs what the unpruned one does.
- * ERR_UNSUPPORTED for 128-token tiles and packed sequences.
+ * uint64 [B, H, Nt * U] (the layout attn_prune_queries writes) on the
+ * device (ERR_NULL if NULL).  Pruned rows are masked, not skipped: the call
+ * costs what the unpruned one does.  ERR_UNSUPPORTED for packed sequences.
  */
 int32_t attn_block_sparse_fwd_pruned(const bsta_geom* g, const void* q_tiled,
                                      const void* k_tiled, const void* v_tiled,

@@ -148,7 +148,7 @@ void path_checks() {
     CHECK(stub_launches() == base + 4);
     bsta_geom g8 = geom(1, 2, 128, 5, 6, 19, 8);
     CHECK(attn_block_sparse_fwd_raster(&g8, F, F, F, FI, FI, 16, s, 0, F, nullptr, nullptr) == BSTA_OK);
-    CHECK(attn_prune_queries(&g8, F, 0.5, FU64, FI, FF, nullptr) == BSTA_ERR_UNSUPPORTED);
+    CHECK(attn_prune_queries(&g8, F, 0.5, FU64, FI, FF, nullptr) == BSTA_OK);
 }
 
 void bwd_checks() {

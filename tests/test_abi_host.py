@@ -202,16 +202,15 @@ def test_geometry_tile128_matches_oracle(lib, grid):
     assert np.array_equal(np.array(occ), geometry.occupancy(T, Y, X, t448))
 
 
-def test_tile128_unsupported_calls(lib):
-    """Query pruning is built for 64-token tiles only; the backward takes
-    128-token tiles (its argument checks pass up to the workspace size,
-    which is checked before any HIP call)."""
+def test_tile128_calls(lib):
+    """The backward and query pruning take 128-token tiles: their argument
+    checks pass up to the first check that fails before any HIP call (the
+    workspace size, the keep ratio); other tile shapes are refused."""
     g = _g(tile=(4, 4, 8))
-    assert lib.attn_prune_queries(ctypes.byref(g), FAKE, 0.5, FAKE, None, FAKE, None) == \
-        _lib.BSTA_ERR_UNSUPPORTED
-    scale = 1.0 / math.sqrt(g.D)
-    assert lib.attn_block_sparse_fwd_pruned(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, 16, scale, 0,
-                                            FAKE, 1, FAKE, None, None) == _lib.BSTA_ERR_UNSUPPORTED
+    assert lib.attn_prune_queries(ctypes.byref(g), FAKE, 1.5, FAKE, None, FAKE, None) == \
+        _lib.BSTA_ERR_SHAPE
+    assert lib.attn_prune_queries(ctypes.byref(g), FAKE, 0.5, None, None, FAKE, None) == \
+        _lib.BSTA_ERR_NULL
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(g), 16)
     assert need > 0
     assert _bwd(lib, g, wsb=need - 1) == _lib.BSTA_ERR_CAPACITY

@@ -42,17 +42,24 @@ def bsta():
     return m
 
 
-def _bits(keep_dev):
-    """int64 [B, H, Nt] device mask words -> bool [B, H, Nt, 64]."""
+T448 = geometry.TILE_SHAPES[128]
+
+
+def _bits(keep_dev, E=64):
+    """int64 [B, H, Nt * E/64] device mask words (one per 64-slot unit) ->
+    bool [B, H, Nt, E]."""
     words = keep_dev.cpu().numpy().view(np.uint64)
-    return ((words[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+    bits = ((words[..., None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+    B, Hh, nu, _ = bits.shape
+    return bits.reshape(B, Hh, nu * 64 // E, E)
 
 
-def accept_keep(gpu_keep, qt, T, Y, X, ratio):
+def accept_keep(gpu_keep, qt, T, Y, X, ratio, tile=geometry.TILE):
     """Every tile's kept set against the oracle (module docstring).  Returns
     (tiles equal to the oracle's, tiles inside the band)."""
-    want = prune.keep_mask(qt, T, Y, X, ratio)
-    occ = geometry.occupancy(T, Y, X)
+    want = prune.keep_mask(qt, T, Y, X, ratio, tile)
+    occ = geometry.occupancy(T, Y, X, tile)
+    E = geometry.tile_elems(tile)
     B, _, Hh, _ = qt.shape
     same = band = 0
     for b in range(B):
@@ -64,7 +71,7 @@ def accept_keep(gpu_keep, qt, T, Y, X, ratio):
                 if np.array_equal(g, o):
                     same += 1
                     continue
-                s = prune.redundancy(qt[b, j * 64:j * 64 + n, h])
+                s = prune.redundancy(qt[b, j * E:j * E + n, h])
                 hi_kept, lo_pruned = s[o[:n]].max(), s[~o[:n]].min()
                 assert lo_pruned - hi_kept < PRUNE_BAND, f"tile {(b, h, j)}: sets differ, gap {lo_pruned - hi_kept}"
                 diff = np.nonzero(g[:n] != o[:n])[0]
@@ -73,11 +80,11 @@ def accept_keep(gpu_keep, qt, T, Y, X, ratio):
     return same, band
 
 
-def _run(m, w, inp, ratio, mode, threshold=0.5, min_blocks=1, raster=True):
+def _run(m, w, inp, ratio, mode, threshold=0.5, min_blocks=1, raster=True, tile_x=4):
     """Tile Q (plain) and K (pooled into the selection), prune Q into the
     selection's pooled-Q part, select from the kept means, attend."""
     import torch
-    g = m.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X)
+    g = m.Geometry(w.B, w.H, w.D, w.T, w.Y, w.X, tile_x=tile_x)
     q, k, v = (H.to_dev(inp[n]) for n in ("q", "k", "v"))
     smode = m.SELECT_CUMULATIVE if mode == "cumulative" else m.SELECT_TOPK
     sel = m.attn_select_alloc(g, smode, w.topk, want_mask=True)
@@ -98,19 +105,21 @@ def _run(m, w, inp, ratio, mode, threshold=0.5, min_blocks=1, raster=True):
     return dict(g=g, qt=qt, kt=kt, vt=vt, sel=sel, keep=keep, count=count, o=o, lse=lse)
 
 
-def _check(w, inp, r, ratio, mode, threshold=0.5, min_blocks=1, heads=None, tiles=None):
+def _check(w, inp, r, ratio, mode, threshold=0.5, min_blocks=1, heads=None, tiles=None,
+           tile=geometry.TILE):
     """The GPU's pruning, selection and output against the oracle."""
     T, Y, X = w.T, w.Y, w.X
-    tf = {n: workloads.bf16_to_f32(tiling.tile(inp[n], T, Y, X)) for n in ("q", "k", "v")}
-    gkeep = _bits(r["keep"])
-    same, band = accept_keep(gkeep, tf["q"], T, Y, X, ratio)
+    E = geometry.tile_elems(tile)
+    tf = {n: workloads.bf16_to_f32(tiling.tile(inp[n], T, Y, X, tile)) for n in ("q", "k", "v")}
+    gkeep = _bits(r["keep"], E)
+    same, band = accept_keep(gkeep, tf["q"], T, Y, X, ratio, tile)
     H.log(f"  kept sets: {same} equal, {band} inside the band")
-    occ = geometry.occupancy(T, Y, X)
+    occ = geometry.occupancy(T, Y, X, tile)
     want_count = np.array([prune.kept_count(int(n), ratio) for n in occ])
     assert np.array_equal(r["count"].cpu().numpy(), np.broadcast_to(want_count, r["count"].shape))
     # means of the GPU's kept rows, and the keys' means
     opq = prune.pool_kept(tf["q"], gkeep)
-    opk = select.pool(tf["k"], T, Y, X)
+    opk = select.pool(tf["k"], T, Y, X, tile)
     gpq, gpk = (t.cpu().numpy() for t in r["sel"].pooled(r["g"]))
     assert np.all(np.abs(gpq - opq) <= H.POOL_TOL * (1 + np.abs(opq)))
     assert np.all(np.abs(gpk - opk) <= H.POOL_TOL * (1 + np.abs(opk)))
@@ -125,10 +134,10 @@ def _check(w, inp, r, ratio, mode, threshold=0.5, min_blocks=1, heads=None, tile
     js = range(nt) if tiles is None else tiles
     rows = [(b, h, i) for b in range(w.B) for h in hs for i in js]
     ref, rlse = prune.pruned_attention(tf["q"], tf["k"], tf["v"], gmask, gkeep, T, Y, X,
-                                       1.0 / math.sqrt(w.D), rows)
+                                       1.0 / math.sqrt(w.D), rows, tile)
     got = H.bf16_dev_to_f32(r["o"])
     assert not np.isnan(got).any(), "every raster row is written"
-    order = geometry.tile_order(T, Y, X)
+    order = geometry.tile_order(T, Y, X, tile)
     start = np.concatenate([[0], np.cumsum(occ)])
     kept_g, kept_r = [], []
     for b, h, i in rows:
@@ -136,13 +145,13 @@ def _check(w, inp, r, ratio, mode, threshold=0.5, min_blocks=1, heads=None, tile
         k = gkeep[b, h, i, :occ[i]]
         assert np.all(got[b, toks[~k], h] == 0.0), "pruned rows are +0.0"
         kept_g.append(got[b, toks[k], h])
-        kept_r.append(ref[b, i * 64 + np.nonzero(k)[0], h])
+        kept_r.append(ref[b, i * E + np.nonzero(k)[0], h])
     mx, mean = H.compare_outputs(np.concatenate(kept_g), np.concatenate(kept_r), "kept rows")
     H.log(f"  kept rows max-abs {mx:.3g}, mean-abs {mean:.3g}")
     glse = r["lse"].cpu().numpy()
     for b, h, i in rows:
         k = gkeep[b, h, i]
-        sl = i * 64 + np.arange(64)
+        sl = i * E + np.arange(E)
         assert np.all(np.isneginf(glse[b, h, sl[~k]]))
         assert np.abs(glse[b, h, sl[k]] - rlse[b, h, sl[k]]).max() <= H.LSE_TOL
 
@@ -243,3 +252,44 @@ def test_pruned_full_size_c3(bsta):
         kept_r.append(ref[b, i * 64 + np.nonzero(k)[0], h])
     mx, mean = H.compare_outputs(np.concatenate(kept_g), np.concatenate(kept_r), "kept rows")
     H.log(f"  kept rows max-abs {mx:.3g}, mean-abs {mean:.3g}")
+
+
+CASES128 = {
+    "ragged_d128": (workloads.custom("prune128_ragged_d128", 2, 3, 128, 5, 6, 19, "topk", 2, seed=81),
+                    0.5),
+    "ragged_d64": (workloads.custom("prune128_ragged_d64", 1, 2, 64, 9, 13, 10, "topk", 3, seed=82),
+                   0.3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES128))
+@pytest.mark.parametrize("mode", ["cumulative", "topk"])
+def test_pruned_path_tile128(bsta, name, mode):
+    """128-token tiles: each tile keeps kept_count(n) of its up to 128 tokens
+    (two mask words, one per 64-slot unit), selection from the kept means,
+    kept rows against the oracle run with the same tile shape."""
+    w, ratio = CASES128[name]
+    H.log(f"pruned path, 128-token tiles, {name} ({mode}, ratio {ratio})")
+    inp = H.inputs(w)
+    r = _run(bsta, w, inp, ratio, mode, tile_x=8)
+    _check(w, inp, r, ratio, mode, tile=T448)
+
+
+def test_ratio_one_is_the_unpruned_path_tile128(bsta):
+    """128-token tiles at ratio 1: every valid bit set, and the kept means
+    equal attn_tile_pool's pooled Q bit for bit (the same sixteen runs of
+    eight slots, added in order)."""
+    import torch
+    w, _ = CASES128["ragged_d128"]
+    inp = H.inputs(w)
+    r = _run(bsta, w, inp, 1.0, "topk", tile_x=8)
+    g = r["g"]
+    sel = bsta.attn_select_alloc(g, bsta.SELECT_TOPK, w.topk, want_mask=False)
+    pq, _ = sel.pooled(g)
+    bsta.attn_tile_pool(g, H.to_dev(inp["q"]), pq)
+    torch.cuda.synchronize()
+    occ = geometry.occupancy(w.T, w.Y, w.X, T448)
+    full = np.arange(128)[None, :] < occ[:, None]
+    got = _bits(r["keep"], 128)
+    assert np.array_equal(got, np.broadcast_to(full, got.shape))
+    assert torch.equal(r["sel"].pooled(g)[0].view(torch.int32), pq.view(torch.int32))
